@@ -1,0 +1,26 @@
+"""Plain f64 CPU oracle for HeadPrep and attention.
+
+TEST INFRASTRUCTURE ONLY.  This package is the checker the GPU library is compared
+against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import it; the GPU library never does, and this package never
+imports the GPU library.
+
+The arithmetic lives in ``oracle.c`` (f64, plain loops).  This module only marshals
+numpy arrays into it and composes the two steps the way the attention path does:
+
+* HeadPrep -- gizml:netops reference page, "Types > HeadPrep".
+* attention and its causal mask -- same page, "Functions > attention" and
+  "Functions > causalMask".
+* headPrepInPlace's position rule (the table row of a token is its sequence row,
+  ``row0`` being the row of the first) -- same page, "Functions > headPrepInPlace".
+"""
+from .oracle import (  # noqa: F401
+    build,
+    library_path,
+    headprep,
+    attention,
+    attention_rows,
+    prefill,
+    decode,
+    threads,
+)

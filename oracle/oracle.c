@@ -1,0 +1,205 @@
+/*
+ * oracle.c -- plain f64 CPU oracle for HeadPrep and scaled-dot-product attention.
+ *
+ * TEST INFRASTRUCTURE ONLY: the checker the GPU library is compared against.  Only
+ * the test suite, the smoke check and the benchmark's CPU-baseline leg load it.  It
+ * shares no code with the GPU library.  Loops are plain and unblocked so that each
+ * step can be read against the definition it follows; the only parallelism is an
+ * OpenMP loop over independent (row, head) or (query row, head) items.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -lm  (no fast-math: IEEE f64).
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * HeadPrep of one head of d values (gizml:netops reference page, Types > HeadPrep):
+ *   1. the head over its RMS, with eps inside the root: x_e / sqrt(mean(x^2) + eps)
+ *      (the same eps placement as layerNorm's sqrt(var + eps) on that page);
+ *   2. times its norm weight w_e;
+ *   3. values e < half turned with e + half by the row's cos and sin (split halves):
+ *        a' = a cos - b sin,  b' = b cos + a sin,  with a = x_e, b = x_{e+half};
+ *      values from 2*half on are left as they are; half = 0 means no turn.
+ */
+static void prep_one_head(double *x, int64_t d, const double *w,
+                          const double *cos_row, const double *sin_row, int64_t half,
+                          double eps)
+{
+    double ms = 0.0;
+    for (int64_t e = 0; e < d; ++e)
+        ms += x[e] * x[e];
+    ms /= (double)d;
+    const double root = sqrt(ms + eps);
+    for (int64_t e = 0; e < d; ++e)
+        x[e] = x[e] / root * w[e];
+    for (int64_t e = 0; e < half; ++e) {
+        const double a = x[e], b = x[e + half];
+        const double c = cos_row[e], s = sin_row[e];
+        x[e] = a * c - b * s;
+        x[e + half] = b * c + a * s;
+    }
+}
+
+int oracle_headprep(double *x, int64_t rows, int64_t heads, int64_t d,
+                    const double *w, const double *cos_t, const double *sin_t,
+                    int64_t half, int64_t table_rows, const int64_t *pos, double eps)
+{
+    if (!x || !w || rows < 0 || heads < 0 || d <= 0 || half < 0 || 2 * half > d || eps < 0)
+        return -1;
+    if (half > 0) {
+        if (!cos_t || !sin_t || !pos || table_rows <= 0)
+            return -1;
+        for (int64_t r = 0; r < rows; ++r)
+            if (pos[r] < 0 || pos[r] >= table_rows)
+                return -2;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t item = 0; item < rows * heads; ++item) {
+        const int64_t r = item / heads;
+        const double *c = half > 0 ? cos_t + pos[r] * half : NULL;
+        const double *s = half > 0 ? sin_t + pos[r] * half : NULL;
+        prep_one_head(x + item * d, d, w, c, s, half, eps);
+    }
+    return 0;
+}
+
+/*
+ * One output row of attention (gizml:netops reference page, Functions > attention,
+ * and Functions > causalMask for the visible keys):
+ *   s_j = scale * sum_p q_p k_jp for each visible key j, m = max_j s_j,
+ *   out = sum_j exp(s_j - m) v_j / sum_j exp(s_j - m).
+ * Visible keys: j < n, and j <= i + n - tq when causal.  No visible key: zeros.
+ * s is scratch of at least n doubles.
+ */
+static void attend_one(const double *q, const double *k, const double *v, double *out,
+                       int64_t b, int64_t i, int64_t h,
+                       int64_t tq, int64_t tk, int64_t hq, int64_t hkv,
+                       int64_t d, int64_t dv, double scale, int causal, int64_t n, double *s)
+{
+    const int64_t g = h / (hq / hkv);
+    const double *qi = q + ((b * tq + i) * hq + h) * d;
+    int64_t last = n - 1;                         /* last visible key */
+    if (causal && i + n - tq < last)
+        last = i + n - tq;
+    for (int64_t e = 0; e < dv; ++e)
+        out[e] = 0.0;
+    if (last < 0)
+        return;
+    double m = -INFINITY;
+    for (int64_t j = 0; j <= last; ++j) {
+        const double *kj = k + ((b * tk + j) * hkv + g) * d;
+        double dot = 0.0;
+        for (int64_t p = 0; p < d; ++p)
+            dot += qi[p] * kj[p];
+        s[j] = scale * dot;
+        if (s[j] > m)
+            m = s[j];
+    }
+    double sum = 0.0;
+    for (int64_t j = 0; j <= last; ++j) {
+        const double wj = exp(s[j] - m);
+        const double *vj = v + ((b * tk + j) * hkv + g) * dv;
+        sum += wj;
+        for (int64_t e = 0; e < dv; ++e)
+            out[e] += wj * vj[e];
+    }
+    for (int64_t e = 0; e < dv; ++e)
+        out[e] /= sum;
+}
+
+static int check_attention_args(const double *q, const double *k, const double *v,
+                                const double *out, int64_t batch, int64_t tq, int64_t tk,
+                                int64_t hq, int64_t hkv, int64_t d, int64_t dv,
+                                const int64_t *lens)
+{
+    if (!q || !k || !v || !out)
+        return -1;
+    if (batch < 0 || tq < 0 || tk < 0 || hq <= 0 || hkv <= 0 || d <= 0 || dv <= 0)
+        return -1;
+    if (hq % hkv != 0)
+        return -1;
+    if (lens)
+        for (int64_t b = 0; b < batch; ++b)
+            if (lens[b] < 0 || lens[b] > tk)
+                return -1;
+    return 0;
+}
+
+int oracle_attention(const double *q, const double *k, const double *v, double *out,
+                     int64_t batch, int64_t tq, int64_t tk, int64_t hq, int64_t hkv,
+                     int64_t d, int64_t dv, double scale, int causal, const int64_t *lens)
+{
+    if (check_attention_args(q, k, v, out, batch, tq, tk, hq, hkv, d, dv, lens))
+        return -1;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(tk > 0 ? tk : 1));
+        if (!s) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t item = 0; item < batch * tq * hq; ++item) {
+                const int64_t h = item % hq;
+                const int64_t i = (item / hq) % tq;
+                const int64_t b = item / (hq * tq);
+                const int64_t n = lens ? lens[b] : tk;
+                attend_one(q, k, v, out + item * dv, b, i, h, tq, tk, hq, hkv, d, dv,
+                           scale, causal, n, s);
+            }
+        }
+        free(s);
+    }
+    return bad ? -3 : 0;
+}
+
+int oracle_attention_rows(const double *q, const double *k, const double *v, double *out,
+                          int64_t batch, int64_t tq, int64_t tk, int64_t hq, int64_t hkv,
+                          int64_t d, int64_t dv, double scale, int causal, const int64_t *lens,
+                          const int64_t *sel, int64_t nsel)
+{
+    if (check_attention_args(q, k, v, out, batch, tq, tk, hq, hkv, d, dv, lens))
+        return -1;
+    if (nsel < 0 || (nsel > 0 && !sel))
+        return -1;
+    for (int64_t r = 0; r < nsel; ++r) {
+        const int64_t b = sel[3 * r], i = sel[3 * r + 1], h = sel[3 * r + 2];
+        if (b < 0 || b >= batch || i < 0 || i >= tq || h < 0 || h >= hq)
+            return -1;
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(tk > 0 ? tk : 1));
+        if (!s) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t r = 0; r < nsel; ++r) {
+                const int64_t b = sel[3 * r], i = sel[3 * r + 1], h = sel[3 * r + 2];
+                const int64_t n = lens ? lens[b] : tk;
+                attend_one(q, k, v, out + r * dv, b, i, h, tq, tk, hq, hkv, d, dv,
+                           scale, causal, n, s);
+            }
+        }
+        free(s);
+    }
+    return bad ? -3 : 0;
+}

@@ -1,0 +1,69 @@
+/*
+ * oracle.h -- plain f64 CPU oracle for HeadPrep and scaled-dot-product attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is the checker that the GPU library is
+ * compared against.  Only the test suite, the smoke check and the CPU-baseline leg
+ * of the benchmark may load it.  It shares no code, header, table or helper with
+ * the GPU library, and the GPU library never calls it.
+ *
+ * Everything is f64 and follows the plain definitions:
+ *   - HeadPrep: gizml:netops reference page, "Types > HeadPrep".
+ *   - attention, causal mask: gizml:netops reference page, "Functions > attention"
+ *     and "Functions > causalMask".
+ * Layouts are row-major, token rows with heads contiguous inside a row.
+ * Every function returns 0 on success and a negative value on a bad argument
+ * (nothing is written in that case).
+ */
+#ifndef ATTN_ORACLE_H
+#define ATTN_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * HeadPrep, in place, on x laid out [rows, heads, d].
+ *   Each head of each row: divide by sqrt(mean of squares + eps), multiply by w[e],
+ *   then for e < half turn the pair (e, e + half) by the angle whose cosine and sine
+ *   are cos_t[pos[row] * half + e], sin_t[pos[row] * half + e].  Values e >= 2*half
+ *   keep their normalised, weighted value.  half == 0 means no rotation.
+ *   w: [d]; cos_t, sin_t: [table_rows, half]; pos: [rows] table rows.
+ * Returns -1 on a bad size, -2 if a position lies outside [0, table_rows).
+ */
+int oracle_headprep(double *x, int64_t rows, int64_t heads, int64_t d,
+                    const double *w, const double *cos_t, const double *sin_t,
+                    int64_t half, int64_t table_rows, const int64_t *pos, double eps);
+
+/*
+ * Scaled-dot-product attention, plain definition.
+ *   q [batch, tq, hq, d], k [batch, tk, hkv, d], v [batch, tk, hkv, dv] -> out [batch, tq, hq, dv].
+ *   q head h reads kv head h / (hq / hkv).
+ *   Keys visible to query i of sequence b: j < n_b, where n_b = lens ? lens[b] : tk,
+ *   and, when causal, j <= i + n_b - tq (bottom-right alignment).
+ *   out = sum_j exp(s_j - max s) v_j / sum_j exp(s_j - max s), s_j = scale * q.k_j.
+ *   A query with no visible key gets an all-zero output row.
+ * Returns -1 on a bad size (hq not a multiple of hkv, lens[b] outside [0, tk], ...).
+ */
+int oracle_attention(const double *q, const double *k, const double *v, double *out,
+                     int64_t batch, int64_t tq, int64_t tk, int64_t hq, int64_t hkv,
+                     int64_t d, int64_t dv, double scale, int causal, const int64_t *lens);
+
+/*
+ * The same attention, only for the nsel query rows named in sel ([nsel, 3] triples
+ * (b, i, h)); out is [nsel, dv].  Used to check very large workloads on a sample.
+ */
+int oracle_attention_rows(const double *q, const double *k, const double *v, double *out,
+                          int64_t batch, int64_t tq, int64_t tk, int64_t hq, int64_t hkv,
+                          int64_t d, int64_t dv, double scale, int causal, const int64_t *lens,
+                          const int64_t *sel, int64_t nsel);
+
+/* Number of OpenMP threads a parallel region of this library uses. */
+int oracle_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,166 @@
+"""ctypes binding of the f64 oracle (``oracle.c``) plus the path's two compositions.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Inputs are numpy arrays of any
+float dtype; they are widened to f64, which is exact for f32 and bf16 values.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_lp = ctypes.POINTER(ctypes.c_int64)
+
+
+def library_path() -> str:
+    return _LIB
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (IEEE f64, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(
+            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+             "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"],
+            check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_headprep.argtypes = [_dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                        _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, _lp,
+                                        ctypes.c_double]
+        lib.oracle_headprep.restype = ctypes.c_int
+        att = [_dp, _dp, _dp, _dp] + [ctypes.c_int64] * 7 + [ctypes.c_double, ctypes.c_int, _lp]
+        lib.oracle_attention.argtypes = att
+        lib.oracle_attention.restype = ctypes.c_int
+        lib.oracle_attention_rows.argtypes = att + [_lp, ctypes.c_int64]
+        lib.oracle_attention_rows.restype = ctypes.c_int
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def threads() -> int:
+    return int(_load().oracle_threads())
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    if a is None:
+        return None
+    if a.dtype == np.float64:
+        return a.ctypes.data_as(_dp)
+    return a.ctypes.data_as(_lp)
+
+
+def headprep(x, w, cos, sin, half: int, pos, eps: float) -> np.ndarray:
+    """HeadPrep of x [..., heads, d] (gizml:netops, Types > HeadPrep), returned as a new
+    f64 array.  ``pos`` gives the table row of each leading index (shape x.shape[:-2])."""
+    x = _f64(x).copy()
+    d = x.shape[-1]
+    heads = x.shape[-2]
+    rows = int(np.prod(x.shape[:-2], dtype=np.int64))
+    w = _f64(w)
+    assert w.shape == (d,)
+    if half > 0:
+        cos = _f64(cos)
+        sin = _f64(sin)
+        assert cos.shape == sin.shape and cos.shape[1] == half
+        table_rows = cos.shape[0]
+        pos = np.ascontiguousarray(np.broadcast_to(np.asarray(pos, dtype=np.int64),
+                                                   x.shape[:-2])).reshape(-1)
+    else:
+        cos = sin = None
+        table_rows = 0
+        pos = None
+    rc = _load().oracle_headprep(_ptr(x), rows, heads, d, _ptr(w), _ptr(cos), _ptr(sin),
+                                 half, table_rows, _ptr(pos), float(eps))
+    if rc != 0:
+        raise ValueError("oracle_headprep rejected its arguments (code %d)" % rc)
+    return x
+
+
+def _attention_shapes(q, k, v):
+    batch, tq, hq, d = q.shape
+    bk, tk, hkv, dk = k.shape
+    bv, tv, hv, dv = v.shape
+    assert bk == batch and bv == batch and tv == tk and hv == hkv and dk == d
+    return batch, tq, tk, hq, hkv, d, dv
+
+
+def attention(q, k, v, scale: float, causal: bool, lens=None) -> np.ndarray:
+    """softmax(q k^T scale [+ causal mask]) v in f64 (gizml:netops, Functions > attention).
+    q [B, tq, hq, d], k [B, tk, hkv, d], v [B, tk, hkv, dv] -> [B, tq, hq, dv]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    batch, tq, tk, hq, hkv, d, dv = _attention_shapes(q, k, v)
+    out = np.zeros((batch, tq, hq, dv), dtype=np.float64)
+    lens_a = None if lens is None else np.ascontiguousarray(np.asarray(lens, dtype=np.int64))
+    rc = _load().oracle_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), batch, tq, tk, hq,
+                                  hkv, d, dv, float(scale), int(bool(causal)), _ptr(lens_a))
+    if rc != 0:
+        raise ValueError("oracle_attention rejected its arguments (code %d)" % rc)
+    return out
+
+
+def attention_rows(q, k, v, scale: float, causal: bool, sel, lens=None) -> np.ndarray:
+    """The attention output only for the query rows sel = [(b, i, h), ...] -> [nsel, dv]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    batch, tq, tk, hq, hkv, d, dv = _attention_shapes(q, k, v)
+    sel = np.ascontiguousarray(np.asarray(sel, dtype=np.int64).reshape(-1, 3))
+    out = np.zeros((sel.shape[0], dv), dtype=np.float64)
+    lens_a = None if lens is None else np.ascontiguousarray(np.asarray(lens, dtype=np.int64))
+    rc = _load().oracle_attention_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(out), batch, tq, tk,
+                                       hq, hkv, d, dv, float(scale), int(bool(causal)),
+                                       _ptr(lens_a), _ptr(sel), sel.shape[0])
+    if rc != 0:
+        raise ValueError("oracle_attention_rows rejected its arguments (code %d)" % rc)
+    return out
+
+
+def prefill(q, k, v, qw, kw, cos, sin, half: int, eps: float, pos0: int, scale: float,
+            causal: bool = True, sel=None, prep: bool = True):
+    """HeadPrep of q and k at positions pos0 + t (headPrepInPlace's row rule), then
+    attention.  Returns (out, k_prepped); with ``sel`` only those query rows of out.
+    With prep=False the inputs go to attention unchanged."""
+    seq = q.shape[1]
+    if prep:
+        pos = (pos0 + np.arange(seq, dtype=np.int64))[None, :].repeat(q.shape[0], axis=0)
+        qh = headprep(q, qw, cos, sin, half, pos, eps)
+        kh = headprep(k, kw, cos, sin, half, pos, eps)
+    else:
+        qh, kh = _f64(q), _f64(k)
+    if sel is None:
+        out = attention(qh, kh, v, scale, causal)
+    else:
+        out = attention_rows(qh, kh, v, scale, causal, sel)
+    return out, kh
+
+
+def decode(q, k_cache, v_cache, lens, pos, qw, cos, sin, half: int, eps: float,
+           scale: float) -> np.ndarray:
+    """One new query row per sequence: q [B, hq, d] prepped at table row pos[b], then
+    attention over the first lens[b] rows of the (already prepped) cache
+    [B, capacity, hkv, d].  Returns [B, hq, dv]."""
+    q = _f64(q)
+    qh = headprep(q[:, None], qw, cos, sin, half, np.asarray(pos, dtype=np.int64)[:, None], eps)
+    out = attention(qh, k_cache, v_cache, scale, causal=False, lens=lens)
+    return out[:, 0]

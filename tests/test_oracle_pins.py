@@ -1,0 +1,324 @@
+"""Pins of the f64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a hand-worked
+example, a library routine (torch's rms_norm and scaled_dot_product_attention, numpy's
+complex product), a closed form, or an invariant of the definition.  Together they are
+chosen so that a dropped term, a wrong sign, a wrong pairing or table row, a missing
+scale, a misaligned mask or a wrong head grouping fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import synthetic
+
+RNG = np.random.default_rng(1234)
+
+
+def _angles_tables(rows, half, d, base=1e4):
+    """Exact f64 tables (no f32 rounding), for the relative-position invariant."""
+    p = np.arange(rows, dtype=np.float64)[:, None]
+    i = np.arange(half, dtype=np.float64)[None, :]
+    ang = p * base ** (-2.0 * i / d)
+    return np.cos(ang), np.sin(ang)
+
+
+def _torch_rmsnorm(x, w, eps):
+    xt = torch.from_numpy(np.asarray(x, dtype=np.float64))
+    return F.rms_norm(xt, (xt.shape[-1],), weight=torch.from_numpy(np.asarray(w, np.float64)),
+                      eps=eps).numpy()
+
+
+# ---------------------------------------------------------------------------- HeadPrep
+
+def test_headprep_worked_examples(golden_dir):
+    with open(os.path.join(golden_dir, "headprep_worked.json")) as f:
+        spec = json.load(f)
+    for case in spec["cases"]:
+        x = np.array(case["x"])[None, None, :]
+        half = case["half"]
+        cos = np.array(case["cos"], dtype=np.float64).reshape(-1, half) if half else None
+        sin = np.array(case["sin"], dtype=np.float64).reshape(-1, half) if half else None
+        got = oracle.headprep(x, case["w"], cos, sin, half, [case["pos"]], case["eps"])
+        np.testing.assert_allclose(got[0, 0], case["expect"], rtol=0, atol=1e-15,
+                                   err_msg=case["name"])
+
+
+@pytest.mark.parametrize("d", [4, 64, 128])
+def test_unit_rms_before_weight(d):
+    """With w = 1 and no turn, each head's RMS is sqrt(ms / (ms + eps))."""
+    eps = 1e-3
+    x = RNG.standard_normal((7, 3, d)) * RNG.uniform(0.01, 10, (7, 3, 1))
+    got = oracle.headprep(x, np.ones(d), None, None, 0, 0, eps)
+    ms = (x ** 2).mean(-1)
+    np.testing.assert_allclose(np.sqrt((got ** 2).mean(-1)), np.sqrt(ms / (ms + eps)),
+                               rtol=1e-13, atol=0)
+
+
+def test_norm_weight_matches_torch_rms_norm():
+    """half = 0 reduces HeadPrep to torch's rms_norm with the same weight and eps."""
+    d = 64
+    x = RNG.standard_normal((5, 4, d)) * 3
+    w = RNG.uniform(0.5, 1.5, d)
+    for eps in (0.0, 1e-6, 0.25):
+        got = oracle.headprep(x, w, None, None, 0, 0, eps)
+        np.testing.assert_allclose(got, _torch_rmsnorm(x, w, eps), rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("d,half", [(64, 32), (128, 64), (128, 32), (10, 3)])
+def test_turn_is_complex_multiplication(d, half):
+    """The split-half turn of pair (e, e+half) is (a + ib) * (cos + i sin)."""
+    rows, heads = 6, 3
+    x = RNG.standard_normal((rows, heads, d))
+    w = RNG.uniform(0.5, 1.5, d)
+    ang = RNG.uniform(-math.pi, math.pi, (9, half))
+    cos, sin = np.cos(ang), np.sin(ang)
+    pos = RNG.integers(0, 9, rows)
+    got = oracle.headprep(x, w, cos, sin, half, pos, 1e-6)
+    n = _torch_rmsnorm(x, w, 1e-6)
+    z = (n[..., :half] + 1j * n[..., half:2 * half]) * np.exp(1j * ang[pos])[:, None, :]
+    np.testing.assert_allclose(got[..., :half], z.real, atol=1e-14)
+    np.testing.assert_allclose(got[..., half:2 * half], z.imag, atol=1e-14)
+    np.testing.assert_allclose(got[..., 2 * half:], n[..., 2 * half:], rtol=0, atol=1e-14)
+
+
+def test_pair_norm_preserved_and_position_zero_identity():
+    d, half = 128, 64
+    x = RNG.standard_normal((4, 2, d))
+    w = RNG.uniform(0.5, 1.5, d)
+    cos, sin = synthetic.rope_tables(64, half, d, 1e4)
+    pos = np.array([0, 5, 17, 63])
+    got = oracle.headprep(x, w, cos.astype(np.float64), sin.astype(np.float64), half, pos, 1e-6)
+    plain = oracle.headprep(x, w, None, None, 0, 0, 1e-6)
+    # |cos|^2 + |sin|^2 of the f32 table entries is 1 within f32 rounding
+    c2s2 = cos.astype(np.float64) ** 2 + sin.astype(np.float64) ** 2
+    before = plain[..., :half] ** 2 + plain[..., half:] ** 2
+    after = got[..., :half] ** 2 + got[..., half:] ** 2
+    np.testing.assert_allclose(after, before * c2s2[pos][:, None, :], rtol=1e-13)
+    np.testing.assert_allclose(np.abs(c2s2 - 1).max(), 0, atol=3e-7)
+    # position 0: cos = 1, sin = 0 exactly, so the turn is the identity
+    np.testing.assert_array_equal(got[0], plain[0])
+
+
+def test_scale_invariance():
+    """prep(c x) = prep(x) up to eps: why scaled outlier keys are inert after HeadPrep."""
+    d, half = 128, 64
+    x = RNG.standard_normal((3, 2, d))
+    w = RNG.uniform(0.5, 1.5, d)
+    cos, sin = _angles_tables(8, half, d)
+    a = oracle.headprep(x, w, cos, sin, half, [1, 4, 7], 1e-6)
+    b = oracle.headprep(8.0 * x, w, cos, sin, half, [1, 4, 7], 1e-6)
+    assert np.abs(a - b).max() < 1e-5
+    assert np.abs(a - b).max() > 0  # eps really is in the formula
+
+
+def test_relative_position():
+    """A q.k score depends on the two positions only through their difference."""
+    d, half = 64, 32
+    cos, sin = _angles_tables(300, half, d)
+    q = RNG.standard_normal((1, 1, d))
+    k = RNG.standard_normal((1, 1, d))
+    w = RNG.uniform(0.5, 1.5, d)
+    scores = []
+    for s in (0, 13, 100, 250):
+        qh = oracle.headprep(q, w, cos, sin, half, [s + 40], 1e-6)
+        kh = oracle.headprep(k, w, cos, sin, half, [s + 7], 1e-6)
+        scores.append(float((qh * kh).sum()))
+    np.testing.assert_allclose(scores, scores[0], rtol=0, atol=1e-11)
+
+
+def test_headprep_rejects_bad_arguments():
+    x = np.zeros((2, 1, 8))
+    cos = np.ones((3, 4))
+    with pytest.raises(ValueError):
+        oracle.headprep(x, np.ones(8), cos, cos, 4, [0, 3], 1e-6)   # position past the table
+    with pytest.raises(ValueError):
+        oracle.headprep(x, np.ones(8), np.ones((3, 5)), np.ones((3, 5)), 5, [0, 1], 1e-6)
+
+
+# --------------------------------------------------------------------------- attention
+
+def test_attention_worked_examples(golden_dir):
+    with open(os.path.join(golden_dir, "attention_worked.json")) as f:
+        spec = json.load(f)
+    k = np.array(spec["k"])[None]      # [1, tk, hkv, d]
+    v = np.array(spec["v"])[None]
+    for case in spec["cases"]:
+        q = np.tile(np.array(spec["q_row"]), (1, case["tq"], spec["hq"], 1))
+        got = oracle.attention(q, k, v, spec["scale"], case["causal"])
+        np.testing.assert_allclose(got[0], np.array(case["expect"], dtype=np.float64),
+                                   rtol=0, atol=1e-14, err_msg=case["name"])
+
+
+def _bottom_right_mask(tq, tk):
+    i = np.arange(tq)[:, None]
+    j = np.arange(tk)[None, :]
+    return j <= i + tk - tq
+
+
+@pytest.mark.parametrize("tq,tk,causal", [(6, 6, True), (6, 6, False), (3, 9, True),
+                                          (1, 9, True), (5, 8, False)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (6, 1)])
+def test_attention_matches_torch_sdpa(tq, tk, causal, hq, hkv):
+    """torch's SDPA in f64 with an explicit bottom-right mask and grouped heads."""
+    b, d, dv = 2, 8, 5
+    q = RNG.standard_normal((b, tq, hq, d))
+    k = RNG.standard_normal((b, tk, hkv, d))
+    v = RNG.standard_normal((b, tk, hkv, dv))
+    scale = 0.37
+    got = oracle.attention(q, k, v, scale, causal)
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(hq // hkv, dim=1)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(hq // hkv, dim=1)
+    mask = torch.from_numpy(_bottom_right_mask(tq, tk)) if causal else None
+    ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+    np.testing.assert_allclose(got, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-13)
+
+
+def test_softmax_weights_sum_to_one():
+    q = RNG.standard_normal((2, 9, 2, 16)) * 3
+    k = RNG.standard_normal((2, 9, 1, 16)) * 3
+    v = np.ones((2, 9, 1, 4))
+    got = oracle.attention(q, k, v, 0.5, True)
+    np.testing.assert_allclose(got, 1.0, rtol=0, atol=1e-14)
+
+
+def test_one_key_returns_v():
+    q = RNG.standard_normal((3, 1, 2, 16))
+    k = RNG.standard_normal((3, 1, 1, 16))
+    v = RNG.standard_normal((3, 1, 1, 7))
+    got = oracle.attention(q, k, v, 0.125, True)
+    np.testing.assert_array_equal(got, np.repeat(v, 2, axis=2))
+
+
+def test_zero_query_gives_prefix_means():
+    """q = 0: all scores 0, so causal row i is the mean of v rows 0..i (closed form)."""
+    s, d = 11, 8
+    q = np.zeros((1, s, 1, d))
+    k = RNG.standard_normal((1, s, 1, d))
+    v = RNG.standard_normal((1, s, 1, 3))
+    got = oracle.attention(q, k, v, 1.0, True)
+    means = np.cumsum(v[0, :, 0], axis=0) / np.arange(1, s + 1)[:, None]
+    np.testing.assert_allclose(got[0, :, 0], means, atol=1e-15)
+
+
+def test_causality():
+    """Changing keys or values after row i leaves rows up to i exactly unchanged."""
+    s, d = 12, 16
+    q = RNG.standard_normal((1, s, 2, d))
+    k = RNG.standard_normal((1, s, 2, d))
+    v = RNG.standard_normal((1, s, 2, d))
+    a = oracle.attention(q, k, v, 0.25, True)
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 7:] = RNG.standard_normal(k2[:, 7:].shape)
+    v2[:, 7:] = RNG.standard_normal(v2[:, 7:].shape)
+    b = oracle.attention(q, k2, v2, 0.25, True)
+    np.testing.assert_array_equal(a[:, :7], b[:, :7])
+    assert np.abs(a[:, 7:] - b[:, 7:]).max() > 1e-3
+
+
+def test_grouped_heads_equal_repeated_heads():
+    q = RNG.standard_normal((2, 10, 8, 16))
+    k = RNG.standard_normal((2, 10, 2, 16))
+    v = RNG.standard_normal((2, 10, 2, 16))
+    a = oracle.attention(q, k, v, 0.25, True)
+    b = oracle.attention(q, np.repeat(k, 4, axis=2), np.repeat(v, 4, axis=2), 0.25, True)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_dominant_key():
+    q = np.zeros((1, 1, 1, 4))
+    q[..., 0] = 1.0
+    k = RNG.standard_normal((1, 6, 1, 4)) * 0.1
+    k[0, 3, 0, 0] = 100.0
+    v = RNG.standard_normal((1, 6, 1, 4))
+    got = oracle.attention(q, k, v, 1.0, False)
+    np.testing.assert_allclose(got[0, 0, 0], v[0, 3, 0], atol=1e-30 + 1e-40)
+
+
+def test_lens_equal_truncated_cache_and_empty_rows_are_zero():
+    q = RNG.standard_normal((3, 1, 4, 16))
+    k = RNG.standard_normal((3, 20, 2, 16))
+    v = RNG.standard_normal((3, 20, 2, 16))
+    lens = [20, 7, 0]
+    got = oracle.attention(q, k, v, 0.25, False, lens=lens)
+    for b, n in enumerate(lens[:2]):
+        ref = oracle.attention(q[b:b + 1], k[b:b + 1, :n], v[b:b + 1, :n], 0.25, False)
+        np.testing.assert_array_equal(got[b], ref[0])
+    np.testing.assert_array_equal(got[2], 0.0)
+
+
+def test_rows_sample_equals_full():
+    q = RNG.standard_normal((2, 33, 4, 16))
+    k = RNG.standard_normal((2, 33, 2, 16))
+    v = RNG.standard_normal((2, 33, 2, 16))
+    full = oracle.attention(q, k, v, 0.25, True)
+    sel = [(0, 0, 0), (1, 32, 3), (0, 17, 2), (1, 5, 1)]
+    got = oracle.attention_rows(q, k, v, 0.25, True, sel)
+    for r, (b, i, h) in enumerate(sel):
+        np.testing.assert_array_equal(got[r], full[b, i, h])
+
+
+# -------------------------------------------------------------------------- the path
+
+def test_decode_equals_prefill_row():
+    """KV-cache equivalence: decode of position p over the cache prefill prepped
+    (first p+1 rows) equals prefill's output row p."""
+    w = synthetic.WORKLOADS["prefill_f32"]
+    inp = synthetic.make_prefill(w, seq=24, batch=2)
+    out, kh = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["qw"], inp["kw"], inp["cos"],
+                             inp["sin"], w.half, w.eps, 0, w.scale, True)
+    for p in (0, 9, 23):
+        lens = np.full(2, p + 1)
+        dec = oracle.decode(inp["q"][:, p], kh, inp["v"], lens, np.full(2, p), inp["qw"],
+                            inp["cos"], inp["sin"], w.half, w.eps, w.scale)
+        np.testing.assert_allclose(dec, out[:, p], rtol=0, atol=1e-14)
+
+
+def test_tiny_workload_end_to_end_against_library_routines():
+    """The tiny f32 workload: oracle prefill vs torch rms_norm + complex turn + SDPA."""
+    w = synthetic.WORKLOADS["tiny_f32"]
+    inp = synthetic.make_prefill(w)
+    out, _ = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["qw"], inp["kw"], inp["cos"],
+                            inp["sin"], w.half, w.eps, 0, w.scale, True)
+
+    def prep(x, wt):
+        n = _torch_rmsnorm(x, wt, w.eps)
+        ang = np.arctan2(inp["sin"].astype(np.float64), inp["cos"].astype(np.float64))
+        rad = np.hypot(inp["sin"].astype(np.float64), inp["cos"].astype(np.float64))
+        z = (n[..., :w.half] + 1j * n[..., w.half:]) * (rad * np.exp(1j * ang))[None, :, None]
+        return np.concatenate([z.real, z.imag], axis=-1)
+
+    qh, kh = prep(inp["q"], inp["qw"]), prep(inp["k"], inp["kw"])
+    ref = F.scaled_dot_product_attention(
+        torch.from_numpy(qh).permute(0, 2, 1, 3), torch.from_numpy(kh).permute(0, 2, 1, 3),
+        torch.from_numpy(inp["v"].astype(np.float64)).permute(0, 2, 1, 3),
+        attn_mask=torch.from_numpy(_bottom_right_mask(w.seq, w.seq)), scale=w.scale)
+    np.testing.assert_allclose(out, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------------- input generation
+
+def test_bf16_rounding_matches_torch():
+    x = np.concatenate([RNG.standard_normal(100000) * 10.0 ** RNG.integers(-6, 6, 100000),
+                        np.array([1.00390625, 1.01171875, -1.00390625, 0.0, 3.0e38])])
+    got = synthetic.bf16_round(x)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_workload_shapes_and_tables():
+    w = synthetic.WORKLOADS["long_prefill_bf16"]
+    inp = synthetic.make_prefill(w, seq=1000, batch=1)
+    assert inp["q"].shape == (1, 1000, 64, 128) and inp["k"].shape == (1, 1000, 8, 128)
+    assert len(inp["outliers"]) == 10
+    np.testing.assert_array_equal(synthetic.bf16_round(inp["k"]), inp["k"])
+    cos, sin = synthetic.rope_tables(5, 64, 128, 1e6)
+    ang = 3 * 1e6 ** (-2 * 5 / 128)
+    assert cos[3, 5] == np.float32(math.cos(ang)) and sin[3, 5] == np.float32(math.sin(ang))

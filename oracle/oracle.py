@@ -39,8 +39,10 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        # A planted-mistake copy of the oracle (built by the mutation test) can be
+        # swapped in through this variable; by default the library built from oracle.c.
+        path = os.environ.get("ATTN_ORACLE_LIB") or build()
+        lib = ctypes.CDLL(path)
         lib.oracle_headprep.argtypes = [_dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                         _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, _lp,
                                         ctypes.c_double]

@@ -1,0 +1,57 @@
+"""Planted mistakes in the oracle, on the CPU: each must make a pin fail.
+
+Each mutant is oracle.c with one plausible slip (a dropped term, a wrong sign, a wrong
+pairing or table row, a missing scale, a misaligned mask, a wrong head grouping).  It
+is compiled to a temporary library and the pin suite is run against it in a child
+process; the suite has to fail.  This shows the pins are not blind to the slip.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "eps outside the root": ("sqrt(ms + eps)", "(sqrt(ms) + eps)"),
+    "eps dropped": ("sqrt(ms + eps)", "sqrt(ms)"),
+    "weight dropped": ("x[e] / root * w[e]", "x[e] / root"),
+    "sum not divided by d": ("ms /= (double)d;", ";"),
+    "wrong turn sign": ("x[e + half] = b * c + a * s;", "x[e + half] = b * c - a * s;"),
+    "turn the other way": ("x[e] = a * c - b * s;\n        x[e + half] = b * c + a * s;",
+                           "x[e] = a * c + b * s;\n        x[e + half] = b * c - a * s;"),
+    "adjacent pairs": ("const double a = x[e], b = x[e + half];",
+                       "const double a = x[e], b = x[e + 1];"),
+    "table row off by one": ("cos_t + pos[r] * half", "cos_t + (pos[r] ? pos[r] - 1 : 0) * half"),
+    "cos and sin swapped": ("const double c = cos_row[e], s = sin_row[e];",
+                            "const double c = sin_row[e], s = cos_row[e];"),
+    "scale dropped": ("s[j] = scale * dot;", "s[j] = dot;"),
+    "top-left causal mask": ("if (causal && i + n - tq < last)\n        last = i + n - tq;",
+                             "if (causal && i < last)\n        last = i;"),
+    "interleaved head groups": ("const int64_t g = h / (hq / hkv);",
+                                "const int64_t g = h % hkv;"),
+    "max not subtracted consistently": ("const double wj = exp(s[j] - m);",
+                                        "const double wj = exp(s[j] - m) * (j == 0 ? 2.0 : 1.0);"),
+    "value of wrong key": ("const double *vj = v + ((b * tk + j) * hkv + g) * dv;",
+                           "const double *vj = v + ((b * tk + (j ? j - 1 : 0)) * hkv + g) * dv;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site not found: " + name
+    mutant = tmp_path / "oracle_mutant.c"
+    mutant.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+                    "-I", os.path.join(ROOT, "oracle"), str(mutant), "-o", str(lib), "-lm"],
+                   check=True)
+    env = dict(os.environ, ATTN_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "no pin caught the mutant '%s':\n%s" % (name, r.stdout[-2000:])

@@ -1,0 +1,190 @@
+#!/usr/bin/env python3
+"""Benchmark of the HeadPrep + attention path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic inputs:
+  1. HeadPrep of k in place (attn_prep)                       -- bf16 prefill workload
+  2. causal attention with q's HeadPrep fused (attn_prefill)   -- bf16 prefill workload
+  3. single-row decode against a 4096-row KV cache (attn_decode) -- bf16 decode workload
+Workloads: prefill batch 4 x 2048 tokens, 32 q heads over 8 kv heads, d 128 (rotary
+base 1e4); decode batch 32, 32 q heads over 8 kv heads, d 128, cache 4096 rows, query
+at position 4096.  Inputs are seeded synthetic N(0, 1) operands (synthetic.py) already
+resident in HBM; the decode step rotates through several cache copies so repeats are
+not served from the 256 MB last-level cache.
+
+Printed: one JSON line.  `value` is the prefill rate (algorithmic flops of the visible
+causal pairs, 4 d per (query, key, head), over the time of steps 1-2), the decode rate
+(algorithmic bytes over the time of step 3) is under "decode".  `roofline` is the
+attention kernel's (step 2 alone), with HIP events on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+
+def prefill_flops(w) -> int:
+    pairs = w.seq * (w.seq + 1) // 2 if w.causal else w.seq * w.seq
+    return 4 * w.d * pairs * w.batch * w.hq
+
+
+def decode_bytes(w) -> int:
+    kv = 2 * w.batch * w.seq * w.hkv * w.d * 2
+    qo = 2 * w.batch * w.hq * w.d * 2
+    return kv + qo + 2 * w.half * 4 + w.d * 4     # + one cos/sin table row + qw
+
+
+def cpu_baseline(w, inp) -> dict:
+    """The f64 oracle, as it stands, on the full prefill workload (HeadPrep of q and k
+    plus attention of every query row) on this host's cores."""
+    import oracle
+    t0 = time.perf_counter()
+    oracle.prefill(inp["q"], inp["k"], inp["v"], inp["qw"], inp["kw"], inp["cos"], inp["sin"],
+                   w.half, w.eps, 0, w.scale, True)
+    dt = time.perf_counter() - t0
+    return {"value": round(prefill_flops(w) / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": "the whole bf16 prefill workload (4 x 2048 tokens, 32/8 heads, d 128): "
+                      "HeadPrep of q and k and causal attention of every row, f64, %.1f s" % dt,
+            "host_cpu": platform.processor() or platform.machine()}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cache-copies", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path is built and timed on a single MI355X "
+              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synthetic
+    import transformer_attention_headprep_amd as tah
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+
+    def to(x, dt="bf16"):
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+        return (t.to(torch.bfloat16) if dt == "bf16" else t).to(dev)
+
+    wp = synthetic.WORKLOADS["prefill_bf16"]
+    wd = synthetic.WORKLOADS["decode_bf16"]
+    ip = synthetic.make_prefill(wp)
+    idc = synthetic.make_decode(wd)
+
+    # prefill operands
+    q3, k3, v3 = to(ip["q"]), to(ip["k"]), to(ip["v"])
+    out3 = torch.empty_like(q3)
+    prep3 = tah.HeadPrep(to(ip["qw"], "f32"), to(ip["kw"], "f32"), to(ip["cos"], "f32"),
+                         to(ip["sin"], "f32"), wp.eps)
+    prep3_q = tah.HeadPrep(prep3.qw, None, prep3.cos, prep3.sin, wp.eps)   # k already prepped
+
+    # decode operands: caches prepped on the GPU (HeadPrep at positions 0 .. 4095)
+    prep4 = tah.HeadPrep(to(idc["qw"], "f32"), to(idc["kw"], "f32"), to(idc["cos"], "f32"),
+                         to(idc["sin"], "f32"), wd.eps)
+    q4 = to(idc["q"])
+    k_raw = to(idc["k_raw"])
+    tah.attn_prep(None, k_raw, prep4, pos0=0)
+    kcs = [k_raw] + [k_raw.clone() for _ in range(args.cache_copies - 1)]
+    v_raw = to(idc["v"])
+    vcs = [v_raw] + [v_raw.clone() for _ in range(args.cache_copies - 1)]
+    lens = torch.tensor(idc["lens"], device=dev)
+    pos = torch.tensor(idc["pos"], device=dev)
+    splits = tah.decode_default_splits(wd.batch, wd.hq, wd.hkv, wd.seq)
+    ws = torch.empty(tah.decode_workspace_size(wd.batch, wd.hq, wd.hkv, wd.d, wd.seq, splits),
+                     dtype=torch.uint8, device=dev)
+    out4 = torch.empty_like(q4)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        tah.attn_prep(None, k3, prep3, pos0=0, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        tah.attn_prefill(q3, k3, v3, out3, prep=prep3_q, causal=True, scale=wp.scale, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        c = i % len(kcs)
+        tah.attn_decode(q4, kcs[c], vcs[c], lens, pos, wd.seq, prep=prep4, scale=wd.scale,
+                        splits=splits, workspace=ws, out=out4, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    prep_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    attn_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+    flops = prefill_flops(wp)
+    nbytes = decode_bytes(wd)
+    pre_tflops = flops / ((prep_ms + attn_ms).mean() * 1e-3) / 1e12
+    attn_tflops = flops / (attn_ms.mean() * 1e-3) / 1e12
+    dec_gbps = nbytes / (dec_ms.mean() * 1e-3) / 1e9
+
+    line = {
+        "metric": "prefill attention TFLOP/s + decode HBM GB/s (HeadPrep fused), 1 MI355X",
+        "value": round(pre_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) operands, U(0.5,1.5) norm weights, f32 rotary tables)",
+        "config": {
+            "workload": "bf16 prefill (batch 4, seq 2048, 32 q / 8 kv heads, d 128, causal) + "
+                        "bf16 decode (batch 32, cache 4096, 32 q / 8 kv heads, d 128)",
+            "prefill": {"batch": wp.batch, "seq": wp.seq, "hq": wp.hq, "hkv": wp.hkv, "d": wp.d,
+                        "half": wp.half, "rotary_base": wp.base, "causal": True},
+            "decode": {"batch": wd.batch, "cache": wd.seq, "query_position": wd.seq, "hq": wd.hq,
+                       "hkv": wd.hkv, "d": wd.d, "splits": splits, "cache_copies": len(kcs)},
+        },
+        "parts_ms": {"k_headprep": round(float(prep_ms.mean()), 5),
+                     "prefill_attention": round(float(attn_ms.mean()), 5),
+                     "decode": round(float(dec_ms.mean()), 5),
+                     "prefill_attention_min": round(float(attn_ms.min()), 5),
+                     "decode_min": round(float(dec_ms.min()), 5)},
+        "decode": {"value": round(dec_gbps, 2), "unit": "GB/s", "bytes": nbytes,
+                   "frac_of_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4)},
+        "roofline": {"kernel": "prefill_bf16_kernel (attention, q HeadPrep fused)",
+                     "bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wp, ip)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,168 @@
+/*
+ * attn.h -- C ABI of libattn: HeadPrep and scaled-dot-product attention (causal
+ * prefill, single-row decode against a KV cache, grouped K/V heads) on AMD
+ * MI355X (gfx950).
+ *
+ * What is computed (gizml:netops reference page):
+ *   - HeadPrep (Types > HeadPrep): each head of q and k is divided by
+ *     sqrt(mean of its squares + eps), multiplied by its norm weight (qw for q,
+ *     kw for k: one [d] f32 vector shared by every head), then every value e < half
+ *     is turned with value e + half by the cosine and sine of its row:
+ *         a' = a cos - b sin,   b' = b cos + a sin   (a = x[e], b = x[e + half]).
+ *     Values from 2*half on keep their normed, weighted value; half = 0: no turn.
+ *   - The cos/sin row of a token is its sequence position (Functions >
+ *     headPrepInPlace: row0 is the sequence row of the first row).
+ *   - attention (Functions > attention, Functions > causalMask):
+ *         out = softmax(q k^T * scale [+ mask]) v,
+ *     where with causal query i sees key j iff j <= i + tk - tq.  The (tq, tk)
+ *     score matrix is never stored.
+ *   - Grouped K/V heads: q head h reads kv head h / (hq / hkv); hkv divides hq.
+ *   - Output type is the operand type; sums run in f32 and are rounded once, to
+ *     nearest even, at the end (compute internals page, "Tensor cores": the product
+ *     type is the operands' type).
+ *
+ * Layout: row-major, token rows with heads contiguous inside a row: element
+ * (b, t, h, e) of a [batch, seq, heads, d] tensor with row stride rs (elements
+ * between consecutive tokens, rs >= heads * d) is at ((b * seq + t) * rs + h * d + e).
+ * A packed qkv buffer [n, (hq + 2 hkv) d] is described by three pointers into it
+ * with the same row stride.
+ *
+ * Ownership: every pointer is caller-owned device memory (HIP device allocations on
+ * the current device).  The library allocates nothing, keeps no per-call state and
+ * never synchronises: work is enqueued on `stream` (a hipStream_t; NULL is the null
+ * stream) and the call returns.  Inputs must stay valid until that work has run.
+ *
+ * Errors: every argument is checked on the host before anything is enqueued; a call
+ * that returns an error has enqueued nothing (it fails closed).  The message of the
+ * last failure on the calling thread is available from attn_last_error().
+ *   ATTN_ERR_ARG          null pointer, size <= 0, hq % hkv != 0, 2*half > d, a row
+ *                         stride smaller than its row, positions past the table, ...
+ *   ATTN_ERR_UNSUPPORTED  head dim d not in {64, 128}, or an unknown dtype.
+ *   ATTN_ERR_WORKSPACE    decode workspace smaller than attn_decode_workspace_size().
+ *   ATTN_ERR_HIP          the HIP runtime reported an error while enqueuing.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_dtype {
+    ATTN_F32 = 0,   /* IEEE binary32 operands */
+    ATTN_BF16 = 1   /* bfloat16 operands (f32 accumulation) */
+} attn_dtype_t;
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_ARG = -1,
+    ATTN_ERR_UNSUPPORTED = -2,
+    ATTN_ERR_WORKSPACE = -3,
+    ATTN_ERR_HIP = -4
+} attn_status_t;
+
+/*
+ * The HeadPrep record (gizml:netops, Types > HeadPrep: {qw, kw, cos, sin, eps}).
+ * All pointers are device f32 arrays.
+ *   qw, kw      [d] norm weights of q and of k.
+ *   cos, sin    [table_rows, half] rotation tables; row p is sequence position p.
+ *   half        number of turned pairs; 0 <= 2 * half <= d; 0 means no turn (cos and
+ *               sin are then not read and may be NULL).
+ *   table_rows  number of rows in cos and sin; every position used must be below it.
+ *   eps         added to the mean of squares under the root (taken as f32).
+ */
+typedef struct attn_headprep {
+    const float *qw;
+    const float *kw;
+    const float *cos;
+    const float *sin;
+    int64_t half;
+    int64_t table_rows;
+    double eps;
+} attn_headprep_t;
+
+/*
+ * attn_prep -- HeadPrep in place on q and k (gizml:netops, Functions >
+ * headPrepInPlace).
+ *   q  [batch, seq, hq, d], row stride q_row_stride; prepped with qw.  May be NULL.
+ *   k  [batch, seq, hkv, d], row stride k_row_stride; prepped with kw.  May be NULL.
+ *   Token t of every sequence uses table row pos0 + t; pos0 + seq <= table_rows.
+ *   dtype is the storage type of q and k; the arithmetic is f32 and the result is
+ *   rounded once to the storage type.  hq (hkv) is ignored when q (k) is NULL.
+ */
+attn_status_t attn_prep(void *q, void *k, int64_t batch, int64_t seq, int64_t hq, int64_t hkv,
+                        int64_t d, int64_t q_row_stride, int64_t k_row_stride, int64_t pos0,
+                        const attn_headprep_t *prep, attn_dtype_t dtype, void *stream);
+
+/*
+ * attn_prefill -- causal (or full) attention of a whole sequence, with HeadPrep.
+ *   q    [batch, seq, hq, d]   (read only; its HeadPrep is applied as it is read)
+ *   k    [batch, seq, hkv, d]  (with prep: prepped IN PLACE first, so on return it
+ *                               holds the prepped keys, ready to serve as a KV cache)
+ *   v    [batch, seq, hkv, d]
+ *   out  [batch, seq, hq, d]   must not overlap q, k or v.
+ *   Token t uses table row pos0 + t.  prep may be NULL: plain attention of q, k, v.
+ *   prep->kw may be NULL: k then already holds prepped keys (e.g. written by an
+ *   earlier attn_prep) and is not modified; q's HeadPrep is still applied.
+ *   causal != 0: query t sees keys 0..t (tq = tk, so bottom-right = top-left).
+ *   scale multiplies q.k (1/sqrt(d) in the usual model).
+ */
+attn_status_t attn_prefill(const void *q, void *k, const void *v, void *out,
+                           int64_t batch, int64_t seq, int64_t hq, int64_t hkv, int64_t d,
+                           int64_t q_row_stride, int64_t k_row_stride, int64_t v_row_stride,
+                           int64_t o_row_stride, int64_t pos0, const attn_headprep_t *prep,
+                           int causal, double scale, attn_dtype_t dtype, void *stream);
+
+/*
+ * attn_decode -- one new query row per sequence against a KV cache whose keys are
+ * already prepped (gizml:netops, Functions > attention with tq = 1 < tk: the row
+ * attends the whole cache).
+ *   q         [batch, hq, d] contiguous; its HeadPrep (qw, cos, sin) is applied at
+ *             table row pos[b] as it is read; kw is not used.  prep may be NULL.
+ *   k_cache   [batch, capacity, hkv, d] contiguous, prepped keys.
+ *   v_cache   [batch, capacity, hkv, d] contiguous.
+ *   out       [batch, hq, d] contiguous.
+ *   lens      device int32 [batch]: sequence b attends cache rows 0 .. lens[b]-1.
+ *   pos       device int32 [batch]: table row of sequence b's query (read only when
+ *             prep is given and half > 0; may be NULL otherwise).
+ *   max_len   host bound on every lens[b]; 1 <= max_len <= capacity.  It sets how
+ *             the keys are split.
+ *   splits    number of key splits per sequence, 0 = the library's choice
+ *             (attn_decode_default_splits).  Results do not depend on it beyond
+ *             rounding.
+ *   workspace device scratch of at least attn_decode_workspace_size(...) bytes with
+ *             the same batch, hq, hkv, d, max_len and splits.  Contents on entry are
+ *             ignored.  Calls that share a workspace must not overlap in time.
+ *   Device-side values the host cannot check: lens[b] == 0 gives a zero output row;
+ *   lens[b] < 0, lens[b] > max_len, or a pos[b] outside [0, table_rows) gives NaN in
+ *   that sequence's output rows (nothing outside the buffers is read).
+ */
+size_t attn_decode_workspace_size(int64_t batch, int64_t hq, int64_t hkv, int64_t d,
+                                  int64_t max_len, int64_t splits);
+int64_t attn_decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len);
+attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *out,
+                          int64_t batch, int64_t hq, int64_t hkv, int64_t d, int64_t capacity,
+                          const int32_t *lens, const int32_t *pos, int64_t max_len,
+                          const attn_headprep_t *prep, double scale, int64_t splits,
+                          void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
+                          void *stream);
+
+/* 1 if head dim d and dtype are built into this library, else 0 (asked before
+ * allocating, like gpukit's gkd_attention_ok). */
+int attn_supported(int64_t d, attn_dtype_t dtype);
+
+/* Static text for a status code. */
+const char *attn_status_str(attn_status_t status);
+
+/* Message of the last failed call on this thread ("" if none); valid until the
+ * thread's next call into the library. */
+const char *attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

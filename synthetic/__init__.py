@@ -59,10 +59,12 @@ WORKLOADS = {
 def bf16_round(x) -> np.ndarray:
     """Round to bfloat16, nearest even, through f32; returned as f32 holding bf16 values."""
     f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = f.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    u = (u + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)
-    return u.astype(np.uint32).view(np.float32).reshape(f.shape)
+    u = f.view(np.uint32)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u                       # finite inputs only: no carry out of bit 31
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32).reshape(f.shape)
 
 
 def to_storage(x, dtype: str) -> np.ndarray:

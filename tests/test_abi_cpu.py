@@ -1,0 +1,153 @@
+"""The C ABI on the CPU: the library loads, exports what include/attn.h declares, and
+rejects bad arguments on the host before enqueuing anything (no GPU is touched: every
+call below fails validation, so no pointer is ever dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_attention_headprep_amd as tah
+from transformer_attention_headprep_amd import attn as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000       # a 16-byte aligned address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tah.load_library()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert declared == sorted(tah.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert lib.attn_status_str(code)
+    assert lib.attn_supported(128, A.ATTN_BF16) == 1
+    assert lib.attn_supported(64, A.ATTN_F32) == 1
+    assert lib.attn_supported(96, A.ATTN_BF16) == 0
+    assert lib.attn_supported(128, 7) == 0
+
+
+def _prep(half=64, rows=4096, qw=FAKE, kw=FAKE, cos=FAKE, sin=FAKE, eps=1e-6):
+    return A.attn_headprep_t(qw, kw, cos, sin, half, rows, eps)
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), out=FAKE + (3 << 32), batch=2, seq=16,
+             hq=8, hkv=2, d=128, qrs=1024, krs=256, vrs=256, ors=1024, pos0=0, prep=_prep(),
+             causal=1, scale=0.088, dtype=A.ATTN_BF16)
+    a.update(kw)
+    prep = ctypes.byref(a["prep"]) if a["prep"] is not None else None
+    return lib.attn_prefill(a["q"], a["k"], a["v"], a["out"], a["batch"], a["seq"], a["hq"], a["hkv"],
+                            a["d"], a["qrs"], a["krs"], a["vrs"], a["ors"], a["pos0"], prep,
+                            a["causal"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), A.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=5), A.ATTN_ERR_UNSUPPORTED),
+    (dict(q=None), A.ATTN_ERR_ARG),
+    (dict(v=None), A.ATTN_ERR_ARG),
+    (dict(q=FAKE + 2), A.ATTN_ERR_ARG),                 # misaligned
+    (dict(hq=6, hkv=4, qrs=768), A.ATTN_ERR_ARG),       # hq not a multiple of hkv
+    (dict(hkv=0), A.ATTN_ERR_ARG),
+    (dict(qrs=1000), A.ATTN_ERR_ARG),                   # stride smaller than the row
+    (dict(krs=260), A.ATTN_ERR_ARG),                    # stride not a multiple of 8
+    (dict(batch=-1), A.ATTN_ERR_ARG),
+    (dict(prep=_prep(half=65)), A.ATTN_ERR_ARG),        # 2 * half > d
+    (dict(prep=_prep(half=-1)), A.ATTN_ERR_ARG),
+    (dict(prep=_prep(rows=15)), A.ATTN_ERR_ARG),        # positions past the table
+    (dict(pos0=1, prep=_prep(rows=16)), A.ATTN_ERR_ARG),
+    (dict(pos0=-1), A.ATTN_ERR_ARG),
+    (dict(prep=_prep(cos=None)), A.ATTN_ERR_ARG),
+    (dict(prep=_prep(qw=None)), A.ATTN_ERR_ARG),
+    (dict(prep=_prep(eps=-1.0)), A.ATTN_ERR_ARG),
+    (dict(prep=_prep(eps=float("nan"))), A.ATTN_ERR_ARG),
+    (dict(scale=float("inf")), A.ATTN_ERR_ARG),
+    (dict(out=FAKE + 512), A.ATTN_ERR_ARG),             # out overlaps q
+])
+def test_prefill_rejects(lib, kw, code):
+    assert _prefill(lib, **kw) == code
+    assert lib.attn_last_error()
+
+
+def test_prefill_empty_is_a_no_op(lib):
+    assert _prefill(lib, seq=0) == A.ATTN_OK
+    assert _prefill(lib, batch=0) == A.ATTN_OK
+
+
+def _prep_call(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 32), batch=1, seq=8, hq=4, hkv=2, d=64, qrs=256, krs=128,
+             pos0=0, prep=_prep(half=32), dtype=A.ATTN_F32)
+    a.update(kw)
+    prep = ctypes.byref(a["prep"]) if a["prep"] is not None else None
+    return lib.attn_prep(a["q"], a["k"], a["batch"], a["seq"], a["hq"], a["hkv"], a["d"], a["qrs"],
+                         a["krs"], a["pos0"], prep, a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None, k=None), A.ATTN_ERR_ARG),
+    (dict(prep=None), A.ATTN_ERR_ARG),
+    (dict(d=256, qrs=1024, krs=512), A.ATTN_ERR_UNSUPPORTED),
+    (dict(prep=_prep(half=32, kw=None)), A.ATTN_ERR_ARG),
+    (dict(pos0=4090, prep=_prep(half=32, rows=4096)), A.ATTN_ERR_ARG),
+    (dict(k=FAKE + 64), A.ATTN_ERR_ARG),                 # k lands on q's heads
+])
+def test_prep_rejects(lib, kw, code):
+    assert _prep_call(lib, **kw) == code
+
+
+def test_prep_empty_is_a_no_op(lib):
+    assert _prep_call(lib, seq=0) == A.ATTN_OK
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), out=FAKE + (3 << 32), batch=32, hq=32,
+             hkv=8, d=128, cap=4096, lens=FAKE + (4 << 32), pos=FAKE + (5 << 32), max_len=4096,
+             prep=_prep(rows=4097), scale=0.088, splits=0, ws=FAKE + (6 << 32), ws_bytes=1 << 30,
+             dtype=A.ATTN_BF16)
+    a.update(kw)
+    prep = ctypes.byref(a["prep"]) if a["prep"] is not None else None
+    return lib.attn_decode(a["q"], a["k"], a["v"], a["out"], a["batch"], a["hq"], a["hkv"], a["d"],
+                           a["cap"], a["lens"], a["pos"], a["max_len"], prep, a["scale"], a["splits"],
+                           a["ws"], a["ws_bytes"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws_bytes=1000), A.ATTN_ERR_WORKSPACE),
+    (dict(ws=None), A.ATTN_ERR_WORKSPACE),
+    (dict(lens=None), A.ATTN_ERR_ARG),
+    (dict(pos=None), A.ATTN_ERR_ARG),
+    (dict(max_len=4097), A.ATTN_ERR_ARG),
+    (dict(max_len=0), A.ATTN_ERR_ARG),
+    (dict(splits=5000), A.ATTN_ERR_ARG),
+    (dict(splits=-2), A.ATTN_ERR_ARG),
+    (dict(hq=30), A.ATTN_ERR_ARG),
+    (dict(d=80), A.ATTN_ERR_UNSUPPORTED),
+    (dict(cap=0, max_len=0), A.ATTN_ERR_ARG),
+    (dict(out=FAKE + 64), A.ATTN_ERR_ARG),               # out overlaps q
+])
+def test_decode_rejects(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_decode_sizes(lib):
+    s = lib.attn_decode_default_splits(32, 32, 8, 4096)
+    assert s >= 1
+    assert lib.attn_decode_workspace_size(32, 32, 8, 128, 4096, 0) == s * 32 * 32 * 130 * 4
+    assert lib.attn_decode_workspace_size(32, 32, 8, 128, 4096, 3) == 3 * 32 * 32 * 130 * 4
+    assert lib.attn_decode_workspace_size(0, 32, 8, 128, 4096, 0) == 0
+    assert _decode(lib, batch=0) == A.ATTN_OK

@@ -1,0 +1,309 @@
+"""GPU parity: libattn's HIP path against the f64 oracle on the same seeded inputs.
+
+Every call goes through the C ABI (via the ctypes binding).  Small cases compare every
+output element; the full-size workloads compare seeded samples of query rows (all
+heads, first and last rows, tile boundaries) plus properties that hold at any size.
+Tolerances: f32 max |d| <= 1e-4; bf16 |d| <= 2e-2 + 1e-2 |oracle| (tests/gpu_util.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+import transformer_attention_headprep_amd as tah
+from gpu_util import assert_close, dev, host, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _prep_dev(inp, half=None):
+    half = inp["half"] if half is None else half
+    cos = dev(inp["cos"][:, :half], "f32").contiguous() if half else None
+    sin = dev(inp["sin"][:, :half], "f32").contiguous() if half else None
+    return tah.HeadPrep(dev(inp["qw"], "f32"), dev(inp["kw"], "f32"), cos, sin, inp["eps"])
+
+
+def _tables(rows, half, d, base=1e4):
+    return synthetic.rope_tables(rows, half, d, base)
+
+
+def _sample_rows(batch, seq, hq, n_extra, seed):
+    rng = np.random.default_rng(seed)
+    rows = sorted({0, 1, 31, 32, 63, 64, 127, 128, 129, seq // 2, seq - 2, seq - 1} & set(range(seq)))
+    sel = []
+    for i, r in enumerate(rows):
+        for b in range(batch):
+            sel.append((b, r, (i + 3 * b) % hq))
+            sel.append((b, r, (i + 3 * b + hq // 2) % hq))
+    for _ in range(n_extra):
+        sel.append((int(rng.integers(batch)), int(rng.integers(seq)), int(rng.integers(hq))))
+    for h in range(hq):                       # every head at least once
+        sel.append((h % batch, int(rng.integers(seq)), h))
+    return np.array(sel, dtype=np.int64)
+
+
+# --------------------------------------------------------------------------- attn_prep
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d,half", [(64, 32), (128, 64), (128, 0), (128, 24), (64, 16), (128, 48)])
+def test_prep_parity(dtype, d, half):
+    require_gpu()
+    w = synthetic.Workload("p", "prefill", dtype, 2, 6, 2, 37, d, half, 1e4, 11)
+    inp = synthetic.make_prefill(w)
+    cos, sin = _tables(40, half, d)
+    inp["cos"], inp["sin"] = cos, sin
+    q, k = dev(inp["q"], dtype), dev(inp["k"], dtype)
+    tah.attn_prep(q, k, _prep_dev(inp), pos0=3)
+    pos = (3 + np.arange(37))[None, :].repeat(2, 0)
+    refq = oracle.headprep(inp["q"], inp["qw"], cos, sin, half, pos, w.eps)
+    refk = oracle.headprep(inp["k"], inp["kw"], cos, sin, half, pos, w.eps)
+    assert_close(host(q), refq, dtype, "prep q")
+    assert_close(host(k), refk, dtype, "prep k")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prep_packed_qkv_rows(dtype):
+    """q, k and v packed in one [n, (hq + 2 hkv) d] buffer; v must stay untouched."""
+    require_gpu()
+    d, hq, hkv, n = 128, 4, 2, 50
+    rng = np.random.default_rng(5)
+    qkv = synthetic.to_storage(rng.standard_normal((1, n, hq + 2 * hkv, d)), dtype)
+    qw = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    kw = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    cos, sin = _tables(n, 64, d)
+    t = dev(qkv, dtype)
+    prep = tah.HeadPrep(dev(qw, "f32"), dev(kw, "f32"), dev(cos, "f32"), dev(sin, "f32"), 1e-6)
+    tah.attn_prep(t[:, :, :hq], t[:, :, hq:hq + hkv], prep, pos0=0)
+    got = host(t)
+    pos = np.arange(n)[None]
+    assert_close(got[:, :, :hq], oracle.headprep(qkv[:, :, :hq], qw, cos, sin, 64, pos, 1e-6), dtype, "q")
+    assert_close(got[:, :, hq:hq + hkv], oracle.headprep(qkv[:, :, hq:hq + hkv], kw, cos, sin, 64, pos, 1e-6),
+                 dtype, "k")
+    np.testing.assert_array_equal(got[:, :, hq + hkv:], qkv[:, :, hq + hkv:])
+
+
+# ------------------------------------------------------------------------ attn_prefill
+
+@pytest.mark.parametrize("name", ["tiny_f32", "prefill_f32"])
+def test_prefill_f32_workloads_full(name):
+    require_gpu()
+    w = synthetic.WORKLOADS[name]
+    inp = synthetic.make_prefill(w)
+    q, k, v = dev(inp["q"], "f32"), dev(inp["k"], "f32"), dev(inp["v"], "f32")
+    out = tah.attn_prefill(q, k, v, prep=_prep_dev(inp), causal=True, scale=w.scale)
+    ref, kh = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["qw"], inp["kw"], inp["cos"], inp["sin"],
+                             w.half, w.eps, 0, w.scale, True)
+    assert_close(host(out), ref, "f32", name)
+    assert_close(host(k), kh, "f32", name + " k prepped in place")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("seq,hq,hkv", [(300, 8, 2), (1, 4, 4), (129, 6, 3), (64, 2, 1)])
+def test_prefill_small_full(dtype, d, causal, seq, hq, hkv):
+    """Several 128-row query tiles and 64-key tiles, with ragged tails, every element."""
+    require_gpu()
+    w = synthetic.Workload("s", "prefill", dtype, 2, hq, hkv, seq, d, d // 2, 1e4, 7, causal=causal)
+    inp = synthetic.make_prefill(w)
+    q, k, v = dev(inp["q"], dtype), dev(inp["k"], dtype), dev(inp["v"], dtype)
+    out = tah.attn_prefill(q, k, v, prep=_prep_dev(inp), causal=causal, scale=w.scale)
+    ref, kh = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["qw"], inp["kw"], inp["cos"], inp["sin"],
+                             w.half, w.eps, 0, w.scale, causal)
+    assert_close(host(out), ref, dtype, "out")
+    assert_close(host(k), kh, dtype, "k prepped in place")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("half", [0, 16, 24, 48])
+def test_prefill_other_halves(dtype, half):
+    """half = 0 (no turn), halves the q prologue turns in registers, and halves that go
+    through the separate prep pass into `out` first."""
+    require_gpu()
+    d = 128
+    w = synthetic.Workload("h", "prefill", dtype, 1, 4, 2, 200, d, half, 1e4, 9)
+    inp = synthetic.make_prefill(w)
+    q, k, v = dev(inp["q"], dtype), dev(inp["k"], dtype), dev(inp["v"], dtype)
+    out = tah.attn_prefill(q, k, v, prep=_prep_dev(inp, half), causal=True, scale=w.scale)
+    ref, _ = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["qw"], inp["kw"], inp["cos"][:, :half],
+                            inp["sin"][:, :half], half, w.eps, 0, w.scale, True)
+    assert_close(host(out), ref, dtype, "out")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_without_prep_and_pos0(dtype):
+    require_gpu()
+    w = synthetic.Workload("n", "prefill", dtype, 2, 4, 1, 150, 64, 32, 1e4, 13)
+    inp = synthetic.make_prefill(w)
+    q, k, v = dev(inp["q"], dtype), dev(inp["k"], dtype), dev(inp["v"], dtype)
+    out = tah.attn_prefill(q, k, v, prep=None, causal=True, scale=0.3)
+    assert_close(host(out), oracle.attention(inp["q"], inp["k"], inp["v"], 0.3, True), dtype, "no prep")
+    # a chunk that starts at position 20 of the tables
+    cos, sin = _tables(170, 32, 64)
+    inp["cos"], inp["sin"] = cos, sin
+    k2 = dev(inp["k"], dtype)
+    out2 = tah.attn_prefill(q, k2, v, prep=_prep_dev(inp), pos0=20, causal=True, scale=w.scale)
+    ref, _ = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["qw"], inp["kw"], cos, sin, 32, w.eps, 20,
+                            w.scale, True)
+    assert_close(host(out2), ref, dtype, "pos0 = 20")
+
+
+def test_prefill_packed_qkv_layout():
+    require_gpu()
+    d, hq, hkv, n = 128, 8, 2, 260
+    rng = np.random.default_rng(17)
+    qkv = synthetic.bf16_round(rng.standard_normal((1, n, hq + 2 * hkv, d)))
+    qw = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    kw = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    cos, sin = _tables(n, 64, d)
+    t = dev(qkv, "bf16")
+    prep = tah.HeadPrep(dev(qw, "f32"), dev(kw, "f32"), dev(cos, "f32"), dev(sin, "f32"), 1e-6)
+    out = tah.attn_prefill(t[:, :, :hq], t[:, :, hq:hq + hkv], t[:, :, hq + hkv:], prep=prep, causal=True)
+    ref, _ = oracle.prefill(qkv[:, :, :hq], qkv[:, :, hq:hq + hkv], qkv[:, :, hq + hkv:], qw, kw, cos, sin,
+                            64, 1e-6, 0, 1 / np.sqrt(d), True)
+    assert_close(host(out), ref, "bf16", "packed")
+
+
+def _check_sampled_prefill(name, n_extra):
+    w = synthetic.WORKLOADS[name]
+    inp = synthetic.make_prefill(w)
+    print("workload %s: q %s" % (name, inp["q"].shape), flush=True)
+    q, k, v = dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16")
+    out = tah.attn_prefill(q, k, v, prep=_prep_dev(inp), causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    sel = _sample_rows(w.batch, w.seq, w.hq, n_extra, seed=w.seed)
+    ref, kh = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["qw"], inp["kw"], inp["cos"], inp["sin"],
+                             w.half, w.eps, 0, w.scale, True, sel=sel)
+    got = host(out)
+    assert np.isfinite(got).all()
+    err = assert_close(got[sel[:, 0], sel[:, 1], sel[:, 2]], ref, "bf16", name)
+    assert_close(host(k), kh, "bf16", name + " k prepped in place")
+    return err, inp, got
+
+
+def test_prefill_bf16_workload_sampled():
+    require_gpu()
+    _check_sampled_prefill("prefill_bf16", 400)
+
+
+def test_long_prefill_workload_sampled():
+    """Long prefill with the literal inputs (1 % of raw k rows scaled x8, which HeadPrep's
+    RMS division makes inert), sampled rows; plus the invariant that the output equals
+    the run without the scaled rows."""
+    require_gpu()
+    _, inp, got = _check_sampled_prefill("long_prefill_bf16", 200)
+    w = synthetic.WORKLOADS["long_prefill_bf16"]
+    k_plain = inp["k"].copy()
+    k_plain[:, inp["outliers"]] = synthetic.bf16_round(k_plain[:, inp["outliers"]] / 8.0)
+    q, k, v = dev(inp["q"], "bf16"), dev(k_plain, "bf16"), dev(inp["v"], "bf16")
+    out2 = host(tah.attn_prefill(q, k, v, prep=_prep_dev(inp), causal=True, scale=w.scale))
+    assert np.abs(out2 - got).max() <= 2e-2
+
+
+def test_prefill_softmax_max_stress():
+    """Prepped keys of 1 % of the rows scaled by 8 after HeadPrep (so they really dominate
+    the softmax maximum), then attention without prep on those exact bf16 values."""
+    require_gpu()
+    w = synthetic.Workload("x", "prefill", "bf16", 1, 8, 1, 2048, 128, 64, 1e6, 21)
+    inp = synthetic.make_prefill(w)
+    pos = np.arange(w.seq)[None]
+    qh = synthetic.bf16_round(oracle.headprep(inp["q"], inp["qw"], inp["cos"], inp["sin"], 64, pos, w.eps))
+    kh = oracle.headprep(inp["k"], inp["kw"], inp["cos"], inp["sin"], 64, pos, w.eps)
+    rows = np.random.default_rng(3).choice(w.seq, 20, replace=False)
+    kh[:, rows] *= 8.0
+    kh = synthetic.bf16_round(kh)
+    out = tah.attn_prefill(dev(qh, "bf16"), dev(kh, "bf16"), dev(inp["v"], "bf16"), prep=None, causal=True,
+                           scale=w.scale)
+    assert_close(host(out), oracle.attention(qh, kh, inp["v"], w.scale, True), "bf16", "stress")
+
+
+# ------------------------------------------------------------------------- attn_decode
+
+def _decode_inputs(w, batch=None, cache=None, seed=None):
+    inp = synthetic.make_decode(w, batch=batch, cache=cache, seed=seed)
+    cap = inp["k_raw"].shape[1]
+    pos = np.arange(cap)[None].repeat(inp["k_raw"].shape[0], 0)
+    kc = oracle.headprep(inp["k_raw"], inp["kw"], inp["cos"], inp["sin"], w.half, pos, w.eps)
+    inp["k_cache"] = synthetic.to_storage(kc, w.dtype)
+    return inp
+
+
+def _run_decode(w, inp, lens, pos, splits=0, max_len=None):
+    dt = w.dtype
+    q, kc, vc = dev(inp["q"], dt), dev(inp["k_cache"], dt), dev(inp["v"], dt)
+    ml = int(max(lens)) if max_len is None else max_len
+    ml = max(ml, 1)
+    out = tah.attn_decode(q, kc, vc, torch.tensor(lens, dtype=torch.int32, device="cuda:0"),
+                          torch.tensor(pos, dtype=torch.int32, device="cuda:0"), ml,
+                          prep=_prep_dev(inp), scale=w.scale, splits=splits)
+    return host(out)
+
+
+def _oracle_decode(w, inp, lens, pos):
+    return oracle.decode(inp["q"], inp["k_cache"], inp["v"], lens, pos, inp["qw"], inp["cos"], inp["sin"],
+                         w.half, w.eps, w.scale)
+
+
+def test_decode_workload_full():
+    require_gpu()
+    w = synthetic.WORKLOADS["decode_bf16"]
+    inp = _decode_inputs(w)
+    got = _run_decode(w, inp, inp["lens"], inp["pos"])
+    ref = _oracle_decode(w, inp, inp["lens"], inp["pos"])
+    assert_close(got, ref, "bf16", "decode")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16, 64])
+def test_decode_split_counts(splits):
+    require_gpu()
+    w = synthetic.WORKLOADS["decode_bf16"]
+    inp = _decode_inputs(w, batch=4, cache=1500, seed=31)
+    lens = np.array([1500, 1, 700, 1337], dtype=np.int32)
+    pos = np.array([1500, 3, 900, 1400], dtype=np.int32)
+    got = _run_decode(w, inp, lens, pos, splits=splits)
+    assert_close(got, _oracle_decode(w, inp, lens, pos), "bf16", "splits=%d" % splits)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 8), (64, 4), (12, 2)])
+def test_decode_shapes(dtype, d, hq, hkv):
+    require_gpu()
+    w = synthetic.Workload("d", "decode", dtype, 3, hq, hkv, 333, d, d // 2, 1e4, 41)
+    inp = _decode_inputs(w)
+    lens = np.array([333, 65, 200], dtype=np.int32)
+    pos = np.array([333, 100, 7], dtype=np.int32)
+    got = _run_decode(w, inp, lens, pos)
+    assert_close(got, _oracle_decode(w, inp, lens, pos), dtype, "decode")
+
+
+def test_decode_empty_and_invalid_rows():
+    """lens 0 gives zeros; lens past max_len or a position past the table gives NaN in
+    that sequence only (the kernels clamp every read)."""
+    require_gpu()
+    w = synthetic.WORKLOADS["decode_bf16"]
+    inp = _decode_inputs(w, batch=4, cache=300, seed=43)
+    lens = np.array([0, 300, 301, 50], dtype=np.int32)
+    pos = np.array([5, 300, 10, 301], dtype=np.int32)     # table has 301 rows
+    got = _run_decode(w, inp, lens, pos, max_len=300)
+    np.testing.assert_array_equal(got[0], 0.0)
+    assert np.isnan(got[2]).all() and np.isnan(got[3]).all()
+    ok = _oracle_decode(w, {**inp, "q": inp["q"][1:2], "k_cache": inp["k_cache"][1:2], "v": inp["v"][1:2]},
+                        lens[1:2], pos[1:2])
+    assert_close(got[1:2], ok, "bf16", "valid row beside invalid ones")
+
+
+def test_decode_matches_prefill_row():
+    """KV-cache equivalence on the GPU: attn_prefill preps k in place; decoding the query
+    of position p against that cache (lens = p + 1) gives prefill's output row p."""
+    require_gpu()
+    w = synthetic.Workload("e", "prefill", "bf16", 2, 16, 4, 600, 128, 64, 1e4, 51)
+    inp = synthetic.make_prefill(w)
+    q, k, v = dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16")
+    prep = _prep_dev(inp)
+    out = tah.attn_prefill(q, k, v, prep=prep, causal=True, scale=w.scale)
+    for p in (0, 127, 599):
+        dec = tah.attn_decode(q[:, p].contiguous(), k, v, torch.full((2,), p + 1, dtype=torch.int32, device="cuda:0"),
+                              torch.full((2,), p, dtype=torch.int32, device="cuda:0"), 600, prep=prep, scale=w.scale)
+        assert_close(host(dec), host(out[:, p]), "bf16", "position %d" % p)

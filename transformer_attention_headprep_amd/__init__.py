@@ -1,0 +1,19 @@
+"""HeadPrep + scaled-dot-product attention for AMD MI355X (gfx950).
+
+The compute lives in ``libattn.so`` (hand-written HIP kernels behind a C ABI, declared
+in ``include/attn.h``); this package is its thin Python binding.  Build the library
+with ``python -m transformer_attention_headprep_amd.build``.
+"""
+from .attn import (  # noqa: F401
+    AttnError,
+    HeadPrep,
+    LIB_PATH,
+    EXPORTS,
+    attn_decode,
+    attn_prefill,
+    attn_prep,
+    attn_supported,
+    decode_default_splits,
+    decode_workspace_size,
+    load_library,
+)

@@ -1,0 +1,214 @@
+"""Thin Python binding of libattn's C ABI (include/attn.h).
+
+Only argument marshalling lives here: torch tensors supply device pointers, strides and
+the current HIP stream; every step of the computation runs in libattn's HIP kernels.
+There is no fallback: if libattn.so is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_OK, ATTN_ERR_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 0, -1, -2, -3, -4
+
+# The entry points include/attn.h declares (checked by the CPU test suite).
+EXPORTS = ("attn_prep", "attn_prefill", "attn_decode", "attn_decode_workspace_size",
+           "attn_decode_default_splits", "attn_supported", "attn_status_str", "attn_last_error")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (status %d)" % (message, status))
+        self.status = status
+
+
+class attn_headprep_t(ctypes.Structure):
+    _fields_ = [("qw", ctypes.c_void_p), ("kw", ctypes.c_void_p), ("cos", ctypes.c_void_p),
+                ("sin", ctypes.c_void_p), ("half", ctypes.c_int64), ("table_rows", ctypes.c_int64),
+                ("eps", ctypes.c_double)]
+
+
+_lib = None
+_i64, _vp, _dbl = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError("libattn.so is not built (expected at %s); run "
+                          "`python -m transformer_attention_headprep_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    hp = ctypes.POINTER(attn_headprep_t)
+    lib.attn_prep.argtypes = [_vp, _vp] + [_i64] * 8 + [hp, ctypes.c_int, _vp]
+    lib.attn_prep.restype = ctypes.c_int
+    lib.attn_prefill.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 10 + [hp, ctypes.c_int, _dbl,
+                                                                         ctypes.c_int, _vp]
+    lib.attn_prefill.restype = ctypes.c_int
+    lib.attn_decode.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 5 + [_vp, _vp, _i64, hp, _dbl, _i64,
+                                                                    _vp, ctypes.c_size_t,
+                                                                    ctypes.c_int, _vp]
+    lib.attn_decode.restype = ctypes.c_int
+    lib.attn_decode_workspace_size.argtypes = [_i64] * 6
+    lib.attn_decode_workspace_size.restype = ctypes.c_size_t
+    lib.attn_decode_default_splits.argtypes = [_i64] * 4
+    lib.attn_decode_default_splits.restype = _i64
+    lib.attn_supported.argtypes = [_i64, ctypes.c_int]
+    lib.attn_supported.restype = ctypes.c_int
+    lib.attn_status_str.argtypes = [ctypes.c_int]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        lib = load_library()
+        raise AttnError(status, (lib.attn_last_error() or b"").decode() or
+                        lib.attn_status_str(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _row_stride(t: torch.Tensor, name: str) -> int:
+    """[B, S, H, D] view whose rows are `stride(1)` elements apart (heads contiguous)."""
+    if t.dim() != 4:
+        raise ValueError("%s must be [batch, seq, heads, d]" % name)
+    B, S, H, D = t.shape
+    if t.stride(3) != 1 or (H > 1 and t.stride(2) != D):
+        raise ValueError("%s: heads and values must be contiguous inside a row" % name)
+    if B > 1 and t.stride(0) != S * t.stride(1):
+        raise ValueError("%s: sequences must follow each other (batch stride = seq * row stride)" % name)
+    return t.stride(1) if S > 1 else (t.stride(0) if B > 1 else H * D)
+
+
+@dataclass
+class HeadPrep:
+    """The HeadPrep record {qw, kw, cos, sin, eps} as device f32 tensors."""
+    qw: torch.Tensor
+    kw: torch.Tensor
+    cos: torch.Tensor | None
+    sin: torch.Tensor | None
+    eps: float
+
+    @property
+    def half(self) -> int:
+        return 0 if self.cos is None else int(self.cos.shape[1])
+
+    def struct(self) -> attn_headprep_t:
+        for name in ("qw", "kw", "cos", "sin"):
+            t = getattr(self, name)
+            if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+                raise ValueError("HeadPrep.%s must be a contiguous float32 tensor" % name)
+        half = self.half
+        return attn_headprep_t(
+            self.qw.data_ptr() if self.qw is not None else None,
+            self.kw.data_ptr() if self.kw is not None else None,
+            self.cos.data_ptr() if half else None, self.sin.data_ptr() if half else None,
+            half, int(self.cos.shape[0]) if half else 0, float(self.eps))
+
+
+def attn_supported(d: int, dtype: torch.dtype) -> bool:
+    return bool(load_library().attn_supported(d, ATTN_BF16 if dtype == torch.bfloat16 else ATTN_F32))
+
+
+def attn_prep(q, k, prep: HeadPrep, pos0: int = 0, stream=None) -> None:
+    """HeadPrep in place on q [B, S, Hq, D] and/or k [B, S, Hkv, D]."""
+    lib = load_library()
+    ref = q if q is not None else k
+    B, S = ref.shape[0], ref.shape[1]
+    D = ref.shape[3]
+    hq = q.shape[2] if q is not None else 0
+    hkv = k.shape[2] if k is not None else 0
+    qrs = _row_stride(q, "q") if q is not None else 0
+    krs = _row_stride(k, "k") if k is not None else 0
+    if q is not None and k is not None and q.dtype != k.dtype:
+        raise TypeError("q and k must share a dtype")
+    st = prep.struct()
+    _check(lib.attn_prep(_ptr(q), _ptr(k), B, S, hq, hkv, D, qrs, krs, pos0, ctypes.byref(st),
+                         _dtype_code(ref), _stream(stream)))
+
+
+def attn_prefill(q, k, v, out=None, prep: HeadPrep | None = None, pos0: int = 0,
+                 causal: bool = True, scale: float | None = None, stream=None) -> torch.Tensor:
+    """out = softmax(prep(q) prep(k)^T scale [+ causal]) v; with prep, k is prepped in place."""
+    lib = load_library()
+    B, S, hq, D = q.shape
+    hkv = k.shape[2]
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    if not (q.dtype == k.dtype == v.dtype == out.dtype):
+        raise TypeError("q, k, v and out must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = prep.struct() if prep is not None else None
+    _check(lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, hq, hkv, D,
+                            _row_stride(q, "q"), _row_stride(k, "k"), _row_stride(v, "v"),
+                            _row_stride(out, "out"), pos0,
+                            ctypes.byref(st) if st is not None else None, int(bool(causal)),
+                            float(scale), _dtype_code(q), _stream(stream)))
+    return out
+
+
+def decode_workspace_size(batch: int, hq: int, hkv: int, d: int, max_len: int, splits: int = 0) -> int:
+    return int(load_library().attn_decode_workspace_size(batch, hq, hkv, d, max_len, splits))
+
+
+def decode_default_splits(batch: int, hq: int, hkv: int, max_len: int) -> int:
+    return int(load_library().attn_decode_default_splits(batch, hq, hkv, max_len))
+
+
+def attn_decode(q, k_cache, v_cache, lens, pos, max_len: int, prep: HeadPrep | None = None,
+                scale: float | None = None, splits: int = 0, workspace=None, out=None,
+                stream=None) -> torch.Tensor:
+    """One query row per sequence (q [B, Hq, D]) against caches [B, capacity, Hkv, D]."""
+    lib = load_library()
+    B, hq, D = q.shape
+    cap, hkv = k_cache.shape[1], k_cache.shape[2]
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if lens.dtype != torch.int32 or (pos is not None and pos.dtype != torch.int32):
+        raise TypeError("lens and pos must be int32 device tensors")
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = decode_workspace_size(B, hq, hkv, D, max_len, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = prep.struct() if prep is not None else None
+    _check(lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), B, hq, hkv, D, cap,
+                           _ptr(lens), _ptr(pos), max_len,
+                           ctypes.byref(st) if st is not None else None, float(scale), splits,
+                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _dtype_code(q), _stream(stream)))
+    return out

@@ -1,0 +1,270 @@
+// attn_api.cpp -- the C ABI of libattn: argument checks, then launches.
+//
+// Every entry point checks all of its arguments on the host before it enqueues
+// anything, and returns an error code without touching the device when a check
+// fails (the "validate and fail closed" convention of the gpukit page's devops
+// wrappers).  Nothing here allocates or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/attn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+attn_status_t fail(attn_status_t code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+attn_status_t hip_status(hipError_t err, const char *where) {
+    if (err == hipSuccess) return ATTN_OK;
+    return fail(ATTN_ERR_HIP, "%s: HIP error %d (%s)", where, (int)err, hipGetErrorString(err));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(attn_dtype_t dt) { return dt == ATTN_BF16 ? 2 : 4; }
+
+attn_status_t check_dtype_d(attn_dtype_t dt, int64_t d) {
+    if (dt != ATTN_F32 && dt != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim %lld not in {64, 128}", (long long)d);
+    return ATTN_OK;
+}
+
+// A [batch, seq, heads, d] operand with row stride rs.
+attn_status_t check_rows(const char *name, const void *p, int64_t heads, int64_t d, int64_t rs) {
+    if (!p) return fail(ATTN_ERR_ARG, "%s is NULL", name);
+    if (!aligned16(p)) return fail(ATTN_ERR_ARG, "%s is not 16-byte aligned", name);
+    if (heads <= 0) return fail(ATTN_ERR_ARG, "%s: head count %lld <= 0", name, (long long)heads);
+    if (rs < heads * d) return fail(ATTN_ERR_ARG, "%s: row stride %lld < heads * d = %lld", name, (long long)rs, (long long)(heads * d));
+    if (rs % 8 != 0) return fail(ATTN_ERR_ARG, "%s: row stride %lld not a multiple of 8 elements", name, (long long)rs);
+    return ATTN_OK;
+}
+
+struct Span { uintptr_t lo, hi; };
+
+Span span(const void *p, int64_t rows, int64_t rs, int64_t heads, int64_t d, size_t es) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    const uintptr_t hi = lo + (uintptr_t)(((rows - 1) * rs + heads * d) * (int64_t)es);
+    return {lo, hi};
+}
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// The HeadPrep record: tables cover positions [first, first + count).
+attn_status_t check_prep(const attn_headprep_t *p, int64_t d, bool need_qw, bool need_kw, int64_t first,
+                         int64_t count) {
+    if (need_qw && !p->qw) return fail(ATTN_ERR_ARG, "prep->qw is NULL");
+    if (need_kw && !p->kw) return fail(ATTN_ERR_ARG, "prep->kw is NULL");
+    if ((need_qw && !aligned16(p->qw)) || (need_kw && !aligned16(p->kw)))
+        return fail(ATTN_ERR_ARG, "prep weights are not 16-byte aligned");
+    if (!(p->eps >= 0.0) || !std::isfinite(p->eps)) return fail(ATTN_ERR_ARG, "prep->eps must be finite and >= 0");
+    if (p->half < 0 || 2 * p->half > d)
+        return fail(ATTN_ERR_ARG, "prep->half = %lld outside [0, d/2]", (long long)p->half);
+    if (p->half > 0) {
+        if (!p->cos || !p->sin) return fail(ATTN_ERR_ARG, "prep->cos/sin is NULL with half > 0");
+        if (!aligned16(p->cos) || !aligned16(p->sin)) return fail(ATTN_ERR_ARG, "prep tables are not 16-byte aligned");
+        if (p->table_rows <= 0) return fail(ATTN_ERR_ARG, "prep->table_rows <= 0");
+        if (count > 0 && (first < 0 || first + count > p->table_rows))
+            return fail(ATTN_ERR_ARG, "positions [%lld, %lld) outside the %lld-row table", (long long)first,
+                        (long long)(first + count), (long long)p->table_rows);
+    }
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_last_error(void) { return g_last_error; }
+
+const char *attn_status_str(attn_status_t s) {
+    switch (s) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_ARG: return "invalid argument";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported head dim or dtype";
+        case ATTN_ERR_WORKSPACE: return "workspace too small";
+        case ATTN_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int attn_supported(int64_t d, attn_dtype_t dt) {
+    return (d == 64 || d == 128) && (dt == ATTN_F32 || dt == ATTN_BF16);
+}
+
+attn_status_t attn_prep(void *q, void *k, int64_t batch, int64_t seq, int64_t hq, int64_t hkv, int64_t d,
+                        int64_t q_row_stride, int64_t k_row_stride, int64_t pos0, const attn_headprep_t *prep,
+                        attn_dtype_t dtype, void *stream) {
+    g_last_error[0] = 0;
+    attn_status_t st = check_dtype_d(dtype, d);
+    if (st) return st;
+    if (!prep) return fail(ATTN_ERR_ARG, "prep is NULL");
+    if (!q && !k) return fail(ATTN_ERR_ARG, "q and k are both NULL");
+    if (batch < 0 || seq < 0) return fail(ATTN_ERR_ARG, "negative batch or seq");
+    if (q && (st = check_rows("q", q, hq, d, q_row_stride))) return st;
+    if (k && (st = check_rows("k", k, hkv, d, k_row_stride))) return st;
+    if ((st = check_prep(prep, d, q != nullptr, k != nullptr, pos0, seq))) return st;
+    if (pos0 < 0) return fail(ATTN_ERR_ARG, "pos0 < 0");
+    if (batch == 0 || seq == 0) return ATTN_OK;
+    const size_t es = elem_size(dtype);
+    if (q && k && overlap(span(q, batch * seq, q_row_stride, hq, d, es), span(k, batch * seq, k_row_stride, hkv, d, es))) {
+        // Packed qkv rows interleave q and k; they only clash if a q head lands on a k head.
+        const intptr_t delta = reinterpret_cast<intptr_t>(k) - reinterpret_cast<intptr_t>(q);
+        if (q_row_stride != k_row_stride || delta % (intptr_t)es != 0)
+            return fail(ATTN_ERR_ARG, "q and k overlap");
+        const int64_t off = delta / (intptr_t)es;
+        if (!(off >= hq * d && off + hkv * d <= q_row_stride) && !(-off >= hkv * d && -off + hq * d <= q_row_stride))
+            return fail(ATTN_ERR_ARG, "q and k overlap");
+    }
+    attn::PrepLaunch a{};
+    a.q_src = q; a.q_dst = q; a.q_src_rs = q_row_stride; a.q_dst_rs = q_row_stride; a.hq = hq;
+    a.k_src = k; a.k_dst = k; a.k_src_rs = k_row_stride; a.k_dst_rs = k_row_stride; a.hkv = hkv;
+    a.batch = batch; a.seq = seq; a.d = d; a.pos0 = pos0;
+    a.qw = prep->qw; a.kw = prep->kw; a.cos = prep->cos; a.sin = prep->sin;
+    a.half = prep->half; a.eps = (float)prep->eps; a.bf16 = dtype == ATTN_BF16;
+    return hip_status(attn::launch_prep(a, static_cast<hipStream_t>(stream)), "attn_prep");
+}
+
+attn_status_t attn_prefill(const void *q, void *k, const void *v, void *out, int64_t batch, int64_t seq, int64_t hq,
+                           int64_t hkv, int64_t d, int64_t q_row_stride, int64_t k_row_stride,
+                           int64_t v_row_stride, int64_t o_row_stride, int64_t pos0, const attn_headprep_t *prep,
+                           int causal, double scale, attn_dtype_t dtype, void *stream) {
+    g_last_error[0] = 0;
+    attn_status_t st = check_dtype_d(dtype, d);
+    if (st) return st;
+    if (batch < 0 || seq < 0) return fail(ATTN_ERR_ARG, "negative batch or seq");
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
+        return fail(ATTN_ERR_ARG, "hq = %lld must be a positive multiple of hkv = %lld", (long long)hq, (long long)hkv);
+    if ((st = check_rows("q", q, hq, d, q_row_stride))) return st;
+    if ((st = check_rows("k", k, hkv, d, k_row_stride))) return st;
+    if ((st = check_rows("v", v, hkv, d, v_row_stride))) return st;
+    if ((st = check_rows("out", out, hq, d, o_row_stride))) return st;
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_ARG, "scale is not finite");
+    if (prep) {
+        if ((st = check_prep(prep, d, true, false, pos0, seq))) return st;
+        if (pos0 < 0) return fail(ATTN_ERR_ARG, "pos0 < 0");
+    }
+    if (batch == 0 || seq == 0) return ATTN_OK;
+    if ((int64_t)((seq + 127) / 128) * batch * hq >= (int64_t)1 << 31 || seq >= (int64_t)1 << 31)
+        return fail(ATTN_ERR_ARG, "problem too large for one launch");
+    const size_t es = elem_size(dtype);
+    const int64_t rows = batch * seq;
+    const Span so = span(out, rows, o_row_stride, hq, d, es);
+    if (overlap(so, span(q, rows, q_row_stride, hq, d, es)) || overlap(so, span(k, rows, k_row_stride, hkv, d, es)) ||
+        overlap(so, span(v, rows, v_row_stride, hkv, d, es)))
+        return fail(ATTN_ERR_ARG, "out overlaps q, k or v");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf16 = dtype == ATTN_BF16;
+
+    attn::PrefillLaunch a{};
+    a.q = q; a.k = k; a.v = v; a.out = out;
+    a.q_rs = q_row_stride; a.k_rs = k_row_stride; a.v_rs = v_row_stride; a.o_rs = o_row_stride;
+    a.batch = batch; a.seq = seq; a.hq = hq; a.hkv = hkv; a.d = d; a.pos0 = pos0;
+    a.causal = causal != 0; a.scale = (float)scale; a.bf16 = bf16;
+    if (prep) {
+        const bool fused = attn::prefill_fuses_half(d, prep->half, bf16);
+        // k is prepped in place; q either in the attention prologue or, for halves the
+        // prologue cannot turn, into `out` first (each attention block then reads its
+        // q rows from out before it overwrites exactly those rows).
+        // prep->kw == NULL: k already holds prepped keys and is left as it is.
+        attn::PrepLaunch pa{};
+        if (prep->kw) {
+            pa.k_src = k; pa.k_dst = k; pa.k_src_rs = k_row_stride; pa.k_dst_rs = k_row_stride; pa.hkv = hkv;
+        }
+        if (!fused) {
+            pa.q_src = q; pa.q_dst = out; pa.q_src_rs = q_row_stride; pa.q_dst_rs = o_row_stride; pa.hq = hq;
+        }
+        pa.batch = batch; pa.seq = seq; pa.d = d; pa.pos0 = pos0;
+        pa.qw = prep->qw; pa.kw = prep->kw; pa.cos = prep->cos; pa.sin = prep->sin;
+        pa.half = prep->half; pa.eps = (float)prep->eps; pa.bf16 = bf16;
+        if (pa.k_src || pa.q_src)
+            if ((st = hip_status(attn::launch_prep(pa, s), "attn_prefill (prep)"))) return st;
+        if (fused) {
+            a.prep_q = true;
+            a.qw = prep->qw; a.cos = prep->cos; a.sin = prep->sin; a.half = prep->half; a.eps = (float)prep->eps;
+        } else {
+            a.q = out; a.q_rs = o_row_stride;
+        }
+    }
+    return hip_status(attn::launch_prefill(a, s), "attn_prefill");
+}
+
+int64_t attn_decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len) {
+    if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || max_len <= 0) return 0;
+    return attn::decode_default_splits(batch, hq, hkv, max_len);
+}
+
+size_t attn_decode_workspace_size(int64_t batch, int64_t hq, int64_t hkv, int64_t d, int64_t max_len,
+                                  int64_t splits) {
+    if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || d <= 0 || max_len <= 0 || splits < 0) return 0;
+    if (splits == 0) splits = attn::decode_default_splits(batch, hq, hkv, max_len);
+    return attn::decode_workspace_bytes(batch, hq, d, splits);
+}
+
+attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *out, int64_t batch,
+                          int64_t hq, int64_t hkv, int64_t d, int64_t capacity, const int32_t *lens,
+                          const int32_t *pos, int64_t max_len, const attn_headprep_t *prep, double scale,
+                          int64_t splits, void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
+                          void *stream) {
+    g_last_error[0] = 0;
+    attn_status_t st = check_dtype_d(dtype, d);
+    if (st) return st;
+    if (batch < 0) return fail(ATTN_ERR_ARG, "negative batch");
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
+        return fail(ATTN_ERR_ARG, "hq = %lld must be a positive multiple of hkv = %lld", (long long)hq, (long long)hkv);
+    if ((st = check_rows("q", q, hq, d, hq * d))) return st;
+    if ((st = check_rows("k_cache", k_cache, hkv, d, hkv * d))) return st;
+    if ((st = check_rows("v_cache", v_cache, hkv, d, hkv * d))) return st;
+    if ((st = check_rows("out", out, hq, d, hq * d))) return st;
+    if (!lens) return fail(ATTN_ERR_ARG, "lens is NULL");
+    if (capacity <= 0 || capacity >= ((int64_t)1 << 31)) return fail(ATTN_ERR_ARG, "capacity %lld outside [1, 2^31)", (long long)capacity);
+    if (max_len < 1 || max_len > capacity) return fail(ATTN_ERR_ARG, "max_len %lld outside [1, capacity]", (long long)max_len);
+    if (splits < 0 || splits > max_len) return fail(ATTN_ERR_ARG, "splits %lld outside [0, max_len]", (long long)splits);
+    if (!std::isfinite(scale)) return fail(ATTN_ERR_ARG, "scale is not finite");
+    if (prep) {
+        if ((st = check_prep(prep, d, true, false, 0, 0))) return st;
+        if (prep->half > 0 && !pos) return fail(ATTN_ERR_ARG, "pos is NULL with a turning HeadPrep");
+        if (prep->table_rows >= ((int64_t)1 << 31)) return fail(ATTN_ERR_ARG, "table too large");
+    }
+    if (batch == 0) return ATTN_OK;
+    if (splits == 0) splits = attn::decode_default_splits(batch, hq, hkv, max_len);
+    if (splits * batch >= ((int64_t)1 << 31) || batch >= 65536 || hkv * hq >= 65536)
+        return fail(ATTN_ERR_ARG, "problem too large for one launch");
+    const size_t need = attn::decode_workspace_bytes(batch, hq, d, splits);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(ATTN_ERR_ARG, "workspace is not 16-byte aligned");
+    const size_t es = elem_size(dtype);
+    const Span so = span(out, batch, hq * d, hq, d, es);
+    const Span sw{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+    if (overlap(so, span(q, batch, hq * d, hq, d, es)) || overlap(so, sw) ||
+        overlap(so, span(k_cache, batch * capacity, hkv * d, hkv, d, es)) ||
+        overlap(so, span(v_cache, batch * capacity, hkv * d, hkv, d, es)))
+        return fail(ATTN_ERR_ARG, "out overlaps an input or the workspace");
+
+    attn::DecodeLaunch a{};
+    a.q = q; a.k = k_cache; a.v = v_cache; a.out = out;
+    a.batch = batch; a.hq = hq; a.hkv = hkv; a.d = d; a.capacity = capacity; a.max_len = max_len;
+    a.lens = lens; a.pos = pos;
+    a.prep_q = prep != nullptr;
+    if (prep) {
+        a.qw = prep->qw; a.cos = prep->cos; a.sin = prep->sin; a.half = prep->half;
+        a.table_rows = prep->table_rows; a.eps = (float)prep->eps;
+    }
+    a.scale = (float)scale; a.splits = splits; a.work = static_cast<float *>(workspace);
+    a.bf16 = dtype == ATTN_BF16;
+    return hip_status(attn::launch_decode(a, static_cast<hipStream_t>(stream)), "attn_decode");
+}
+
+}  // extern "C"

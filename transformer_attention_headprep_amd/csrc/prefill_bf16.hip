@@ -1,0 +1,333 @@
+// prefill_bf16.hip -- bf16 attention of whole sequences on the gfx950 matrix cores.
+//
+// softmax(q k^T scale [+ causal mask]) v (gizml:netops reference page, Functions >
+// attention) with the (tq, tk) scores never leaving the chip: keys go in tiles of 64
+// through LDS, and each query row keeps a running maximum, sum and output that are
+// rescaled when the maximum moves (the online softmax described there and on the
+// gpukit page's fused attention).  Products run on v_mfma_f32_32x32x16_bf16 with f32
+// accumulation; the output is rounded to bf16 once at the end.
+//
+// Work split: a block of 4 waves owns 128 query rows of one (batch, q head); each
+// wave owns 32 rows.  Both products are computed transposed so that one lane always
+// holds one query row:
+//   S^T = K Q^T   (A = K tile from LDS, B = prepped Q held in registers)
+//   O^T += V^T P^T (A = V^T tile from LDS, B = P straight from the S^T registers)
+// With that layout the row maximum is a max over a lane's own 32 scores plus one
+// exchange with lane ^ 32, and the rescale of O needs no exchange at all.
+//
+// The q prologue applies HeadPrep (RMS, qw, split-half turn at the row's position)
+// in registers before rounding q to bf16; it needs half to be 0 or a multiple of 16
+// (then every turned pair sits in one lane).  Other halves are prepped by the prep
+// kernel beforehand.
+//
+// LDS: K is stored row-major [key][d] with rows padded by 16 bytes (conflict-free
+// 16-byte reads down a column).  V is stored transposed [d][key] so that a lane's
+// 8 keys for one d are 16 contiguous bytes; the 16-byte chunks of a row are XOR-
+// swizzled by the row so that both the transposing writes and the reads spread over
+// the banks.  Keys inside each 16-key group are placed in the order the S^T
+// accumulator registers hold them (bits 2 and 3 of the key index swapped), so P needs
+// no shuffling before the second product.
+#include "common.h"
+#include "kernels.h"
+
+namespace attn {
+
+hipError_t launch_prefill_f32(const PrefillLaunch &a, hipStream_t stream);
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kBM = 32 * kWaves;   // query rows per block
+constexpr int kBN = 64;            // keys per tile
+
+__device__ __forceinline__ int vt_swizzle(int row) { return (row ^ (row >> 3)) & 7; }
+
+// Split-half turn of a lane's q values held as NC chunks of 8 (chunk c = d 16c + 8g ..):
+// chunk c < HC pairs with chunk c + HC (half = 16 HC), using table entries d0 .. d0 + 7.
+template <int NC, int HC>
+__device__ __forceinline__ void turn_chunks(float (&x)[NC][8], const float *cr, const float *sr, int g) {
+    if constexpr (HC >= 1 && 2 * HC <= NC) {
+#pragma unroll
+    for (int c = 0; c < HC; ++c) {
+        const int d0 = 16 * c + 8 * g;
+        const float4 c0 = *reinterpret_cast<const float4 *>(cr + d0);
+        const float4 c1 = *reinterpret_cast<const float4 *>(cr + d0 + 4);
+        const float4 s0 = *reinterpret_cast<const float4 *>(sr + d0);
+        const float4 s1 = *reinterpret_cast<const float4 *>(sr + d0 + 4);
+        const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float a = x[c][e], b = x[c + HC][e];
+            x[c][e] = a * cv[e] - b * sv[e];
+            x[c + HC][e] = b * cv[e] + a * sv[e];
+        }
+    }
+    }
+}
+
+template <int D>
+struct Smem {
+    static constexpr int kStride = D + 8;                 // bf16 elements per K row
+    uint16_t k[kBN * kStride];
+    uint16_t vt[D * kBN];                                // [d][64 keys], 128-byte rows
+};
+
+template <int D, bool CAUSAL, bool PREP>
+__global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillLaunch p) {
+    __shared__ Smem<D> sm;
+    constexpr int KS = Smem<D>::kStride;
+    constexpr int NC = D / 16;       // 16-wide d chunks of the q.k product
+    constexpr int NDB = D / 32;      // 32-wide d blocks of the output
+
+    const int tid = threadIdx.x;
+    const int w = tid / 64, lane = tid % 64;
+    const int n = lane % 32, g = lane / 32;
+
+    const int nq_tiles = (int)((p.seq + kBM - 1) / kBM);
+    const int bh = blockIdx.x % (int)(p.batch * p.hq);
+    const int qtile = nq_tiles - 1 - blockIdx.x / (int)(p.batch * p.hq);   // longest first
+    const int b = bh / (int)p.hq, h = bh % (int)p.hq;
+    const int kvh = h / (int)(p.hq / p.hkv);
+
+    const int64_t r = (int64_t)qtile * kBM + 32 * w + n;
+    const bool row_ok = r < p.seq;
+
+    // ---- q prologue: load this lane's 64 (or 32) values of its row, HeadPrep, bf16.
+    bf16x8 qf[NC];
+    {
+        const uint16_t *qrow = static_cast<const uint16_t *>(p.q) +
+                               ((int64_t)b * p.seq + (row_ok ? r : 0)) * p.q_rs + (int64_t)h * D;
+        uint4 raw[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            raw[c] = row_ok ? *reinterpret_cast<const uint4 *>(qrow + 16 * c + 8 * g) : make_uint4(0, 0, 0, 0);
+        if constexpr (PREP) {
+            float x[NC][8];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                unpack_bf16x2(raw[c].x, x[c][0], x[c][1]);
+                unpack_bf16x2(raw[c].y, x[c][2], x[c][3]);
+                unpack_bf16x2(raw[c].z, x[c][4], x[c][5]);
+                unpack_bf16x2(raw[c].w, x[c][6], x[c][7]);
+            }
+            float ss = 0.f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += x[c][e] * x[c][e];
+            ss += __shfl_xor(ss, 32, 64);
+            const float inv = 1.0f / __builtin_sqrtf(ss * (1.0f / D) + p.eps);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const float4 w0 = *reinterpret_cast<const float4 *>(p.qw + 16 * c + 8 * g);
+                const float4 w1 = *reinterpret_cast<const float4 *>(p.qw + 16 * c + 8 * g + 4);
+                const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[c][e] = x[c][e] * inv * wv[e];
+            }
+            const int hc = (int)p.half / 16;     // turned pairs are hc chunks apart
+            if (hc > 0 && row_ok) {
+                const float *cr = p.cos + (p.pos0 + r) * p.half;
+                const float *sr = p.sin + (p.pos0 + r) * p.half;
+                // hc is a run-time value; dispatch to unrolled code so x stays in registers.
+                switch (hc) {
+                    case 1: turn_chunks<NC, 1>(x, cr, sr, g); break;
+                    case 2: turn_chunks<NC, 2>(x, cr, sr, g); break;
+                    case 3: turn_chunks<NC, 3>(x, cr, sr, g); break;
+                    default: turn_chunks<NC, NC / 2>(x, cr, sr, g); break;
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                uint4 u;
+                u.x = pack_bf16x2(x[c][0], x[c][1]);
+                u.y = pack_bf16x2(x[c][2], x[c][3]);
+                u.z = pack_bf16x2(x[c][4], x[c][5]);
+                u.w = pack_bf16x2(x[c][6], x[c][7]);
+                qf[c] = __builtin_bit_cast(bf16x8, u);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) qf[c] = __builtin_bit_cast(bf16x8, raw[c]);
+        }
+    }
+
+    const float C = p.scale * kLog2e;
+    float m_run = -INFINITY, l_run = 0.f;   // l_run: this lane's share of the row sum
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+
+    const int64_t last_key = CAUSAL ? min<int64_t>(p.seq - 1, (int64_t)qtile * kBM + kBM - 1) : p.seq - 1;
+    const int ntiles = (int)(last_key / kBN) + 1;
+    const uint16_t *kbase = static_cast<const uint16_t *>(p.k) + (int64_t)b * p.seq * p.k_rs + (int64_t)kvh * D;
+    const uint16_t *vbase = static_cast<const uint16_t *>(p.v) + (int64_t)b * p.seq * p.v_rs + (int64_t)kvh * D;
+
+    for (int kt = 0; kt < ntiles; ++kt) {
+        const int64_t key0 = (int64_t)kt * kBN;
+        __syncthreads();
+        // K tile -> LDS, row-major with padded rows.
+#pragma unroll
+        for (int it = 0; it < kBN * D / 8 / 256; ++it) {
+            const int idx = it * 256 + tid;
+            const int key = idx / (D / 8), seg = idx % (D / 8);
+            const int64_t j = key0 + key;
+            uint4 val = make_uint4(0, 0, 0, 0);
+            if (j < p.seq) val = *reinterpret_cast<const uint4 *>(kbase + j * p.k_rs + 8 * seg);
+            *reinterpret_cast<uint4 *>(&sm.k[key * KS + 8 * seg]) = val;
+        }
+        // V tile -> LDS transposed: each thread moves 4 keys x 8 d.
+        if (tid < (kBN / 4) * (D / 8)) {
+            const int seg = tid % (D / 8), quad = tid / (D / 8);
+            uint4 vv[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int64_t j = key0 + 4 * quad + jj;
+                vv[jj] = j < p.seq ? *reinterpret_cast<const uint4 *>(vbase + j * p.v_rs + 8 * seg)
+                                   : make_uint4(0, 0, 0, 0);
+            }
+            const int pq = (quad & ~3) | ((quad & 1) << 1) | ((quad >> 1) & 1);
+            const uint32_t wd[4][4] = {{vv[0].x, vv[0].y, vv[0].z, vv[0].w},
+                                       {vv[1].x, vv[1].y, vv[1].z, vv[1].w},
+                                       {vv[2].x, vv[2].y, vv[2].z, vv[2].w},
+                                       {vv[3].x, vv[3].y, vv[3].z, vv[3].w}};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+#pragma unroll
+                for (int hi = 0; hi < 2; ++hi) {
+                    const int row = 8 * seg + 2 * e + hi;
+                    uint32_t lo01, lo23;
+                    if (hi == 0) {
+                        lo01 = (wd[0][e] & 0xFFFFu) | (wd[1][e] << 16);
+                        lo23 = (wd[2][e] & 0xFFFFu) | (wd[3][e] << 16);
+                    } else {
+                        lo01 = (wd[0][e] >> 16) | (wd[1][e] & 0xFFFF0000u);
+                        lo23 = (wd[2][e] >> 16) | (wd[3][e] & 0xFFFF0000u);
+                    }
+                    const int chunk = (pq >> 1) ^ vt_swizzle(row);
+                    *reinterpret_cast<uint2 *>(&sm.vt[row * kBN + chunk * 8 + (pq & 1) * 4]) =
+                        make_uint2(lo01, lo23);
+                }
+            }
+        }
+        __syncthreads();
+
+        // S^T = K Q^T for 2 blocks of 32 keys.
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&sm.k[(kb * 32 + n) * KS + 16 * c + 8 * g]);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
+            }
+        }
+        // Mask: register 4i+jj of block kb holds key key0 + 32 kb + 8 i + 4 g + jj.
+        const bool need_mask = (key0 + kBN > p.seq) || (CAUSAL && key0 + kBN - 1 > (int64_t)qtile * kBM);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int64_t j = key0 + 32 * kb + 8 * (i / 4) + 4 * g + (i % 4);
+                    if (j >= p.seq || (CAUSAL && j > r)) s[kb][i] = -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx * C);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s[kb][i] = fast_exp2(fmaf(s[kb][i], C, -m_use));
+                psum += s[kb][i];
+            }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+
+        // P as the B operand: step u covers keys 16u..16u+15 (registers 8(u%2).. of block u/2).
+        bf16x8 pf[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            uint4 pk;
+            pk.x = pack_bf16x2(s[u / 2][8 * (u % 2) + 0], s[u / 2][8 * (u % 2) + 1]);
+            pk.y = pack_bf16x2(s[u / 2][8 * (u % 2) + 2], s[u / 2][8 * (u % 2) + 3]);
+            pk.z = pack_bf16x2(s[u / 2][8 * (u % 2) + 4], s[u / 2][8 * (u % 2) + 5]);
+            pk.w = pack_bf16x2(s[u / 2][8 * (u % 2) + 6], s[u / 2][8 * (u % 2) + 7]);
+            pf[u] = __builtin_bit_cast(bf16x8, pk);
+        }
+        // O^T += V^T P^T
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int row = 32 * db + n;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int chunk = (2 * u + g) ^ vt_swizzle(row);
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&sm.vt[row * kBN + chunk * 8]);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[u], o[db], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- epilogue: divide by the row sum, round once to bf16, store.
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (row_ok) {
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        uint16_t *orow = static_cast<uint16_t *>(p.out) + ((int64_t)b * p.seq + r) * p.o_rs + (int64_t)h * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint2 u;
+                u.x = pack_bf16x2(o[db][4 * i] * inv, o[db][4 * i + 1] * inv);
+                u.y = pack_bf16x2(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
+                *reinterpret_cast<uint2 *>(orow + 32 * db + 8 * i + 4 * g) = u;
+            }
+    }
+}
+
+template <int D, bool CAUSAL>
+void launch_bf16_d(const PrefillLaunch &a, hipStream_t stream) {
+    const int64_t nq_tiles = (a.seq + kBM - 1) / kBM;
+    const dim3 grid((unsigned)(nq_tiles * a.batch * a.hq));
+    if (a.prep_q)
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false>), grid, dim3(256), 0, stream, a);
+}
+
+}  // namespace
+
+bool prefill_fuses_half(int64_t d, int64_t half, bool bf16) {
+    if (!bf16) return half == 0 || 2 * half == d;
+    return half == 0 || half % 16 == 0;   // pairs 1, 2, 3 or 4 chunks of 16 apart
+}
+
+hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream) {
+    if (!a.bf16) return launch_prefill_f32(a, stream);
+    if (a.d == 64) {
+        if (a.causal) launch_bf16_d<64, true>(a, stream); else launch_bf16_d<64, false>(a, stream);
+    } else {
+        if (a.causal) launch_bf16_d<128, true>(a, stream); else launch_bf16_d<128, false>(a, stream);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace attn

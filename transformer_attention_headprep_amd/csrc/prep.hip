@@ -1,0 +1,188 @@
+// prep.hip -- HeadPrep kernel (gizml:netops reference page, Types > HeadPrep and
+// Functions > headPrepInPlace).
+//
+// One head of d values is one work unit: over its RMS (eps under the root), times
+// its norm weight, then values e < half turned with e + half by the cos/sin row of
+// the token's sequence position.  q and k units share one launch.
+//
+// The pass is HBM-bound (read and write each value once), so the layout is chosen for
+// coalescing: d/8 consecutive lanes own one head, lane i holding the 4 values at
+// 4i.. and the 4 values at d/2 + 4i.., so each wave reads 2 x 64 contiguous 8-byte
+// (bf16) or 16-byte (f32) pieces and, when half = d/2, every turned pair sits in one
+// lane.  Other halves go through LDS.
+#include "common.h"
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+constexpr int kPrepThreads = 256;
+
+struct PrepParams {
+    const void *q_src; void *q_dst; int64_t q_src_rs, q_dst_rs; int64_t hq;
+    const void *k_src; void *k_dst; int64_t k_src_rs, k_dst_rs; int64_t hkv;
+    int64_t seq, pos0, n_q_units, n_units;
+    const float *qw, *kw, *cos, *sin;
+    int half;
+    float eps;
+};
+
+template <bool BF16>
+__device__ __forceinline__ void load4(const void *base, int64_t off, float (&x)[4]) {
+    if constexpr (BF16) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(base) + off);
+        unpack_bf16x2(w.x, x[0], x[1]);
+        unpack_bf16x2(w.y, x[2], x[3]);
+    } else {
+        const float4 w = *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + off);
+        x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store4(void *base, int64_t off, const float (&x)[4]) {
+    if constexpr (BF16) {
+        uint2 w;
+        w.x = pack_bf16x2(x[0], x[1]);
+        w.y = pack_bf16x2(x[2], x[3]);
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(base) + off) = w;
+    } else {
+        *reinterpret_cast<float4 *>(static_cast<float *>(base) + off) =
+            make_float4(x[0], x[1], x[2], x[3]);
+    }
+}
+
+// MODE 0: no turn (half = 0); MODE 1: half = d/2, pairs in-lane; MODE 2: any half, via LDS.
+template <bool BF16, int D, int MODE>
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepParams p) {
+    constexpr int LPH = D / 8;                  // lanes per head
+    constexpr int HPB = kPrepThreads / LPH;     // heads per block
+    __shared__ float stage[MODE == 2 ? HPB * D : 1];
+
+    const int li = threadIdx.x % LPH;
+    const int hb = threadIdx.x / LPH;
+    const int64_t unit = (int64_t)blockIdx.x * HPB + hb;
+    const bool valid = unit < p.n_units;
+    const bool is_q = unit < p.n_q_units;
+
+    const void *src;
+    void *dst;
+    int64_t src_off, dst_off, row;
+    const float *w;
+    if (is_q) {
+        const int64_t u = valid ? unit : 0;
+        row = u / p.hq;
+        const int64_t h = u % p.hq;
+        src = p.q_src; dst = p.q_dst; w = p.qw;
+        src_off = row * p.q_src_rs + h * D;
+        dst_off = row * p.q_dst_rs + h * D;
+    } else {
+        const int64_t u = valid ? unit - p.n_q_units : 0;
+        row = u / p.hkv;
+        const int64_t h = u % p.hkv;
+        src = p.k_src; dst = p.k_dst; w = p.kw;
+        src_off = row * p.k_src_rs + h * D;
+        dst_off = row * p.k_dst_rs + h * D;
+    }
+    const int e_lo = 4 * li, e_hi = D / 2 + 4 * li;
+
+    float lo[4] = {0.f, 0.f, 0.f, 0.f}, hi[4] = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+        load4<BF16>(src, src_off + e_lo, lo);
+        load4<BF16>(src, src_off + e_hi, hi);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ss += lo[i] * lo[i] + hi[i] * hi[i];
+    ss = sum_lanes<LPH>(ss);
+    const float inv = 1.0f / __builtin_sqrtf(ss * (1.0f / D) + p.eps);
+    if (valid) {
+        const float4 wl = *reinterpret_cast<const float4 *>(w + e_lo);
+        const float4 wh = *reinterpret_cast<const float4 *>(w + e_hi);
+        lo[0] = lo[0] * inv * wl.x; lo[1] = lo[1] * inv * wl.y;
+        lo[2] = lo[2] * inv * wl.z; lo[3] = lo[3] * inv * wl.w;
+        hi[0] = hi[0] * inv * wh.x; hi[1] = hi[1] * inv * wh.y;
+        hi[2] = hi[2] * inv * wh.z; hi[3] = hi[3] * inv * wh.w;
+    }
+    const int64_t posrow = p.pos0 + row % p.seq;
+
+    if constexpr (MODE == 1) {
+        if (valid) {
+            const float4 c = *reinterpret_cast<const float4 *>(p.cos + posrow * (D / 2) + e_lo);
+            const float4 s = *reinterpret_cast<const float4 *>(p.sin + posrow * (D / 2) + e_lo);
+            const float cc[4] = {c.x, c.y, c.z, c.w}, sc[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float a = lo[i], b = hi[i];
+                lo[i] = a * cc[i] - b * sc[i];
+                hi[i] = b * cc[i] + a * sc[i];
+            }
+        }
+    } else if constexpr (MODE == 2) {
+        float *st = stage + hb * D;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            st[e_lo + i] = lo[i];
+            st[e_hi + i] = hi[i];
+        }
+        __syncthreads();
+        if (valid) {
+            const int half = p.half;
+            const float *crow = p.cos + posrow * half;
+            const float *srow = p.sin + posrow * half;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = i < 4 ? e_lo + i : e_hi + i - 4;
+                float y = st[e];
+                if (e < half) {
+                    y = st[e] * crow[e] - st[e + half] * srow[e];
+                } else if (e < 2 * half) {
+                    const int f = e - half;
+                    y = st[e] * crow[f] + st[f] * srow[f];
+                }
+                if (i < 4) lo[i] = y; else hi[i - 4] = y;
+            }
+        }
+    }
+    if (valid) {
+        store4<BF16>(dst, dst_off + e_lo, lo);
+        store4<BF16>(dst, dst_off + e_hi, hi);
+    }
+}
+
+template <bool BF16, int D>
+hipError_t launch_prep_d(const PrepParams &p, int mode, hipStream_t stream) {
+    constexpr int HPB = kPrepThreads / (D / 8);
+    const int64_t blocks = (p.n_units + HPB - 1) / HPB;
+    if (blocks == 0) return hipSuccess;
+    if (mode == 0)
+        hipLaunchKernelGGL((prep_kernel<BF16, D, 0>), dim3(blocks), dim3(kPrepThreads), 0, stream, p);
+    else if (mode == 1)
+        hipLaunchKernelGGL((prep_kernel<BF16, D, 1>), dim3(blocks), dim3(kPrepThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((prep_kernel<BF16, D, 2>), dim3(blocks), dim3(kPrepThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prep(const PrepLaunch &a, hipStream_t stream) {
+    PrepParams p;
+    p.q_src = a.q_src; p.q_dst = a.q_dst; p.q_src_rs = a.q_src_rs; p.q_dst_rs = a.q_dst_rs;
+    p.hq = a.q_src ? a.hq : 1;
+    p.k_src = a.k_src; p.k_dst = a.k_dst; p.k_src_rs = a.k_src_rs; p.k_dst_rs = a.k_dst_rs;
+    p.hkv = a.k_src ? a.hkv : 1;
+    p.seq = a.seq;
+    p.pos0 = a.pos0;
+    p.n_q_units = a.q_src ? a.batch * a.seq * a.hq : 0;
+    p.n_units = p.n_q_units + (a.k_src ? a.batch * a.seq * a.hkv : 0);
+    p.qw = a.qw; p.kw = a.kw; p.cos = a.cos; p.sin = a.sin;
+    p.half = (int)a.half;
+    p.eps = a.eps;
+    const int mode = a.half == 0 ? 0 : (2 * a.half == a.d ? 1 : 2);
+    if (a.d == 64)
+        return a.bf16 ? launch_prep_d<true, 64>(p, mode, stream) : launch_prep_d<false, 64>(p, mode, stream);
+    return a.bf16 ? launch_prep_d<true, 128>(p, mode, stream) : launch_prep_d<false, 128>(p, mode, stream);
+}
+
+}  // namespace attn

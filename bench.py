@@ -65,6 +65,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cache-copies", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times), to scale HBM "
+                         "byte counters read by a profiler")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path is built and timed on a single MI355X "
@@ -79,6 +82,15 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n, "copies": 5}))
+        return 0
 
     def to(x, dt="bf16"):
         t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))

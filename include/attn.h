@@ -35,8 +35,9 @@
  * Errors: every argument is checked on the host before anything is enqueued; a call
  * that returns an error has enqueued nothing (it fails closed).  The message of the
  * last failure on the calling thread is available from attn_last_error().
- *   ATTN_ERR_ARG          null pointer, size <= 0, hq % hkv != 0, 2*half > d, a row
- *                         stride smaller than its row, positions past the table, ...
+ *   ATTN_ERR_ARG          null pointer, size < 0, hq % hkv != 0, 2*half > d, a row
+ *                         stride smaller than its row, positions past the table,
+ *                         scale <= 0, ...  (batch or seq 0 is a no-op returning ATTN_OK)
  *   ATTN_ERR_UNSUPPORTED  head dim d not in {64, 128}, or an unknown dtype.
  *   ATTN_ERR_WORKSPACE    decode workspace smaller than attn_decode_workspace_size().
  *   ATTN_ERR_HIP          the HIP runtime reported an error while enqueuing.
@@ -108,7 +109,7 @@ attn_status_t attn_prep(void *q, void *k, int64_t batch, int64_t seq, int64_t hq
  *   prep->kw may be NULL: k then already holds prepped keys (e.g. written by an
  *   earlier attn_prep) and is not modified; q's HeadPrep is still applied.
  *   causal != 0: query t sees keys 0..t (tq = tk, so bottom-right = top-left).
- *   scale multiplies q.k (1/sqrt(d) in the usual model).
+ *   scale multiplies q.k; finite and > 0 (1/sqrt(d) in the usual model).
  */
 attn_status_t attn_prefill(const void *q, void *k, const void *v, void *out,
                            int64_t batch, int64_t seq, int64_t hq, int64_t hkv, int64_t d,

@@ -77,6 +77,8 @@ def _prefill(lib, **kw):
     (dict(prep=_prep(eps=-1.0)), A.ATTN_ERR_ARG),
     (dict(prep=_prep(eps=float("nan"))), A.ATTN_ERR_ARG),
     (dict(scale=float("inf")), A.ATTN_ERR_ARG),
+    (dict(scale=0.0), A.ATTN_ERR_ARG),
+    (dict(scale=-0.1), A.ATTN_ERR_ARG),
     (dict(out=FAKE + 512), A.ATTN_ERR_ARG),             # out overlaps q
 ])
 def test_prefill_rejects(lib, kw, code):

@@ -150,7 +150,7 @@ attn_status_t attn_prefill(const void *q, void *k, const void *v, void *out, int
     if ((st = check_rows("k", k, hkv, d, k_row_stride))) return st;
     if ((st = check_rows("v", v, hkv, d, v_row_stride))) return st;
     if ((st = check_rows("out", out, hq, d, o_row_stride))) return st;
-    if (!std::isfinite(scale)) return fail(ATTN_ERR_ARG, "scale is not finite");
+    if (!std::isfinite(scale) || !(scale > 0.0)) return fail(ATTN_ERR_ARG, "scale must be finite and > 0");
     if (prep) {
         if ((st = check_prep(prep, d, true, false, pos0, seq))) return st;
         if (pos0 < 0) return fail(ATTN_ERR_ARG, "pos0 < 0");
@@ -231,7 +231,7 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
     if (capacity <= 0 || capacity >= ((int64_t)1 << 31)) return fail(ATTN_ERR_ARG, "capacity %lld outside [1, 2^31)", (long long)capacity);
     if (max_len < 1 || max_len > capacity) return fail(ATTN_ERR_ARG, "max_len %lld outside [1, capacity]", (long long)max_len);
     if (splits < 0 || splits > max_len) return fail(ATTN_ERR_ARG, "splits %lld outside [0, max_len]", (long long)splits);
-    if (!std::isfinite(scale)) return fail(ATTN_ERR_ARG, "scale is not finite");
+    if (!std::isfinite(scale) || !(scale > 0.0)) return fail(ATTN_ERR_ARG, "scale must be finite and > 0");
     if (prep) {
         if ((st = check_prep(prep, d, true, false, 0, 0))) return st;
         if (prep->half > 0 && !pos) return fail(ATTN_ERR_ARG, "pos is NULL with a turning HeadPrep");

@@ -48,6 +48,7 @@ attn_status_t check_rows(const char *name, const void *p, int64_t heads, int64_t
     if (heads <= 0) return fail(ATTN_ERR_ARG, "%s: head count %lld <= 0", name, (long long)heads);
     if (rs < heads * d) return fail(ATTN_ERR_ARG, "%s: row stride %lld < heads * d = %lld", name, (long long)rs, (long long)(heads * d));
     if (rs % 8 != 0) return fail(ATTN_ERR_ARG, "%s: row stride %lld not a multiple of 8 elements", name, (long long)rs);
+    if (rs >= ((int64_t)1 << 24)) return fail(ATTN_ERR_ARG, "%s: row stride %lld >= 2^24 elements", name, (long long)rs);
     return ATTN_OK;
 }
 

@@ -20,13 +20,22 @@
 // so there is one barrier per tile.  Two blocks fit a CU (2 waves per SIMD), so the
 // softmax arithmetic of one wave overlaps the matrix products of the other.
 //
-// Online softmax in base-2 units (scale log2 e folded into one FMA before v_exp_f32).
-// The running maximum is only raised when a tile's maximum exceeds it by more than
-// 2^8: the weights 2^(s - m) then stay below 256, which f32 sums and bf16 weights hold
-// exactly as well as weights below 1, and the rescale of O (64 multiplies a lane) is
-// skipped on almost every tile.  The result is the same softmax: numerator and
-// denominator use the same m.  The row sum adds the bf16-rounded weights that the
-// P V product uses (v_dot2_f32_bf16), so numerator and denominator match.
+// Online softmax in base-2 units.  A prepped q (computed in f32 anyway) is multiplied
+// by scale log2 e before it is rounded to bf16, and every S^T accumulation starts from
+// -m (the row's running maximum, held in 16 registers), so the matrix core returns
+// s log2 e - m directly and the weights are a bare v_exp_f32 of the accumulator.  A q
+// given without HeadPrep is used as it is (rescaling it would round it a second time)
+// and the exponent takes one multiply by scale log2 e instead.  The running maximum is only
+// raised when a tile's maximum exceeds it by more than 8 (base 2): the weights
+// 2^(s - m) then stay below 256, which f32 sums and bf16 weights hold exactly as well
+// as weights below 1, and the rescale of O (64 multiplies a lane) is skipped on almost
+// every tile.  The result is the same softmax: numerator and denominator use the same
+// m.  The row sum adds the bf16-rounded weights that the P V product uses
+// (v_dot2_f32_bf16), so numerator and denominator match.
+//
+// K and V tiles are read with buffer loads whose descriptor starts at the tile and
+// ends at the sequence: rows past the end read as zero with no branch, and the tile
+// offset is scalar arithmetic.
 //
 // The q prologue applies HeadPrep (RMS, qw, split-half turn at the row's position)
 // in registers before rounding q to bf16; it needs half to be 0 or a multiple of 16
@@ -101,23 +110,41 @@ struct Staged {
     uint4 v[4];
 };
 
+// Buffer descriptor over `bytes` bytes from `base` (raw, untyped; reads past the end
+// return zero).
+// The arguments are block-uniform; readfirstlane puts the descriptor in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base, int64_t bytes) {
+    const int n = bytes > 0 ? (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF) : 0;
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *sbase = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(sbase, (short)0, __builtin_amdgcn_readfirstlane(n), 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+    return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
+}
+
+// Loads the 64-key tile that starts at key0; the descriptors end with the sequence's
+// last row, so keys past the sequence read as zero.
 template <int D>
 __device__ __forceinline__ void load_tile(Staged<D> &st, const uint16_t *kbase, const uint16_t *vbase,
-                                          int64_t k_rs, int64_t v_rs, int64_t key0, int64_t seq, int tid) {
+                                          int k_rs, int v_rs, int key0, int seq, int tid) {
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase + (int64_t)key0 * k_rs, ((int64_t)(seq - 1 - key0) * k_rs + D) * 2);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase + (int64_t)key0 * v_rs, ((int64_t)(seq - 1 - key0) * v_rs + D) * 2);
 #pragma unroll
     for (int it = 0; it < Staged<D>::KL; ++it) {
         const int idx = it * 256 + tid;
         const int key = idx / (D / 8), seg = idx % (D / 8);
-        const int64_t j = key0 + key;
-        st.k[it] = j < seq ? *reinterpret_cast<const uint4 *>(kbase + j * k_rs + 8 * seg) : make_uint4(0, 0, 0, 0);
+        st.k[it] = buffer_load16(rk, (key * k_rs + 8 * seg) * 2);
     }
     if (tid < (kBN / 4) * (D / 8)) {
         const int seg = tid % (D / 8), quad = tid / (D / 8);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int64_t j = key0 + 4 * quad + jj;
-            st.v[jj] = j < seq ? *reinterpret_cast<const uint4 *>(vbase + j * v_rs + 8 * seg) : make_uint4(0, 0, 0, 0);
-        }
+        for (int jj = 0; jj < 4; ++jj) st.v[jj] = buffer_load16(rv, ((4 * quad + jj) * v_rs + 8 * seg) * 2);
     }
 }
 
@@ -202,8 +229,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillLaunc
     const uint16_t *vbase = static_cast<const uint16_t *>(p.v) + (int64_t)b * p.seq * p.v_rs + (int64_t)kvh * D;
 
     // First tile on its way before the q prologue.
+    const int seq = (int)p.seq, k_rs = (int)p.k_rs, v_rs = (int)p.v_rs;
     Staged<D> st;
-    load_tile<D>(st, kbase, vbase, p.k_rs, p.v_rs, 0, p.seq, tid);
+    load_tile<D>(st, kbase, vbase, k_rs, v_rs, 0, seq, tid);
+
+    const float C = p.scale * kLog2e;       // q is scaled by this before it is rounded
 
     // ---- q prologue: load this lane's 64 (or 32) values of its row, HeadPrep, bf16.
     bf16x8 qf[NC];
@@ -238,6 +268,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillLaunc
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[c][e] = x[c][e] * inv * wv[e];
             }
+
             const int hc = (int)p.half / 16;     // turned pairs are hc chunks apart
             if (hc > 0 && row_ok) {
                 const float *cr = p.cos + (p.pos0 + r) * p.half;
@@ -253,20 +284,26 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillLaunc
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 uint4 u;
-                u.x = pack_bf16x2(x[c][0], x[c][1]);
-                u.y = pack_bf16x2(x[c][2], x[c][3]);
-                u.z = pack_bf16x2(x[c][4], x[c][5]);
-                u.w = pack_bf16x2(x[c][6], x[c][7]);
+                u.x = pack_bf16x2(x[c][0] * C, x[c][1] * C);
+                u.y = pack_bf16x2(x[c][2] * C, x[c][3] * C);
+                u.z = pack_bf16x2(x[c][4] * C, x[c][5] * C);
+                u.w = pack_bf16x2(x[c][6] * C, x[c][7] * C);
                 qf[c] = __builtin_bit_cast(bf16x8, u);
             }
         } else {
+            // q is taken as given: scaling it before the product would round it twice.
 #pragma unroll
             for (int c = 0; c < NC; ++c) qf[c] = __builtin_bit_cast(bf16x8, raw[c]);
         }
     }
+    // Accumulator units: base 2 when q carries scale log2 e (PREP), else raw q.k, which
+    // the exponent then scales.
+    const float sc = PREP ? 1.0f : C;
 
-    const float C = p.scale * kLog2e;
     float m_run = -INFINITY, l_run = 0.f;   // l_run: this lane's share of the row sum
+    f32x16 bias;                             // -m_run (0 until the first visible key)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bias[i] = 0.f;
     f32x16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -278,32 +315,32 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillLaunc
     __syncthreads();
 
     for (int kt = 0; kt < ntiles; ++kt) {
-        const int64_t key0 = (int64_t)kt * kBN;
+        const int key0 = kt * kBN;
         const TileBuf<D> &buf = bufs[kt & 1];
         const bool more = kt + 1 < ntiles;
-        if (more) load_tile<D>(st, kbase, vbase, p.k_rs, p.v_rs, key0 + kBN, p.seq, tid);
+        if (more) load_tile<D>(st, kbase, vbase, k_rs, v_rs, key0 + kBN, seq, tid);
 
-        // S^T = K Q^T for 2 blocks of 32 keys.
+        // S^T = K Q^T - m for 2 blocks of 32 keys (two independent accumulation chains).
         f32x16 s[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int c = 0; c < NC; ++c) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
+            for (int kb = 0; kb < 2; ++kb) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&buf.k[(kb * 32 + n) * KS + 16 * c + 8 * g]);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[kb], 0, 0, 0);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], c == 0 ? bias : s[kb], 0, 0, 0);
             }
         }
         // Mask: register 4i+jj of block kb holds key key0 + 32 kb + 8 i + 4 g + jj.
-        const bool need_mask = (key0 + kBN > p.seq) || (CAUSAL && key0 + kBN - 1 > (int64_t)qtile * kBM);
+        const int row = (int)r;
+        const bool need_mask = (key0 + kBN > seq) || (CAUSAL && key0 + kBN - 1 > qtile * kBM);
         if (need_mask) {
+            const int lim = CAUSAL ? min(seq - 1, row) : seq - 1;   // last visible key
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int64_t j = key0 + 32 * kb + 8 * (i / 4) + 4 * g + (i % 4);
-                    if (j >= p.seq || (CAUSAL && j > r)) s[kb][i] = -INFINITY;
+                    const int j = key0 + 32 * kb + 8 * (i / 4) + 4 * g + (i % 4);
+                    if (j > lim) s[kb][i] = -INFINITY;
                 }
         }
         float mx = fmaxf(s[0][0], s[0][1]);
@@ -311,20 +348,26 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillLaunc
         for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[0][i], s[0][i + 1]));
 #pragma unroll
         for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[1][i], s[1][i + 1]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_tile = mx * C;                          // scale > 0
-        const bool raise = m_tile > m_run + kRaiseAbove;
-        if (__builtin_amdgcn_ballot_w64(raise)) {            // wave-uniform branch
-            const float m_new = raise ? m_tile : m_run;
-            const float alpha = fast_exp2(m_run - m_new);   // 0 on the first visible tile
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));               // tile max of s - m
+        const bool first = m_run == -INFINITY;
+        const bool raise = first ? mx > -INFINITY : mx * sc > kRaiseAbove;
+        if (__builtin_amdgcn_ballot_w64(raise)) {            // wave-uniform, rare
+            const float delta = raise ? mx : 0.f;
+            const float alpha = fast_exp2(-delta * sc);
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-            m_run = m_new;
+            if (raise) m_run = (first ? 0.f : m_run) + delta;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[kb][i] -= delta;
+            const float nb = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) bias[i] = nb;
         }
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
         // P as the B operand: step u covers keys 16u..16u+15 (registers 8(u%2).. of block u/2).
         bf16x8 pf[4];
@@ -332,7 +375,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillLaunc
         for (int u = 0; u < 4; ++u) {
             float e8[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) e8[i] = fast_exp2(fmaf(s[u / 2][8 * (u % 2) + i], C, -m_use));
+            for (int i = 0; i < 8; ++i) e8[i] = fast_exp2(s[u / 2][8 * (u % 2) + i] * sc);
             uint4 pk;
             pk.x = pack_bf16x2(e8[0], e8[1]);
             pk.y = pack_bf16x2(e8[2], e8[3]);
@@ -344,14 +387,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillLaunc
             l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk.w), ones, l_run, false);
             pf[u] = __builtin_bit_cast(bf16x8, pk);
         }
-        // O^T += V^T P^T
+        // O^T += V^T P^T (the NDB output blocks are independent chains)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            const int row = 32 * db + n;
+        for (int u = 0; u < 4; ++u) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int chunk = (2 * u + g) ^ vt_swizzle(row);
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&buf.vt[row * kBN + chunk * 8]);
+            for (int db = 0; db < NDB; ++db) {
+                const int vrow = 32 * db + n;
+                const int chunk = (2 * u + g) ^ vt_swizzle(vrow);
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&buf.vt[vrow * kBN + chunk * 8]);
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[u], o[db], 0, 0, 0);
             }
         }

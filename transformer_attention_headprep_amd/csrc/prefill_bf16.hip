@@ -11,48 +11,47 @@
 // wave owns 32 rows.  Both products are computed transposed so that one lane always
 // holds one query row:
 //   S^T = K Q^T   (A = K tile from LDS, B = prepped Q held in registers)
-//   O^T += V^T P^T (A = V^T tile from LDS, B = P straight from the S^T registers)
+//   O^T += V^T P^T (A = V^T read from LDS with ds_read_b64_tr_b16, B = P straight
+//                   from the S^T accumulator registers)
 // With that layout the row maximum is a max over a lane's own 32 scores plus one
-// exchange with lane ^ 32, and the rescale of O needs no exchange at all.
+// exchange with lane ^ 32 (v_permlane32_swap), and the rescale of O needs no exchange.
 //
-// Pipeline: two LDS tile buffers; while a tile is consumed, the next one is already
-// in flight from HBM into registers, and is written to the other buffer afterwards,
-// so there is one barrier per tile.  Two blocks fit a CU (2 waves per SIMD), so the
-// softmax arithmetic of one wave overlaps the matrix products of the other.
+// Tiles move HBM -> LDS by buffer loads that write LDS directly (no registers, no LDS
+// store instructions), double-buffered: tile kt+1 is in flight while tile kt is used,
+// one barrier per tile.  The buffer descriptor of a tile ends with the sequence, so
+// keys past its end arrive as zeros.  K rows are stored 16 bytes wider than their data
+// and V rows 32 bytes wider (the extra slots are filled by the same loads), which
+// makes the column reads of both products free of bank conflicts with every LDS
+// offset an immediate.  Two blocks fit a CU (2 waves per SIMD).
+//
+// The ds_read_b64_tr_b16 layout (gfx950): in each group of 16 lanes, lane i receives
+// element (i mod 4) of the 4-element vectors addressed by lanes 4r + i/4, r = 0..3.
+// So lanes 4r .. 4r+3 address 4 consecutive values of key row r, and every lane
+// receives one column (one d) across 4 keys: the A fragment of V^T.
 //
 // Online softmax in base-2 units.  A prepped q (computed in f32 anyway) is multiplied
 // by scale log2 e before it is rounded to bf16, and every S^T accumulation starts from
 // -m (the row's running maximum, held in 16 registers), so the matrix core returns
 // s log2 e - m directly and the weights are a bare v_exp_f32 of the accumulator.  A q
 // given without HeadPrep is used as it is (rescaling it would round it a second time)
-// and the exponent takes one multiply by scale log2 e instead.  The running maximum is only
-// raised when a tile's maximum exceeds it by more than 8 (base 2): the weights
+// and the exponent takes one multiply by scale log2 e instead.  The running maximum is
+// only raised when a tile's maximum exceeds it by more than 8 (base 2): the weights
 // 2^(s - m) then stay below 256, which f32 sums and bf16 weights hold exactly as well
 // as weights below 1, and the rescale of O (64 multiplies a lane) is skipped on almost
 // every tile.  The result is the same softmax: numerator and denominator use the same
 // m.  The row sum adds the bf16-rounded weights that the P V product uses
 // (v_dot2_f32_bf16), so numerator and denominator match.
 //
-// K and V tiles are read with buffer loads whose descriptor starts at the tile and
-// ends at the sequence: rows past the end read as zero with no branch, and the tile
-// offset is scalar arithmetic.
-//
 // The q prologue applies HeadPrep (RMS, qw, split-half turn at the row's position)
 // in registers before rounding q to bf16; it needs half to be 0 or a multiple of 16
 // (then every turned pair sits in one lane).  Other halves are prepped by the prep
 // kernel beforehand.
 //
-// LDS: K is stored row-major [key][d] with rows padded by 16 bytes (conflict-free
-// 16-byte reads down a column).  V is stored transposed [d][key] so that a lane's
-// 8 keys for one d are 16 contiguous bytes; the 16-byte chunks of a row are XOR-
-// swizzled by the row so that both the transposing writes and the reads spread over
-// the banks.  Keys inside each 16-key group are placed in the order the S^T
-// accumulator registers hold them (bits 2 and 3 of the key index swapped), so P needs
-// no shuffling before the second product.
-//
 // Block order: longest causal query tiles first; when the (batch, kv head) pairs
 // divide evenly over the 8 XCDs, every pair's blocks go to one XCD (blocks are
 // dealt to XCDs round-robin), so its K/V stay in that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -68,7 +67,21 @@ constexpr int kBN = 64;            // keys per tile
 constexpr int kXcds = 8;
 constexpr float kRaiseAbove = 8.0f;   // base-2 headroom before the running max moves
 
-__device__ __forceinline__ int vt_swizzle(int row) { return (row ^ (row >> 3)) & 7; }
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+extern __shared__ __attribute__((aligned(16))) unsigned char prefill_smem[];
+
+// 16 bytes per lane from a buffer straight into LDS: lane L writes lds + 16 L.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, void *lds, int voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 16, voffset,
+                                             0, 0, 0);
+}
+
+// The value held by lane ^ 32 (v_permlane32_swap: no LDS round trip).
+__device__ __forceinline__ float lane_pair(float x, int g) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(g == 0 ? r[1] : r[0]);
+}
 
 // Split-half turn of a lane's q values held as NC chunks of 8 (chunk c = d 16c + 8g ..):
 // chunk c < HC pairs with chunk c + HC (half = 16 HC), using table entries d0 .. d0 + 7.
@@ -94,26 +107,27 @@ __device__ __forceinline__ void turn_chunks(float (&x)[NC][8], const float *cr, 
     }
 }
 
+// LDS geometry of one tile buffer for head dim D.
 template <int D>
-struct TileBuf {
-    static constexpr int kStride = D + 8;                 // bf16 elements per K row
-    uint16_t k[kBN * kStride];
-    uint16_t vt[D * kBN];                                // [d][64 keys], 128-byte rows
-};
-
-// One tile's K and V as this thread moves them: KL 16-byte pieces of K, and 4 keys x
-// 8 values of V (V is transposed on its way into LDS).
-template <int D>
-struct Staged {
-    static constexpr int KL = kBN * D / 8 / 256;
-    uint4 k[KL];
-    uint4 v[4];
+struct Geo {
+    static constexpr int kRow = 2 * D;                   // data bytes of one key row
+    static constexpr int kChunks = D / 8;                // 16-byte chunks of data per row
+    static constexpr int kKStride = kRow + 16;           // K row pitch (one pad slot)
+    static constexpr int kVStride = kRow + 32;           // V row pitch (two pad slots)
+    static constexpr int kKSlots = kKStride / 16;
+    static constexpr int kVSlots = kVStride / 16;
+    static constexpr int kKBytes = kBN * kKStride;
+    static constexpr int kVBytes = kBN * kVStride;
+    static constexpr int kBufBytes = kKBytes + kVBytes;
+    static constexpr int kKLoads = kBN * kKSlots / 64;   // 64-lane loads per K tile
+    static constexpr int kVLoads = kBN * kVSlots / 64;
+    static constexpr int kPerWave = (kVLoads + 1) / 2;   // waves 0,1 load K; 2,3 load V
+    static_assert(kBN * kKSlots % 64 == 0 && kBN * kVSlots % 64 == 0, "whole 64-lane loads");
 };
 
 // Buffer descriptor over `bytes` bytes from `base` (raw, untyped; reads past the end
-// return zero).
-// The arguments are block-uniform; readfirstlane puts the descriptor in scalar registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base, int64_t bytes) {
+// return zero).  The arguments are block-uniform; readfirstlane keeps it in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const uint16_t *base, int64_t bytes) {
     const int n = bytes > 0 ? (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF) : 0;
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
@@ -122,68 +136,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base
     return __builtin_amdgcn_make_buffer_rsrc(sbase, (short)0, __builtin_amdgcn_readfirstlane(n), 0x00020000);
 }
 
-__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
-    typedef int v4i __attribute__((ext_vector_type(4)));
-    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
-    return make_uint4((uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w);
-}
-
-// Loads the 64-key tile that starts at key0; the descriptors end with the sequence's
-// last row, so keys past the sequence read as zero.
-template <int D>
-__device__ __forceinline__ void load_tile(Staged<D> &st, const uint16_t *kbase, const uint16_t *vbase,
-                                          int k_rs, int v_rs, int key0, int seq, int tid) {
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase + (int64_t)key0 * k_rs, ((int64_t)(seq - 1 - key0) * k_rs + D) * 2);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase + (int64_t)key0 * v_rs, ((int64_t)(seq - 1 - key0) * v_rs + D) * 2);
-#pragma unroll
-    for (int it = 0; it < Staged<D>::KL; ++it) {
-        const int idx = it * 256 + tid;
-        const int key = idx / (D / 8), seg = idx % (D / 8);
-        st.k[it] = buffer_load16(rk, (key * k_rs + 8 * seg) * 2);
-    }
-    if (tid < (kBN / 4) * (D / 8)) {
-        const int seg = tid % (D / 8), quad = tid / (D / 8);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) st.v[jj] = buffer_load16(rv, ((4 * quad + jj) * v_rs + 8 * seg) * 2);
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(TileBuf<D> &buf, const Staged<D> &st, int tid) {
-    constexpr int KS = TileBuf<D>::kStride;
-#pragma unroll
-    for (int it = 0; it < Staged<D>::KL; ++it) {
-        const int idx = it * 256 + tid;
-        const int key = idx / (D / 8), seg = idx % (D / 8);
-        *reinterpret_cast<uint4 *>(&buf.k[key * KS + 8 * seg]) = st.k[it];
-    }
-    if (tid < (kBN / 4) * (D / 8)) {
-        const int seg = tid % (D / 8), quad = tid / (D / 8);
-        const int pq = (quad & ~3) | ((quad & 1) << 1) | ((quad >> 1) & 1);
-        const uint32_t wd[4][4] = {{st.v[0].x, st.v[0].y, st.v[0].z, st.v[0].w},
-                                   {st.v[1].x, st.v[1].y, st.v[1].z, st.v[1].w},
-                                   {st.v[2].x, st.v[2].y, st.v[2].z, st.v[2].w},
-                                   {st.v[3].x, st.v[3].y, st.v[3].z, st.v[3].w}};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-#pragma unroll
-            for (int hi = 0; hi < 2; ++hi) {
-                const int row = 8 * seg + 2 * e + hi;
-                // pack value (row) of keys 4quad .. 4quad+3: low halves (even d) or high halves (odd d)
-                const uint32_t sel = hi == 0 ? 0x05040100u : 0x07060302u;
-                const uint32_t lo01 = __builtin_amdgcn_perm(wd[1][e], wd[0][e], sel);
-                const uint32_t lo23 = __builtin_amdgcn_perm(wd[3][e], wd[2][e], sel);
-                const int chunk = (pq >> 1) ^ vt_swizzle(row);
-                *reinterpret_cast<uint2 *>(&buf.vt[row * kBN + chunk * 8 + (pq & 1) * 4]) = make_uint2(lo01, lo23);
-            }
-        }
-    }
-}
-
 template <int D, bool CAUSAL, bool PREP>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillLaunch p) {
-    __shared__ TileBuf<D> bufs[2];
-    constexpr int KS = TileBuf<D>::kStride;
+    typedef Geo<D> G;
+    unsigned char *smem = prefill_smem;                                  // 2 tile buffers
     constexpr int NC = D / 16;       // 16-wide d chunks of the q.k product
     constexpr int NDB = D / 32;      // 32-wide d blocks of the output
 
@@ -222,16 +178,41 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillLaunc
 
     const int64_t r = (int64_t)qtile * kBM + 32 * w + n;
     const bool row_ok = r < p.seq;
+    const int seq = (int)p.seq;
 
     const int64_t last_key = CAUSAL ? min<int64_t>(p.seq - 1, (int64_t)qtile * kBM + kBM - 1) : p.seq - 1;
     const int ntiles = (int)(last_key / kBN) + 1;
-    const uint16_t *kbase = static_cast<const uint16_t *>(p.k) + (int64_t)b * p.seq * p.k_rs + (int64_t)kvh * D;
-    const uint16_t *vbase = static_cast<const uint16_t *>(p.v) + (int64_t)b * p.seq * p.v_rs + (int64_t)kvh * D;
+
+    // ---- tile loads: waves 0 and 1 move K, waves 2 and 3 move V; load t of a wave
+    // fills 64 consecutive 16-byte slots; a slot past a row's data repeats its last
+    // chunk (it is padding, never read).
+    const bool loads_k = w < 2;
+    const int wl = w & 1;
+    const int nloads = loads_k ? (G::kKLoads - wl + 1) / 2 : (G::kVLoads - wl + 1) / 2;
+    const int64_t rs = loads_k ? p.k_rs : p.v_rs;
+    const uint16_t *src = static_cast<const uint16_t *>(loads_k ? p.k : p.v) +
+                          (int64_t)b * p.seq * rs + (int64_t)kvh * D;
+    const int slots = loads_k ? G::kKSlots : G::kVSlots;
+    int voff[G::kPerWave];
+#pragma unroll
+    for (int t = 0; t < G::kPerWave; ++t) {
+        const int sidx = (wl + 2 * t) * 64 + lane;
+        const int row = sidx / slots, col = sidx % slots;
+        voff[t] = (int)(row * rs + 8 * min(col, G::kChunks - 1)) * 2;
+    }
+    auto load_tile = [&](int kt, int bsel) {
+        const int key0 = kt * kBN;
+        const __amdgpu_buffer_rsrc_t rsrc = seq_rsrc(src + (int64_t)key0 * rs, ((int64_t)(seq - 1 - key0) * rs + D) * 2);
+        unsigned char *dst = smem + bsel * G::kBufBytes + (loads_k ? 0 : G::kKBytes);
+#pragma unroll
+        for (int t = 0; t < G::kPerWave; ++t) {
+            if (t < nloads)
+                buffer_to_lds16(rsrc, dst + (wl + 2 * t) * 1024, voff[t]);
+        }
+    };
 
     // First tile on its way before the q prologue.
-    const int seq = (int)p.seq, k_rs = (int)p.k_rs, v_rs = (int)p.v_rs;
-    Staged<D> st;
-    load_tile<D>(st, kbase, vbase, k_rs, v_rs, 0, seq, tid);
+    load_tile(0, 0);
 
     const float C = p.scale * kLog2e;       // q is scaled by this before it is rounded
 
@@ -299,7 +280,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillLaunc
     // Accumulator units: base 2 when q carries scale log2 e (PREP), else raw q.k, which
     // the exponent then scales.
     const float sc = PREP ? 1.0f : C;
-
     float m_run = -INFINITY, l_run = 0.f;   // l_run: this lane's share of the row sum
     f32x16 bias;                             // -m_run (0 until the first visible key)
 #pragma unroll
@@ -311,14 +291,19 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillLaunc
         for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    store_tile<D>(bufs[0], st, tid);
+    // Per-lane LDS byte offsets (the rest of every address is an immediate).
+    const int k_lane = n * G::kKStride + 16 * g;                        // K row n, chunk g
+    const int j16 = lane % 16, rg = (lane % 32) / 16;
+    const int v_lane = G::kKBytes + (4 * g + j16 / 4) * G::kVStride + (16 * rg + 4 * (j16 % 4)) * 2;
+
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int kt = 0; kt < ntiles; ++kt) {
         const int key0 = kt * kBN;
-        const TileBuf<D> &buf = bufs[kt & 1];
-        const bool more = kt + 1 < ntiles;
-        if (more) load_tile<D>(st, kbase, vbase, k_rs, v_rs, key0 + kBN, seq, tid);
+        const int bsel = kt & 1;
+        if (kt + 1 < ntiles) load_tile(kt + 1, bsel ^ 1);
+        const unsigned char *buf = smem + bsel * G::kBufBytes;
 
         // S^T = K Q^T - m for 2 blocks of 32 keys (two independent accumulation chains).
         f32x16 s[2];
@@ -326,29 +311,26 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillLaunc
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&buf.k[(kb * 32 + n) * KS + 16 * c + 8 * g]);
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(buf + k_lane + kb * 32 * G::kKStride + 32 * c);
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], c == 0 ? bias : s[kb], 0, 0, 0);
             }
         }
         // Mask: register 4i+jj of block kb holds key key0 + 32 kb + 8 i + 4 g + jj.
-        const int row = (int)r;
         const bool need_mask = (key0 + kBN > seq) || (CAUSAL && key0 + kBN - 1 > qtile * kBM);
         if (need_mask) {
-            const int lim = CAUSAL ? min(seq - 1, row) : seq - 1;   // last visible key
+            const int lim = (CAUSAL ? min(seq - 1, (int)r) : seq - 1) - (key0 + 4 * g);   // last visible
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int j = key0 + 32 * kb + 8 * (i / 4) + 4 * g + (i % 4);
-                    if (j > lim) s[kb][i] = -INFINITY;
-                }
+                for (int i = 0; i < 16; ++i)
+                    if (32 * kb + 8 * (i / 4) + (i % 4) > lim) s[kb][i] = -INFINITY;
         }
         float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
         for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[0][i], s[0][i + 1]));
 #pragma unroll
         for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[1][i], s[1][i + 1]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));               // tile max of s - m
+        mx = fmaxf(mx, lane_pair(mx, g));                     // tile max of s - m
         const bool first = m_run == -INFINITY;
         const bool raise = first ? mx > -INFINITY : mx * sc > kRaiseAbove;
         if (__builtin_amdgcn_ballot_w64(raise)) {            // wave-uniform, rare
@@ -369,7 +351,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillLaunc
             for (int i = 0; i < 16; ++i) bias[i] = nb;
         }
 
-        // P as the B operand: step u covers keys 16u..16u+15 (registers 8(u%2).. of block u/2).
+        // P as the B operand: step u covers keys 16u..16u+15 (registers 8(u%2).. of block u/2),
+        // slot s of lane half g holding key 16u + 8(s/4) + 4g + s%4.
         bf16x8 pf[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -387,18 +370,20 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillLaunc
             l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk.w), ones, l_run, false);
             pf[u] = __builtin_bit_cast(bf16x8, pk);
         }
-        // O^T += V^T P^T (the NDB output blocks are independent chains)
+        // O^T += V^T P^T: the A fragment of (d block db, keys of step u) is two transposing
+        // reads, keys 16u + 4g + 0..3 and 16u + 8 + 4g + 0..3 (the slot order of P).
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const int vrow = 32 * db + n;
-                const int chunk = (2 * u + g) ^ vt_swizzle(vrow);
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&buf.vt[vrow * kBN + chunk * 8]);
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[u], o[db], 0, 0, 0);
+                const unsigned char *va = buf + v_lane + 16 * u * G::kVStride + 64 * db;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(va));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(va + 8 * G::kVStride));
+                const i16x4 both[2] = {lo, hi};
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pf[u], o[db], 0, 0, 0);
             }
         }
-        if (more) store_tile<D>(bufs[(kt + 1) & 1], st, tid);
+        __builtin_amdgcn_s_waitcnt(0);        // this wave's loads of tile kt+1 are in LDS
         __syncthreads();
     }
 
@@ -423,10 +408,11 @@ template <int D, bool CAUSAL>
 void launch_bf16_d(const PrefillLaunch &a, hipStream_t stream) {
     const int64_t nq_tiles = (a.seq + kBM - 1) / kBM;
     const dim3 grid((unsigned)(nq_tiles * a.batch * a.hq));
+    const size_t lds = 2 * Geo<D>::kBufBytes;
     if (a.prep_q)
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true>), grid, dim3(256), lds, stream, a);
     else
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false>), grid, dim3(256), lds, stream, a);
 }
 
 }  // namespace

@@ -20,9 +20,11 @@
 // store instructions), double-buffered: tile kt+1 is in flight while tile kt is used,
 // one barrier per tile.  The buffer descriptor of a tile ends with the sequence, so
 // keys past its end arrive as zeros.  K rows are stored 16 bytes wider than their data
-// and V rows 32 bytes wider (the extra slots are filled by the same loads), which
-// makes the column reads of both products free of bank conflicts with every LDS
-// offset an immediate.  Two blocks fit a CU (2 waves per SIMD).
+// and V rows 64 bytes wider (the extra slots are filled by the same loads): K row
+// pitches step 4 banks, so the 16-byte reads of 16 consecutive key rows cover all 64
+// banks once; V row pitches step 16 banks, so the transposing reads of 4 key rows x 64
+// bytes by 32 lanes do too.  Every LDS offset is then an immediate.  Two blocks fit a
+// CU (2 waves per SIMD).
 //
 // The ds_read_b64_tr_b16 layout (gfx950): in each group of 16 lanes, lane i receives
 // element (i mod 4) of the 4-element vectors addressed by lanes 4r + i/4, r = 0..3.
@@ -113,7 +115,7 @@ struct Geo {
     static constexpr int kRow = 2 * D;                   // data bytes of one key row
     static constexpr int kChunks = D / 8;                // 16-byte chunks of data per row
     static constexpr int kKStride = kRow + 16;           // K row pitch (one pad slot)
-    static constexpr int kVStride = kRow + 32;           // V row pitch (two pad slots)
+    static constexpr int kVStride = kRow + 64;           // V row pitch (four pad slots)
     static constexpr int kKSlots = kKStride / 16;
     static constexpr int kVSlots = kVStride / 16;
     static constexpr int kKBytes = kBN * kKStride;
@@ -137,7 +139,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const uint16_t *base,
 }
 
 template <int D, bool CAUSAL, bool PREP>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(const PrefillLaunch p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(const PrefillLaunch p) {
     typedef Geo<D> G;
     unsigned char *smem = prefill_smem;                                  // 2 tile buffers
     constexpr int NC = D / 16;       // 16-wide d chunks of the q.k product

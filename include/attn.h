@@ -136,7 +136,9 @@ attn_status_t attn_prefill(const void *q, void *k, const void *v, void *out,
  *             rounding.
  *   workspace device scratch of at least attn_decode_workspace_size(...) bytes with
  *             the same batch, hq, hkv, d, max_len and splits.  Contents on entry are
- *             ignored.  Calls that share a workspace must not overlap in time.
+ *             ignored.  Calls that share a workspace must not overlap in time.  The
+ *             size is 0 when the call runs as a single split (the output is then
+ *             written directly); workspace may be NULL in that case.
  *   Device-side values the host cannot check: lens[b] == 0 gives a zero output row;
  *   lens[b] < 0, lens[b] > max_len, or a pos[b] outside [0, table_rows) gives NaN in
  *   that sequence's output rows (nothing outside the buffers is read).

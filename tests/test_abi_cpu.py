@@ -117,9 +117,10 @@ def test_prep_empty_is_a_no_op(lib):
 
 
 def _decode(lib, **kw):
+    # splits=4: the call needs a workspace, so every case below fails on the host.
     a = dict(q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), out=FAKE + (3 << 32), batch=32, hq=32,
              hkv=8, d=128, cap=4096, lens=FAKE + (4 << 32), pos=FAKE + (5 << 32), max_len=4096,
-             prep=_prep(rows=4097), scale=0.088, splits=0, ws=FAKE + (6 << 32), ws_bytes=1 << 30,
+             prep=_prep(rows=4097), scale=0.088, splits=4, ws=FAKE + (6 << 32), ws_bytes=1 << 30,
              dtype=A.ATTN_BF16)
     a.update(kw)
     prep = ctypes.byref(a["prep"]) if a["prep"] is not None else None
@@ -147,9 +148,15 @@ def test_decode_rejects(lib, kw, code):
 
 
 def test_decode_sizes(lib):
-    s = lib.attn_decode_default_splits(32, 32, 8, 4096)
-    assert s >= 1
-    assert lib.attn_decode_workspace_size(32, 32, 8, 128, 4096, 0) == s * 32 * 32 * 130 * 4
+    # 256 (sequence, kv head) units already give every CU a block: one split, no workspace
+    assert lib.attn_decode_default_splits(32, 32, 8, 4096) == 1
+    assert lib.attn_decode_workspace_size(32, 32, 8, 128, 4096, 0) == 0
+    assert lib.attn_decode_workspace_size(32, 32, 8, 128, 4096, 1) == 0
     assert lib.attn_decode_workspace_size(32, 32, 8, 128, 4096, 3) == 3 * 32 * 32 * 130 * 4
+    # one sequence: about four blocks per CU, at least 256 keys per split
+    s = lib.attn_decode_default_splits(1, 32, 8, 4096)
+    assert s == 16
+    assert lib.attn_decode_workspace_size(1, 32, 8, 128, 4096, 0) == s * 32 * 130 * 4
+    assert lib.attn_decode_default_splits(1, 32, 8, 100000) == 128
     assert lib.attn_decode_workspace_size(0, 32, 8, 128, 4096, 0) == 0
     assert _decode(lib, batch=0) == A.ATTN_OK

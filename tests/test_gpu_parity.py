@@ -267,7 +267,7 @@ def test_decode_split_counts(splits):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (32, 8), (64, 4), (12, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (64, 4), (12, 2)])
 def test_decode_shapes(dtype, d, hq, hkv):
     require_gpu()
     w = synthetic.Workload("d", "decode", dtype, 3, hq, hkv, 333, d, d // 2, 1e4, 41)
@@ -276,6 +276,42 @@ def test_decode_shapes(dtype, d, hq, hkv):
     pos = np.array([333, 100, 7], dtype=np.int32)
     got = _run_decode(w, inp, lens, pos)
     assert_close(got, _oracle_decode(w, inp, lens, pos), dtype, "decode")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_ignores_rows_past_len(dtype):
+    """Cache rows at or past lens[b] hold NaN: nothing of them may reach the output
+    (ragged lengths, so the last chunk of a split is partly past the end)."""
+    require_gpu()
+    w = synthetic.Workload("g", "decode", dtype, 4, 16, 4, 700, 128, 64, 1e4, 47)
+    inp = _decode_inputs(w)
+    lens = np.array([700, 1, 333, 517], dtype=np.int32)
+    pos = lens.copy()
+    for b, n in enumerate(lens):
+        inp["k_cache"][b, n:] = np.nan
+        inp["v"][b, n:] = np.nan
+    for splits in (0, 1, 5):
+        got = _run_decode(w, inp, lens, pos, splits=splits, max_len=700)
+        assert np.isfinite(got).all()
+        assert_close(got, _oracle_decode(w, inp, lens, pos), dtype, "splits=%d" % splits)
+
+
+def test_decode_softmax_max_stress():
+    """A few cached keys scaled by 8 after HeadPrep dominate the softmax, and the scores
+    of one sequence grow along the cache, so the running max has to move many times."""
+    require_gpu()
+    w = synthetic.Workload("s", "decode", "bf16", 3, 32, 8, 2048, 128, 64, 1e6, 53)
+    inp = _decode_inputs(w)
+    kc = inp["k_cache"].astype(np.float64)
+    rows = np.random.default_rng(5).choice(2048, 12, replace=False)
+    kc[0, rows] *= 8.0
+    kc[1] *= np.linspace(0.1, 4.0, 2048)[:, None, None]
+    inp["k_cache"] = synthetic.bf16_round(kc)
+    lens = np.array([2048, 2048, 1999], dtype=np.int32)
+    pos = lens.copy()
+    for splits in (0, 1, 3):
+        got = _run_decode(w, inp, lens, pos, splits=splits)
+        assert_close(got, _oracle_decode(w, inp, lens, pos), "bf16", "splits=%d" % splits)
 
 
 def test_decode_empty_and_invalid_rows():

@@ -203,12 +203,12 @@ def attn_decode(q, k_cache, v_cache, lens, pos, max_len: int, prep: HeadPrep | N
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     need = decode_workspace_size(B, hq, hkv, D, max_len, splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = prep.struct() if prep is not None else None
     _check(lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), B, hq, hkv, D, cap,
                            _ptr(lens), _ptr(pos), max_len,
                            ctypes.byref(st) if st is not None else None, float(scale), splits,
-                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
                            _dtype_code(q), _stream(stream)))
     return out

@@ -240,12 +240,14 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
     }
     if (batch == 0) return ATTN_OK;
     if (splits == 0) splits = attn::decode_default_splits(batch, hq, hkv, max_len);
-    if (splits * batch >= ((int64_t)1 << 31) || batch >= 65536 || hkv * hq >= 65536)
+    if (splits * batch >= ((int64_t)1 << 31) || splits >= 65536 || batch >= 65536 || hkv * hq >= 65536)
         return fail(ATTN_ERR_ARG, "problem too large for one launch");
     const size_t need = attn::decode_workspace_bytes(batch, hq, d, splits);
-    if (!workspace || workspace_bytes < need)
-        return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
-    if (!aligned16(workspace)) return fail(ATTN_ERR_ARG, "workspace is not 16-byte aligned");
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+        if (!aligned16(workspace)) return fail(ATTN_ERR_ARG, "workspace is not 16-byte aligned");
+    }
     const size_t es = elem_size(dtype);
     const Span so = span(out, batch, hq * d, hq, d, es);
     const Span sw{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};

@@ -12,6 +12,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // 1 / ln 2: scores are kept in base-2 units so the softmax uses exp2.
 constexpr float kLog2e = 1.4426950408889634f;
@@ -51,5 +53,31 @@ __device__ __forceinline__ float max_lanes(float v) {
         v = fmaxf(v, __shfl_xor(v, o, 64));
     return v;
 }
+
+// Buffer descriptor over `bytes` bytes from `base` (raw, untyped; reads past the end
+// return zero).  The arguments must be wave-uniform; readfirstlane keeps it in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const void *base, int64_t bytes) {
+    const int n = bytes > 0 ? (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF) : 0;
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *sbase = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(sbase, (short)0, __builtin_amdgcn_readfirstlane(n), 0x00020000);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane L writes lds + 16 L.
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, void *lds, int voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 16, voffset,
+                                             0, 0, 0);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element i % 4 of
+// the four 4 x 16-bit vectors addressed by lanes 4 r + i / 4, r = 0..3 (in order r).
+__device__ __forceinline__ i16x4 lds_read_tr16(const void *lds) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(lds));
+}
+
+// Wait until at most n vector-memory loads of this wave are outstanding (vmcnt only).
+#define ATTN_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 
 }  // namespace attn

@@ -7,19 +7,27 @@
 //
 // Split-KV: a block owns one (sequence, kv head, group of up to 8 q heads, key split).
 // The q heads of one kv head share every K/V read.  Its 4 waves take interleaved
-// chunks of 16 keys and each keeps an online softmax (running max m, sum l, output
-// a, rescaled by 2^(m_old - m_new) when m moves; scores are in base-2 units).
-//   - Q K^T runs on the matrix cores with the chunk's keys as the 16 rows of A and
-//     the (up to 8) prepped q heads as columns of B: v_mfma_f32_16x16x32_bf16 for
-//     bf16 caches, v_mfma_f32_16x16x4f32 for f32 caches.  Each lane loads 16 bytes of
-//     one key row straight into its A fragment.
-//   - P V runs on the vector ALUs: d/8 (bf16) lanes share one value row, each lane
-//     holding 8 of its values, and the chunk's weights come through LDS.
-// The waves' states are merged in LDS and the block writes one partial (m, l, a[d])
-// per q head to the workspace; a second kernel merges the splits (the same rescale
-// applied across splits) and divides by l.
-#include <type_traits>
-
+// chunks of 16 keys and each keeps an online softmax in base-2 units (running max m,
+// sum l, output a).  The waves' states are merged in LDS and the block writes one
+// partial (m, l, a[d]) per q head to the workspace; a second kernel merges the splits
+// (the same rescale applied across splits) and divides by l.
+//
+// bf16 caches (decode_bf16_kernel): both products on the matrix cores.
+//   - every load instruction reads whole cache rows of the kv head (4 rows of 256 bytes
+//     for d = 128); a wave stores its chunk's 16 K rows and 16 V rows to swizzled LDS
+//     buffers and reads them back in the layouts the matrix cores take.
+//   - S^T = K Q^T with v_mfma_f32_16x16x32_bf16: the chunk's 16 keys are the rows of A,
+//     the q heads the columns of B, once as bf16 and once as the bf16 remainder of the
+//     prepped f32 q.  Lane (head n, kk) ends up with keys 4kk .. 4kk+3 of head n.
+//   - O^T += V^T P^T with v_mfma_f32_16x16x16_bf16: those four probabilities, rounded to
+//     bf16, are exactly the lane's B fragment; V^T fragments come from transposing LDS
+//     reads (ds_read_b64_tr_b16).  No probability or value passes through the vector
+//     ALUs.
+//   - the running max only moves when a score exceeds it by more than 2^8 (a
+//     wave-uniform branch); otherwise a chunk costs 4 exponentials per lane.
+//   - the loads of chunk j+1 are in flight while chunk j is computed.
+// f32 caches (decode_f32_kernel): S^T on v_mfma_f32_16x16x4f32, P V on the vector ALUs
+// (D/4 lanes share one value row) with the chunk's weights passed through LDS.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,11 +36,15 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kChunk = 16;       // keys per wave step (the 16 rows of one MFMA)
+constexpr int kChunk = 16;            // keys per wave step (the 16 rows of one MFMA)
+constexpr float kRaiseAbove = 8.0f;   // base-2 headroom before the running max moves
+constexpr int64_t kCUs = 256;         // compute units of one MI355X
 
 struct DecodeParams {
     const void *q; const void *k; const void *v;
     float *work;
+    void *out;                  // written directly when there is a single split
+    bool direct, check_pos;
     int64_t batch, hq, hkv, capacity, max_len, per_split, splits;
     const int32_t *lens, *pos;
     const float *qw, *cos, *sin;
@@ -41,36 +53,27 @@ struct DecodeParams {
     bool prep_q;
 };
 
+// Block coordinates: the kv-head groups of one (sequence, split) are consecutive block
+// ids, so the blocks reading the same cache rows are dealt to different XCDs together.
+struct BlockCoord {
+    int split, kvh, grp, b;
+};
+__device__ __forceinline__ BlockCoord block_coord(const DecodeParams &p) {
+    BlockCoord c;
+    c.kvh = blockIdx.x / p.ngroups;
+    c.grp = blockIdx.x % p.ngroups;
+    c.split = blockIdx.y;
+    c.b = blockIdx.z;
+    return c;
+}
+
+// Load the block's q heads, RMS-normalise with qw and turn at table row pos[b] (when
+// prep_q); leaves the prepped rows in qh (f32).  Every thread of the block takes part;
+// `part` is LDS scratch of kThreads / 64 floats.
 template <bool BF16, int D, int GB>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeParams p) {
-    constexpr int ES = BF16 ? 2 : 4;          // bytes per element
-    constexpr int VE = 16 / ES;               // elements per 16-byte load
-    constexpr int LPK = D / VE;               // lanes per value row
-    constexpr int KPI = 64 / LPK;             // value rows per wave load
-    constexpr int KA = BF16 ? 8 : 4;          // A-fragment elements per lane per MFMA row-slot group
-    constexpr int NKC = D / (4 * KA);         // 16-byte K loads per lane per chunk
-
-    __shared__ float qs[GB][D];               // q rows, then normed
-    __shared__ float qh[GB][D];               // prepped q
-    __shared__ float pb[kWaves][kChunk][GB];  // chunk weights
-    __shared__ float ab[kWaves][GB];          // chunk rescale factors
-    __shared__ float wm[kWaves][GB], wl[kWaves][GB];
-    __shared__ float wo[kWaves][GB][D];
-
-    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
-    const int split = blockIdx.x;
-    const int kvh = blockIdx.y / p.ngroups, grp = blockIdx.y % p.ngroups;
-    const int b = blockIdx.z;
-    const int h0 = kvh * p.group + grp * GB;
-    const int nh = min(GB, p.group - grp * GB);
-
-    // Clamp what the device reads; the merge kernel turns bad lens/pos into NaN.
-    int len = p.lens[b];
-    len = len < 0 ? 0 : (len > p.max_len ? (int)p.max_len : len);
-    const int start = split * (int)p.per_split;
-    const int end = min(len, start + (int)p.per_split);
-
-    // ---- q prologue (through LDS, any half).
+__device__ void q_prologue(const DecodeParams &p, int b, int h0, int nh, float (*qs)[D], float (*qh)[D],
+                           float *part) {
+    const int tid = threadIdx.x, w = tid / 64;
     for (int idx = tid; idx < GB * D; idx += kThreads) {
         const int i = idx / D, e = idx % D;
         float x = 0.f;
@@ -92,9 +95,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
             for (int e = li * EPL; e < li * EPL + EPL; ++e) ss += qs[i][e] * qs[i][e];
         ss = sum_lanes<(LPH < 64 ? LPH : 64)>(ss);
         __syncthreads();
-        if (LPH > 64) {   // reduce across the waves of one head
-            __shared__ float part[kThreads / 64];
-            if (lane == 0) part[w] = ss;
+        if (LPH > 64) {   // reduce across the waves of one head (part: kThreads / 64 floats)
+            if (tid % 64 == 0) part[w] = ss;
             __syncthreads();
             ss = 0.f;
             for (int j = 0; j < LPH / 64; ++j) ss += part[(i * LPH) / 64 + j];
@@ -122,35 +124,308 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
         for (int idx = tid; idx < GB * D; idx += kThreads) qh[idx / D][idx % D] = qs[idx / D][idx % D];
     }
     __syncthreads();
+}
 
-    // ---- B fragments: lane (n = lane % 16 head, kk = lane / 16).
-    const int n = lane % 16, kk = lane / 16;
-    typedef typename std::conditional<BF16, bf16x8, float>::type BFrag;
-    BFrag qb[BF16 ? D / 32 : D / 4];
-    if constexpr (BF16) {
+// Merge the waves' states (wm, wl, wo in LDS, written before a block barrier).  With
+// several splits, write the block's partial (a[d], m, l) of each of its q heads to the
+// workspace; with one split, write the output rows themselves (a / l, zeros for an
+// empty row, NaN for a row with invalid lens or pos).
+template <bool BF16, int D, int GB>
+__device__ void write_partial(const DecodeParams &p, int split, int b, int h0, int nh, const float (*wm)[GB],
+                              const float (*wl)[GB], const float (*wo)[GB][D]) {
+    const int64_t stride = (int64_t)D + 2;
+    bool bad = false;
+    if (p.direct) {
+        const int len = p.lens[b];
+        bad = len < 0 || len > p.max_len;
+        if (p.check_pos) {
+            const int pr = p.pos[b];
+            bad = bad || pr < 0 || pr >= p.table_rows;
+        }
+    }
+    for (int idx = threadIdx.x; idx < nh * D; idx += kThreads) {
+        const int i = idx / D, e = idx % D;
+        float M = -INFINITY;
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) {
-            uint4 u = make_uint4(0, 0, 0, 0);
+        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, wm[ww][i]);
+        float L = 0.f, A = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) {
+                const float f = fast_exp2(wm[ww][i] - M);
+                L += wl[ww][i] * f;
+                A += wo[ww][i][e] * f;
+            }
+        }
+        const int64_t row = (int64_t)b * p.hq + h0 + i;
+        if (p.direct) {
+            float y = L > 0.f ? A / L : 0.f;
+            if (bad) y = __builtin_nanf("");
+            if constexpr (BF16) {
+                f32x2 v2 = {y, 0.f};
+                bf16x2 hv = __builtin_convertvector(v2, bf16x2);
+                static_cast<uint16_t *>(p.out)[row * D + e] = (uint16_t)(__builtin_bit_cast(uint32_t, hv) & 0xFFFFu);
+            } else {
+                static_cast<float *>(p.out)[row * D + e] = y;
+            }
+        } else {
+            float *dst = p.work + ((int64_t)split * p.batch * p.hq + row) * stride;
+            dst[e] = A;
+            if (e == 0) {
+                dst[D] = M;
+                dst[D + 1] = L;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// bf16 caches.
+
+template <int D>
+struct DecGeo {
+    static constexpr int kRow = 2 * D;               // bytes of one cache row of one kv head
+    static constexpr int kCpr = kRow / 16;           // 16-byte chunks per row
+    static constexpr int kRpi = 64 / kCpr;           // rows per 64-lane load
+    static constexpr int kLoads = kChunk / kRpi;     // 16-byte loads per lane per chunk, each of K and V
+    static constexpr int kKMfma = D / 32;            // S^T MFMAs per chunk (per q part)
+    static constexpr int kNT = D / 16;               // 16-row d tiles of O^T
+    static constexpr int kBuf = kChunk * kRow;       // LDS bytes of one chunk of K (or of V)
+};
+
+// LDS slot of 16-byte chunk c of row `row` (0..15) of a K or V chunk.  The swizzles make
+// the reads conflict-free: the K fragment reads of 16 lanes (16 rows, one chunk each)
+// and the transposing V reads of 32 lanes (8 rows x 32 bytes) touch 64 distinct banks.
+template <int D>
+__device__ __forceinline__ int kslot(int row, int c) {
+    return c ^ (D == 128 ? row : row >> 1);
+}
+template <int D>
+__device__ __forceinline__ int vslot(int row, int c) {
+    return c ^ (D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3));
+}
+
+template <int D, int GB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 4 ? 4 : 3))) void decode_bf16_kernel(const DecodeParams p) {
+    typedef DecGeo<D> G;
+    constexpr int kTiles = kWaves * 2 * G::kBuf;               // K and V chunk of every wave
+    constexpr int kQBytes = 2 * GB * D * 4 + 4 * (kThreads / 64);
+    constexpr int kOBytes = kWaves * GB * D * 4 + 2 * kWaves * GB * 4;
+    static_assert(kQBytes <= kTiles && kOBytes <= kTiles, "prologue and merge fit the tile region");
+    constexpr int kQFrag = 2 * G::kKMfma * 64 * 16;            // B fragments of S^T, read every chunk
+    // One LDS region, reused: q rows (prologue), then one K and one V chunk per wave,
+    // then the waves' outputs (after a block barrier); the q fragments follow it.
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kTiles + kQFrag];
+
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+    const BlockCoord bc = block_coord(p);
+    const int b = bc.b, split = bc.split;
+    const int h0 = bc.kvh * p.group + bc.grp * GB;
+    const int nh = min(GB, p.group - bc.grp * GB);
+
+    // Clamp what the device reads; the merge kernel turns bad lens/pos into NaN.
+    int len = p.lens[b];
+    len = len < 0 ? 0 : (len > p.max_len ? (int)p.max_len : len);
+    const int start = split * (int)p.per_split;
+    const int end = min(len, start + (int)p.per_split);
+
+    float (*qs)[D] = reinterpret_cast<float (*)[D]>(smem);
+    float (*qh)[D] = reinterpret_cast<float (*)[D]>(smem + GB * D * 4);
+    q_prologue<true, D, GB>(p, b, h0, nh, qs, qh, reinterpret_cast<float *>(smem + 2 * GB * D * 4));
+
+    // B fragments of S^T: lane (head n, kk) holds q[n][32c + 8kk .. +7], split into a
+    // bf16 high part and a bf16 remainder (q - high) so the scores carry q to about 16
+    // bits rather than 8 (the matrix cores are idle enough to take both).  They are kept
+    // in LDS (lane-linear, so reads are conflict-free) rather than in 32 VGPRs.
+    const int n = lane % 16, kk = lane / 16;
+    u32x4 *qf = reinterpret_cast<u32x4 *>(smem + kTiles);
+    if (w == 0) {
+#pragma unroll
+        for (int c = 0; c < G::kKMfma; ++c) {
+            u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
             if (n < nh) {
                 const float *src = &qh[n][32 * c + 8 * kk];
-                u.x = pack_bf16x2(src[0], src[1]);
-                u.y = pack_bf16x2(src[2], src[3]);
-                u.z = pack_bf16x2(src[4], src[5]);
-                u.w = pack_bf16x2(src[6], src[7]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float a = src[2 * e], b2 = src[2 * e + 1];
+                    hi[e] = pack_bf16x2(a, b2);
+                    float ha, hb;
+                    unpack_bf16x2(hi[e], ha, hb);
+                    lo[e] = pack_bf16x2(a - ha, b2 - hb);
+                }
             }
-            qb[c] = __builtin_bit_cast(bf16x8, u);
+            qf[64 * (2 * c) + lane] = hi;
+            qf[64 * (2 * c + 1) + lane] = lo;
         }
-    } else {
-        // MFMA 4c + j takes d = 16c + 4kk + j (the order of a lane's 16-byte K load).
+    }
+    __syncthreads();     // q rows are dead: the LDS now holds K and V chunks
+
+    const int64_t rowb = p.hkv * D * 2;       // bytes between consecutive cache rows
+    const uint8_t *kbase = static_cast<const uint8_t *>(p.k) + ((int64_t)b * p.capacity * p.hkv + bc.kvh) * D * 2;
+    const uint8_t *vbase = static_cast<const uint8_t *>(p.v) + ((int64_t)b * p.capacity * p.hkv + bc.kvh) * D * 2;
+    unsigned char *kbuf = smem + w * 2 * G::kBuf;    // this wave's K chunk
+    unsigned char *vbuf = kbuf + G::kBuf;            // and V chunk
+
+    // Load i of a chunk: lane L reads 16 bytes (chunk L % kCpr) of row kRpi i + L / kCpr,
+    // kRpi whole rows per instruction.  The row offset stays in the VGPR offset (the part
+    // the descriptor's range check covers); each load has its own descriptor.
+    const int lrow = lane / G::kCpr, lchunk = lane % G::kCpr;
+    const int loff = lrow * (int)rowb + 16 * lchunk;
+
+    f32x4 acc[G::kNT];
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c)
+    for (int t = 0; t < G::kNT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, thr = -INFINITY, l_lane = 0.f;
+
+    // This wave's chunks: keys start + 16 (w + 4 j) .. +15, j < nch.
+    const int first = start + kChunk * w;
+    const int nch = end > first ? (end - first + kChunk * kWaves - 1) / (kChunk * kWaves) : 0;
+
+    struct Regs {
+        u32x4 k[G::kLoads];
+        u32x4 v[G::kLoads];
+    };
+    // Chunk j's rows, read through descriptors that end at the cache's last valid row
+    // (rows past it, and every row of a chunk past the end, read as zero without a fetch).
+    auto issue = [&](int j, Regs &r) {
+        const int key0 = first + kChunk * kWaves * j;
+        const int64_t bytes = (int64_t)min(kChunk, end - key0) * rowb;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) qb[4 * c + j] = n < nh ? qh[n][16 * c + 4 * kk + j] : 0.f;
+        for (int i = 0; i < G::kLoads; ++i) {
+            const int64_t skip = (int64_t)(G::kRpi * i) * rowb;
+            r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(seq_rsrc(kbase + key0 * rowb + skip, bytes - skip), loff, 0, 0);
+            r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(seq_rsrc(vbase + key0 * rowb + skip, bytes - skip), loff, 0, 0);
+        }
+    };
+
+    // A wave's LDS operations run in order, so chunk j+1's stores cannot overtake
+    // chunk j's reads of the same buffers.
+    auto compute = [&](int j, const Regs &r) {
+        const int key0 = first + kChunk * kWaves * j;
+#pragma unroll
+        for (int i = 0; i < G::kLoads; ++i) {
+            const int row = G::kRpi * i + lrow;
+            *reinterpret_cast<u32x4 *>(kbuf + row * G::kRow + 16 * kslot<D>(row, lchunk)) = r.k[i];
+            *reinterpret_cast<u32x4 *>(vbuf + row * G::kRow + 16 * vslot<D>(row, lchunk)) = r.v[i];
+        }
+        // S^T: lane (key n, kk) takes chunk 4c + kk of its key row for MFMA c.
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < G::kKMfma; ++c) {
+            const bf16x8 kc = *reinterpret_cast<const bf16x8 *>(kbuf + n * G::kRow + 16 * kslot<D>(n, 4 * c + kk));
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, __builtin_bit_cast(bf16x8, qf[64 * (2 * c) + lane]), s, 0, 0, 0);
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, __builtin_bit_cast(bf16x8, qf[64 * (2 * c + 1) + lane]), s, 0, 0, 0);
+        }
+        if (key0 + kChunk > end) {            // ragged last chunk (wave-uniform)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (key0 + 4 * kk + i >= end) s[i] = -INFINITY;
+        }
+        const float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {
+            // Raise the running max of every head to its max so far.
+            float mh = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mh = fmaxf(mh, __shfl_xor(mh, 32, 64));
+            const float m_new = fmaxf(m_run, mh * p.C);
+            const float alpha = fast_exp2(m_run - m_new);
+            l_lane *= alpha;
+#pragma unroll
+            for (int t = 0; t < G::kNT; ++t) acc[t] *= alpha;
+            m_run = m_new;
+            thr = (m_run + kRaiseAbove) / p.C;
+        }
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(s[i], p.C, -m_run));
+        l_lane += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
+        const i16x4 pf = __builtin_bit_cast(i16x4, make_uint2(p01, p23));
+        // O^T: for d tile t, lane 16g + 4r + q addresses V[4g + r][16t + 4q .. +3].
+        const int vkey = 4 * kk + (lane % 16) / 4, q = lane % 4;
+#pragma unroll
+        for (int t = 0; t < G::kNT; ++t) {
+            const i16x4 a = lds_read_tr16(vbuf + vkey * G::kRow + 16 * vslot<D>(vkey, 2 * t + q / 2) + 8 * (q % 2));
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pf, acc[t], 0, 0, 0);
+        }
+    };
+
+    // Two chunks per iteration so the register buffers alternate statically;
+    // chunk j+1 is in flight while chunk j is computed.  The chunk after the last one
+    // is issued with empty descriptors (nothing fetched), which keeps the loop free of
+    // branches around the loads.
+    Regs ra, rb;
+    issue(0, ra);
+    for (int j = 0; j < nch; j += 2) {
+        issue(j + 1, rb);
+        compute(j, ra);
+        if (j + 1 >= nch) break;
+        issue(j + 2, ra);
+        compute(j + 1, rb);
     }
 
-    const uint8_t *kbase = static_cast<const uint8_t *>(p.k) + (((int64_t)b * p.capacity) * p.hkv + kvh) * D * ES;
-    const uint8_t *vbase = static_cast<const uint8_t *>(p.v) + (((int64_t)b * p.capacity) * p.hkv + kvh) * D * ES;
-    const int64_t rowb = p.hkv * D * ES;      // bytes between consecutive cache rows
+    // ---- merge: the lanes of one head (kk), then the waves.
+    float l_head = l_lane + __shfl_xor(l_lane, 16, 64);
+    l_head += __shfl_xor(l_head, 32, 64);
+    __syncthreads();                          // every wave is done with its chunk buffers
+    float (*wo)[GB][D] = reinterpret_cast<float (*)[GB][D]>(smem);
+    float (*wm)[GB] = reinterpret_cast<float (*)[GB]>(smem + kWaves * GB * D * 4);
+    float (*wl)[GB] = reinterpret_cast<float (*)[GB]>(smem + kWaves * GB * D * 4 + kWaves * GB * 4);
+    if (n < GB) {
+#pragma unroll
+        for (int t = 0; t < G::kNT; ++t) *reinterpret_cast<f32x4 *>(&wo[w][n][16 * t + 4 * kk]) = acc[t];
+        if (kk == 0) {
+            wm[w][n] = m_run;
+            wl[w][n] = l_head;
+        }
+    }
+    __syncthreads();
+    write_partial<true, D, GB>(p, split, b, h0, nh, wm, wl, wo);
+}
+
+// ---------------------------------------------------------------------------------
+// f32 caches.
+
+template <int D, int GB>
+__global__ __launch_bounds__(kThreads) void decode_f32_kernel(const DecodeParams p) {
+    constexpr int VE = 4;                     // elements per 16-byte load
+    constexpr int LPK = D / VE;               // lanes per value row
+    constexpr int KPI = 64 / LPK;             // value rows per wave load
+    constexpr int NKC = D / 16;               // 16-byte K loads per lane per chunk
+
+    __shared__ float qs[GB][D];
+    __shared__ float qh[GB][D];
+    __shared__ float pb[kWaves][kChunk][GB];  // chunk weights
+    __shared__ float ab[kWaves][GB];          // chunk rescale factors
+    __shared__ float wm[kWaves][GB], wl[kWaves][GB];
+    __shared__ float wo[kWaves][GB][D];
+
+    const int tid = threadIdx.x, w = tid / 64, lane = tid % 64;
+    const BlockCoord bc = block_coord(p);
+    const int b = bc.b, split = bc.split;
+    const int h0 = bc.kvh * p.group + bc.grp * GB;
+    const int nh = min(GB, p.group - bc.grp * GB);
+
+    int len = p.lens[b];
+    len = len < 0 ? 0 : (len > p.max_len ? (int)p.max_len : len);
+    const int start = split * (int)p.per_split;
+    const int end = min(len, start + (int)p.per_split);
+
+    __shared__ float part[kThreads / 64];
+    q_prologue<false, D, GB>(p, b, h0, nh, qs, qh, part);
+
+    // B fragments: lane (n = lane % 16 head, kk = lane / 16); MFMA 4c + j takes
+    // d = 16c + 4kk + j (the order of a lane's 16-byte K load).
+    const int n = lane % 16, kk = lane / 16;
+    float qb[D / 4];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qb[4 * c + j] = n < nh ? qh[n][16 * c + 4 * kk + j] : 0.f;
+
+    const uint8_t *kbase = static_cast<const uint8_t *>(p.k) + ((int64_t)b * p.capacity * p.hkv + bc.kvh) * D * 4;
+    const uint8_t *vbase = static_cast<const uint8_t *>(p.v) + ((int64_t)b * p.capacity * p.hkv + bc.kvh) * D * 4;
+    const int64_t rowb = p.hkv * D * 4;
 
     float m_run = -INFINITY, l_run = 0.f;     // state of head n (replicated over kk)
     const int kq = lane / LPK, dseg = lane % LPK;
@@ -161,15 +436,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
         for (int e = 0; e < VE; ++e) o[i][e] = 0.f;
 
     for (int key0 = start + kChunk * w; key0 < end; key0 += kChunk * kWaves) {
-        // K rows -> A fragments; V rows -> registers.
         uint4 kr[NKC];
         const int kj = key0 + (lane % 16);
 #pragma unroll
-        for (int c = 0; c < NKC; ++c) {
-            // bf16: d = 32c + 8kk; f32: d = 16c + 4kk (16 bytes each)
-            const int d0 = BF16 ? 32 * c + 8 * kk : 16 * c + 4 * kk;
-            kr[c] = kj < end ? *reinterpret_cast<const uint4 *>(kbase + kj * rowb + d0 * ES) : make_uint4(0, 0, 0, 0);
-        }
+        for (int c = 0; c < NKC; ++c)
+            kr[c] = kj < end ? *reinterpret_cast<const uint4 *>(kbase + kj * rowb + (16 * c + 4 * kk) * 4)
+                             : make_uint4(0, 0, 0, 0);
         uint4 vr[kChunk / KPI];
 #pragma unroll
         for (int i = 0; i < kChunk / KPI; ++i) {
@@ -178,19 +450,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
         }
 
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (BF16) {
 #pragma unroll
-            for (int c = 0; c < NKC; ++c)
-                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[c]), qb[c], s, 0, 0, 0);
-        } else {
+        for (int c = 0; c < NKC; ++c) {
+            const float kv[4] = {__uint_as_float(kr[c].x), __uint_as_float(kr[c].y),
+                                 __uint_as_float(kr[c].z), __uint_as_float(kr[c].w)};
 #pragma unroll
-            for (int c = 0; c < NKC; ++c) {
-                const float kv[4] = {__uint_as_float(kr[c].x), __uint_as_float(kr[c].y),
-                                     __uint_as_float(kr[c].z), __uint_as_float(kr[c].w)};
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    s = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[j], qb[4 * c + j], s, 0, 0, 0);
-            }
+            for (int j = 0; j < 4; ++j) s = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[j], qb[4 * c + j], s, 0, 0, 0);
         }
         // lane (n, kk) holds keys key0 + 4kk + i, i < 4, for head n.
         float mx = -INFINITY;
@@ -231,16 +496,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
             for (int e = 0; e < VE; ++e) o[i][e] *= al[i];
 #pragma unroll
         for (int r = 0; r < kChunk / KPI; ++r) {
-            float vv[VE];
-            if constexpr (BF16) {
-                unpack_bf16x2(vr[r].x, vv[0], vv[1]);
-                unpack_bf16x2(vr[r].y, vv[2], vv[3]);
-                unpack_bf16x2(vr[r].z, vv[4], vv[5]);
-                unpack_bf16x2(vr[r].w, vv[6], vv[7]);
-            } else {
-                vv[0] = __uint_as_float(vr[r].x); vv[1] = __uint_as_float(vr[r].y);
-                vv[2] = __uint_as_float(vr[r].z); vv[3] = __uint_as_float(vr[r].w);
-            }
+            const float vv[VE] = {__uint_as_float(vr[r].x), __uint_as_float(vr[r].y), __uint_as_float(vr[r].z),
+                                  __uint_as_float(vr[r].w)};
             const int key = KPI * r + kq;
 #pragma unroll
             for (int i = 0; i < GB; ++i) {
@@ -272,28 +529,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodePara
         wl[w][n] = l_run;
     }
     __syncthreads();
-    const int64_t stride = (int64_t)D + 2;
-    for (int idx = tid; idx < nh * D; idx += kThreads) {
-        const int i = idx / D, e = idx % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, wm[ww][i]);
-        float L = 0.f, A = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww) {
-                const float f = fast_exp2(wm[ww][i] - M);
-                L += wl[ww][i] * f;
-                A += wo[ww][i][e] * f;
-            }
-        }
-        float *dst = p.work + ((int64_t)split * p.batch * p.hq + (int64_t)b * p.hq + h0 + i) * stride;
-        dst[e] = A;
-        if (e == 0) {
-            dst[D] = M;
-            dst[D + 1] = L;
-        }
-    }
+    write_partial<false, D, GB>(p, split, b, h0, nh, wm, wl, wo);
 }
 
 // Merge the splits of one (sequence, q head) and write the output row.
@@ -336,8 +572,11 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float *work, void
 
 template <bool BF16, int D, int GB>
 void launch_split(const DecodeParams &p, hipStream_t stream) {
-    const dim3 grid((unsigned)p.splits, (unsigned)(p.hkv * p.ngroups), (unsigned)p.batch);
-    hipLaunchKernelGGL((decode_split_kernel<BF16, D, GB>), grid, dim3(kThreads), 0, stream, p);
+    const dim3 grid((unsigned)(p.hkv * p.ngroups), (unsigned)p.splits, (unsigned)p.batch);
+    if constexpr (BF16)
+        hipLaunchKernelGGL((decode_bf16_kernel<D, GB>), grid, dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_f32_kernel<D, GB>), grid, dim3(kThreads), 0, stream, p);
 }
 
 template <bool BF16, int D>
@@ -363,7 +602,8 @@ int64_t decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t ma
     const int64_t gb = decode_heads_per_block(hq, hkv);
     const int64_t groups = (hq / hkv + gb - 1) / gb;
     const int64_t units = batch * hkv * groups;
-    int64_t splits = (1024 + units - 1) / units;                   // about 4 blocks per CU
+    if (units >= kCUs) return 1;                                   // a block per CU already
+    int64_t splits = (4 * kCUs + units - 1) / units;               // about 4 blocks per CU
     const int64_t most = (max_len + 255) / 256;                    // at least 256 keys each
     if (splits > most) splits = most;
     if (splits < 1) splits = 1;
@@ -371,12 +611,15 @@ int64_t decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t ma
 }
 
 size_t decode_workspace_bytes(int64_t batch, int64_t hq, int64_t d, int64_t splits) {
+    if (splits <= 1) return 0;                                     // one split writes the output
     return (size_t)splits * (size_t)batch * (size_t)hq * (size_t)(d + 2) * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream) {
     DecodeParams p;
-    p.q = a.q; p.k = a.k; p.v = a.v; p.work = a.work;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.work = a.work; p.out = a.out;
+    p.direct = a.splits == 1;
+    p.check_pos = a.prep_q && a.half > 0;
     p.batch = a.batch; p.hq = a.hq; p.hkv = a.hkv; p.capacity = a.capacity; p.max_len = a.max_len;
     p.splits = a.splits;
     const int64_t per = (a.max_len + a.splits - 1) / a.splits;
@@ -397,8 +640,8 @@ hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream) {
         if (a.bf16) launch_split_gb<true, 128>(p, gb, stream); else launch_split_gb<false, 128>(p, gb, stream);
     }
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const bool check_pos = a.prep_q && a.half > 0;
+    if (err != hipSuccess || p.direct) return err;
+    const bool check_pos = p.check_pos;
     const dim3 grid((unsigned)(a.batch * a.hq));
     if (a.d == 64) {
         if (a.bf16)

@@ -69,15 +69,7 @@ constexpr int kBN = 64;            // keys per tile
 constexpr int kXcds = 8;
 constexpr float kRaiseAbove = 8.0f;   // base-2 headroom before the running max moves
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
 extern __shared__ __attribute__((aligned(16))) unsigned char prefill_smem[];
-
-// 16 bytes per lane from a buffer straight into LDS: lane L writes lds + 16 L.
-__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, void *lds, int voffset) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 16, voffset,
-                                             0, 0, 0);
-}
 
 // The value held by lane ^ 32 (v_permlane32_swap: no LDS round trip).
 __device__ __forceinline__ float lane_pair(float x, int g) {
@@ -126,17 +118,6 @@ struct Geo {
     static constexpr int kPerWave = (kVLoads + 1) / 2;   // waves 0,1 load K; 2,3 load V
     static_assert(kBN * kKSlots % 64 == 0 && kBN * kVSlots % 64 == 0, "whole 64-lane loads");
 };
-
-// Buffer descriptor over `bytes` bytes from `base` (raw, untyped; reads past the end
-// return zero).  The arguments are block-uniform; readfirstlane keeps it in SGPRs.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const uint16_t *base, int64_t bytes) {
-    const int n = bytes > 0 ? (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF) : 0;
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    void *sbase = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(sbase, (short)0, __builtin_amdgcn_readfirstlane(n), 0x00020000);
-}
 
 template <int D, bool CAUSAL, bool PREP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(const PrefillLaunch p) {

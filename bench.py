@@ -11,14 +11,24 @@ at position 4096.  Inputs are seeded synthetic N(0, 1) operands (synthetic.py) a
 resident in HBM; the decode step rotates through several cache copies so repeats are
 not served from the 256 MB last-level cache.
 
+After the timed steps: the long prefill workload (batch 1 x 16384 tokens, 64 q / 8 kv
+heads, rotary base 1e6, 1 % outlier key rows), k HeadPrep + attention per call; then two
+calibration kernels (libpeak.so: a bf16 MFMA loop and a streaming read) give measured
+ceilings next to the published ones.
+
 Printed: one JSON line.  `value` is the prefill rate (algorithmic flops of the visible
-causal pairs, 4 d per (query, key, head), over the time of steps 1-2), the decode rate
-(algorithmic bytes over the time of step 3) is under "decode".  `roofline` is the
-attention kernel's (step 2 alone), with HIP events on the launch stream.
+causal pairs, 4 d per (query, key, head), over the mean time of steps 1-2); the decode
+rate (algorithmic bytes over the mean time of step 3) is under "decode".  `roofline` is
+the attention kernel's (step 2 alone), `decode_roofline` the decode call's, both timed
+with HIP events on the launch stream.  `traffic` is the HBM bytes per launch read from
+profiles/traffic.json (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a plain copy), or
+null when the kernel sources changed since those counters were taken.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import os
 import platform
@@ -28,8 +38,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E (published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def prefill_flops(w) -> int:
@@ -41,6 +52,26 @@ def decode_bytes(w) -> int:
     kv = 2 * w.batch * w.seq * w.hkv * w.d * 2
     qo = 2 * w.batch * w.hq * w.d * 2
     return kv + qo + 2 * w.half * 4 + w.d * 4     # + one cos/sin table row + qw
+
+
+def sources_sha(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter run, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if sources_sha(rec["sources"]) != rec["sources_sha256"]:
+        return None
+    return rec["bytes_per_launch"]
 
 
 def cpu_baseline(w, inp) -> dict:
@@ -58,13 +89,58 @@ def cpu_baseline(w, inp) -> dict:
             "host_cpu": platform.processor() or platform.machine()}
 
 
+def stats_ms(a) -> dict:
+    import numpy as np
+    a = np.asarray(a)
+    return {"mean": round(float(a.mean()), 5), "median": round(float(np.median(a)), 5),
+            "min": round(float(a.min()), 5)}
+
+
+def measured_peaks(torch, dev) -> dict:
+    """Best of a few runs of the two calibration kernels."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "transformer_attention_headprep_amd", "libpeak.so"))
+    lib.peak_mfma_bf16_flops.restype = ctypes.c_double
+    lib.peak_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    sink = torch.zeros(4, dtype=torch.float32, device=dev)
+
+    def best(launch, reps=5):
+        launch()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        return min(times)
+
+    blocks, iters = 512, 4000                  # 2 waves per SIMD on 256 CUs
+    t = best(lambda: lib.peak_mfma_bf16(blocks, iters, ctypes.c_void_p(sink.data_ptr()), sp))
+    mfma = lib.peak_mfma_bf16_flops(blocks, iters) / t / 1e12
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    t = best(lambda: lib.peak_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), sp))
+    del buf
+    return {"mfma_bf16_tflops": round(mfma, 1), "hbm_read_gbps": round(nbytes / t / 1e9, 1),
+            "how": "libpeak.so: %d blocks x 4 waves x %d rounds of 8 independent "
+                   "v_mfma_f32_32x32x16_bf16; a grid-stride 16-byte read of 1 GiB; best of 5" % (blocks, iters)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cache-copies", type=int, default=3)
+    ap.add_argument("--long-calls", type=int, default=20, help="timed calls of the long prefill (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the calibration kernels")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 times), to scale HBM "
                          "byte counters read by a profiler")
@@ -120,8 +196,8 @@ def main() -> int:
     lens = torch.tensor(idc["lens"], device=dev)
     pos = torch.tensor(idc["pos"], device=dev)
     splits = tah.decode_default_splits(wd.batch, wd.hq, wd.hkv, wd.seq)
-    ws = torch.empty(tah.decode_workspace_size(wd.batch, wd.hq, wd.hkv, wd.d, wd.seq, splits),
-                     dtype=torch.uint8, device=dev)
+    need = tah.decode_workspace_size(wd.batch, wd.hq, wd.hkv, wd.d, wd.seq, splits)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
     out4 = torch.empty_like(q4)
     stream = torch.cuda.current_stream()
 
@@ -158,6 +234,44 @@ def main() -> int:
     pre_tflops = flops / ((prep_ms + attn_ms).mean() * 1e-3) / 1e12
     attn_tflops = flops / (attn_ms.mean() * 1e-3) / 1e12
     dec_gbps = nbytes / (dec_ms.mean() * 1e-3) / 1e9
+    del q3, k3, v3, out3, kcs, vcs, k_raw, v_raw
+
+    # ---- long prefill: k HeadPrep + attention per call
+    long_line = None
+    if args.long_calls > 0:
+        wl = synthetic.WORKLOADS["long_prefill_bf16"]
+        il = synthetic.make_prefill(wl)
+        q5, k5, v5 = to(il["q"]), to(il["k"]), to(il["v"])
+        out5 = torch.empty_like(q5)
+        prep5 = tah.HeadPrep(to(il["qw"], "f32"), to(il["kw"], "f32"), to(il["cos"], "f32"),
+                             to(il["sin"], "f32"), wl.eps)
+        prep5_q = tah.HeadPrep(prep5.qw, None, prep5.cos, prep5.sin, wl.eps)
+
+        def call5():
+            tah.attn_prep(None, k5, prep5, pos0=0, stream=stream)
+            tah.attn_prefill(q5, k5, v5, out5, prep=prep5_q, causal=True, scale=wl.scale, stream=stream)
+
+        for _ in range(3):
+            call5()
+        ev5 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.long_calls)]
+        torch.cuda.synchronize()
+        for a, b in ev5:
+            a.record(stream)
+            call5()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms5 = np.array([a.elapsed_time(b) for a, b in ev5])
+        tf5 = prefill_flops(wl) / (ms5.mean() * 1e-3) / 1e12
+        long_line = {"workload": "bf16 long prefill (batch 1, seq 16384, 64 q / 8 kv heads, d 128, "
+                                 "rotary base 1e6, 1 % outlier key rows), k HeadPrep + attention",
+                     "value": round(tf5, 3), "unit": "TFLOP/s", "calls": args.long_calls,
+                     "ms": stats_ms(ms5), "flops": prefill_flops(wl),
+                     "frac_of_bf16_peak": round(tf5 / PEAK_BF16_TFLOPS, 4)}
+        del q5, k5, v5, out5
+        torch.cuda.empty_cache()
+
+    peaks = None if args.no_peaks else measured_peaks(torch, dev)
 
     line = {
         "metric": "prefill attention TFLOP/s + decode HBM GB/s (HeadPrep fused), 1 MI355X",
@@ -178,20 +292,27 @@ def main() -> int:
             "prefill": {"batch": wp.batch, "seq": wp.seq, "hq": wp.hq, "hkv": wp.hkv, "d": wp.d,
                         "half": wp.half, "rotary_base": wp.base, "causal": True},
             "decode": {"batch": wd.batch, "cache": wd.seq, "query_position": wd.seq, "hq": wd.hq,
-                       "hkv": wd.hkv, "d": wd.d, "splits": splits, "cache_copies": len(kcs)},
+                       "hkv": wd.hkv, "d": wd.d, "splits": splits, "cache_copies": args.cache_copies},
         },
-        "parts_ms": {"k_headprep": round(float(prep_ms.mean()), 5),
-                     "prefill_attention": round(float(attn_ms.mean()), 5),
-                     "decode": round(float(dec_ms.mean()), 5),
-                     "prefill_attention_min": round(float(attn_ms.min()), 5),
-                     "decode_min": round(float(dec_ms.min()), 5)},
+        "parts_ms": {"k_headprep": stats_ms(prep_ms), "prefill_attention": stats_ms(attn_ms),
+                     "decode": stats_ms(dec_ms)},
         "decode": {"value": round(dec_gbps, 2), "unit": "GB/s", "bytes": nbytes,
                    "frac_of_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4)},
         "roofline": {"kernel": "prefill_bf16_kernel (attention, q HeadPrep fused)",
                      "bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "flops_per_launch": flops},
+                     "traffic": recorded_traffic("prefill_bf16_kernel"), "flops_per_launch": flops},
+        "decode_roofline": {"kernel": "decode_bf16_kernel (q HeadPrep fused, one split)",
+                            "bound": "hbm", "achieved": round(dec_gbps, 2), "peak": PEAK_HBM_GBPS,
+                            "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                            "traffic": recorded_traffic("decode_bf16_kernel"), "bytes_per_launch": nbytes},
     }
+    if long_line is not None:
+        line["long_prefill"] = long_line
+    if peaks is not None:
+        peaks["prefill_attention_frac"] = round(attn_tflops / peaks["mfma_bf16_tflops"], 4)
+        peaks["decode_frac"] = round(dec_gbps / peaks["hbm_read_gbps"], 4)
+        line["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wp, ip)
     print(json.dumps(line), flush=True)

@@ -160,3 +160,23 @@ def test_decode_sizes(lib):
     assert lib.attn_decode_default_splits(1, 32, 8, 100000) == 128
     assert lib.attn_decode_workspace_size(0, 32, 8, 128, 4096, 0) == 0
     assert _decode(lib, batch=0) == A.ATTN_OK
+
+
+def test_peak_library_exports_what_peak_h_declares():
+    """libpeak.so (calibration kernels of the benchmark) loads without a GPU and exports
+    every function include/peak.h declares; bad arguments are refused on the host."""
+    src = open(os.path.join(ROOT, "include", "peak.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    declared = sorted(set(re.findall(r"\b(peak_[a-z0-9_]+)\s*\(", src)))
+    assert declared == ["peak_mfma_bf16", "peak_mfma_bf16_flops", "peak_stream_read"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "transformer_attention_headprep_amd", "libpeak.so"))
+    for name in declared:
+        assert hasattr(lib, name), name
+    lib.peak_mfma_bf16_flops.restype = ctypes.c_double
+    lib.peak_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    assert lib.peak_mfma_bf16_flops(2, 3) == 2 * 4 * 3 * 8 * 2 * 32 * 32 * 16
+    lib.peak_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.peak_mfma_bf16(0, 10, FAKE, None) == -1
+    lib.peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.peak_stream_read(FAKE, 1000, FAKE, None) == -1       # not a multiple of 16
+    assert lib.peak_stream_read(FAKE + 8, 1024, FAKE, None) == -1   # misaligned

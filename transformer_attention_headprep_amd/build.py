@@ -1,10 +1,12 @@
-"""Build libattn.so (HIP for gfx950) in-tree with hipcc.
+"""Build libattn.so and libpeak.so (HIP for gfx950) in-tree with hipcc.
 
     python -m transformer_attention_headprep_amd.build
 
 Each source is compiled to an object under ``_build/`` in parallel, then linked into
-``transformer_attention_headprep_amd/libattn.so``.  Device code is built for gfx950
-only, with packed-f32 instructions turned off.
+``transformer_attention_headprep_amd/libattn.so`` (the attention path) and
+``transformer_attention_headprep_amd/libpeak.so`` (calibration kernels for the
+benchmark).  Device code is built for gfx950 only, with packed-f32 instructions turned
+off.
 """
 from __future__ import annotations
 
@@ -18,8 +20,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libattn.so")
+PEAK_OUT = os.path.join(PKG, "libpeak.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["attn_api.cpp", "prep.hip", "prefill_f32.hip", "prefill_bf16.hip", "decode.hip"]
+PEAK_SOURCES = ["peak.hip"]
 # Per-source flags.  The bf16 prefill kernel never sees NaN operands in valid use, so it
 # drops NaN quieting: row maxima become single v_max3 instructions.
 EXTRA = {"prefill_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
@@ -48,17 +52,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    """Compile every source and link libattn.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(SOURCES)))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp%d" % os.getpid()
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(jobs: int = 8) -> str:
+    """Compile every source and link libattn.so and libpeak.so; returns libattn's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PEAK_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], OUT)
+    _link(objs[len(SOURCES):], PEAK_OUT)
     return OUT
 
 

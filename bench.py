@@ -12,7 +12,9 @@ resident in HBM; the decode step rotates through several cache copies so repeats
 not served from the 256 MB last-level cache.
 
 After the timed steps: the long prefill workload (batch 1 x 16384 tokens, 64 q / 8 kv
-heads, rotary base 1e6, 1 % outlier key rows), k HeadPrep + attention per call; then two
+heads, rotary base 1e6, 1 % outlier key rows), k HeadPrep + attention per call; the
+chunked prefill workload (batch 4: 512 new tokens appended to a 3584-row cache, 32 q / 8
+kv heads, attention over all 4096 rows) per attn_prefill_chunk call; then two
 calibration kernels (libpeak.so: a bf16 MFMA loop and a streaming read) give measured
 ceilings next to the published ones.
 
@@ -139,6 +141,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cache-copies", type=int, default=3)
     ap.add_argument("--long-calls", type=int, default=20, help="timed calls of the long prefill (0: skip)")
+    ap.add_argument("--chunk-calls", type=int, default=20, help="timed calls of the chunked prefill (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the calibration kernels")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -146,8 +149,8 @@ def main() -> int:
                          "byte counters read by a profiler")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this path is built and timed on a single MI355X "
-              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: this path is built and timed on a single MI355X; "
+              "run with --gpus 1", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -271,6 +274,46 @@ def main() -> int:
         del q5, k5, v5, out5
         torch.cuda.empty_cache()
 
+    # ---- chunked prefill: append 512 tokens to a 3584-row cache and attend all 4096
+    chunk_line = None
+    if args.chunk_calls > 0:
+        wc = synthetic.WORKLOADS["chunk_prefill_bf16"]
+        n_past, tq = wc.extra["n_past"], wc.extra["tq"]
+        ic = synthetic.make_prefill(wc)
+        prep6 = tah.HeadPrep(to(ic["qw"], "f32"), to(ic["kw"], "f32"), to(ic["cos"], "f32"),
+                             to(ic["sin"], "f32"), wc.eps)
+        kc6, vc6 = to(ic["k"]), to(ic["v"])                  # [4, 4096, 8, 128]: the cache
+        tah.attn_prep(None, kc6, prep6, pos0=0)              # rows 0 .. 3583 hold prepped keys
+        q6 = to(ic["q"][:, n_past:])
+        kn6, vn6 = to(ic["k"][:, n_past:]), to(ic["v"][:, n_past:])
+        out6 = torch.empty_like(q6)
+
+        def call6():
+            tah.attn_prefill_chunk(q6, kn6, vn6, kc6, vc6, n_past, out=out6, prep=prep6, causal=True,
+                                   scale=wc.scale, stream=stream)
+
+        for _ in range(3):
+            call6()
+        ev6 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.chunk_calls)]
+        torch.cuda.synchronize()
+        for a, b in ev6:
+            a.record(stream)
+            call6()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms6 = np.array([a.elapsed_time(b) for a, b in ev6])
+        pairs6 = sum(n_past + i + 1 for i in range(tq))
+        flops6 = 4 * wc.d * pairs6 * wc.batch * wc.hq
+        tf6 = flops6 / (ms6.mean() * 1e-3) / 1e12
+        chunk_line = {"workload": "bf16 chunked prefill (batch 4, 512 new tokens after 3584 cached, 32 q / 8 kv "
+                                  "heads, d 128): k HeadPrep + cache append + attention over 4096 rows",
+                      "value": round(tf6, 3), "unit": "TFLOP/s", "calls": args.chunk_calls,
+                      "ms": stats_ms(ms6), "flops": flops6,
+                      "frac_of_bf16_peak": round(tf6 / PEAK_BF16_TFLOPS, 4)}
+        del q6, kn6, vn6, out6, kc6, vc6
+        torch.cuda.empty_cache()
+
     peaks = None if args.no_peaks else measured_peaks(torch, dev)
 
     line = {
@@ -309,6 +352,8 @@ def main() -> int:
     }
     if long_line is not None:
         line["long_prefill"] = long_line
+    if chunk_line is not None:
+        line["chunk_prefill"] = chunk_line
     if peaks is not None:
         peaks["prefill_attention_frac"] = round(attn_tflops / peaks["mfma_bf16_tflops"], 4)
         peaks["decode_frac"] = round(dec_gbps / peaks["hbm_read_gbps"], 4)

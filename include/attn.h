@@ -118,6 +118,34 @@ attn_status_t attn_prefill(const void *q, void *k, const void *v, void *out,
                            int causal, double scale, attn_dtype_t dtype, void *stream);
 
 /*
+ * attn_prefill_chunk -- a chunk of tq new tokens per sequence against a KV cache that
+ * already holds n_past prepped rows (chunked prefill: gizml:netops, Functions >
+ * attention with tq < tk, whose causal mask is aligned bottom-right), appending the
+ * chunk's keys and values to the cache.  In order, on `stream`:
+ *   1. k_cache[b, n_past + t] = HeadPrep of k_new[b, t] at table row n_past + t with kw
+ *      (prep NULL or prep->kw NULL: k_new holds prepped keys and is copied as it is);
+ *   2. v_cache[b, n_past + t] = v_new[b, t];
+ *   3. out[b, i] = attention of q[b, i] (its HeadPrep at table row n_past + i when prep
+ *      is given) over cache rows 0 .. n_past + tq - 1; with causal != 0, query i sees
+ *      rows j <= n_past + i.
+ *   q            [batch, tq, hq, d] contiguous, read only
+ *   k_new, v_new [batch, tq, hkv, d] contiguous, read only
+ *   k_cache, v_cache [batch, capacity, hkv, d] contiguous; rows 0 .. n_past - 1 must
+ *                hold the earlier tokens (keys prepped); rows n_past .. n_past + tq - 1
+ *                are overwritten; later rows are not touched.
+ *   out          [batch, tq, hq, d] contiguous; must not overlap any other buffer.
+ *   n_past       the same for every sequence; 0 <= n_past, n_past + tq <= capacity
+ *                (n_past = 0 is attn_prefill of the chunk with the cache as k and v).
+ *   scale        finite and > 0.
+ *   The caches must not overlap each other or k_new / v_new.  Errors as attn_prefill.
+ */
+attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                                 void *v_cache, void *out, int64_t batch, int64_t tq, int64_t hq,
+                                 int64_t hkv, int64_t d, int64_t capacity, int64_t n_past,
+                                 const attn_headprep_t *prep, int causal, double scale,
+                                 attn_dtype_t dtype, void *stream);
+
+/*
  * attn_decode -- one new query row per sequence against a KV cache whose keys are
  * already prepped (gizml:netops, Functions > attention with tq = 1 < tk: the row
  * attends the whole cache).

@@ -6,7 +6,8 @@ against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg 
 imports the GPU library.
 
 The arithmetic lives in ``oracle.c`` (f64, plain loops).  This module only marshals
-numpy arrays into it and composes the two steps the way the attention path does:
+numpy arrays into it and composes the steps the way the attention path does (prefill,
+chunked prefill against a KV cache, decode):
 
 * HeadPrep -- gizml:netops reference page, "Types > HeadPrep".
 * attention and its causal mask -- same page, "Functions > attention" and
@@ -21,6 +22,7 @@ from .oracle import (  # noqa: F401
     attention,
     attention_rows,
     prefill,
+    prefill_chunk,
     decode,
     threads,
 )

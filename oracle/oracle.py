@@ -1,4 +1,5 @@
-"""ctypes binding of the f64 oracle (``oracle.c``) plus the path's two compositions.
+"""ctypes binding of the f64 oracle (``oracle.c``) plus the path's compositions (prefill,
+chunked prefill against a cache, decode).
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).  Inputs are numpy arrays of any
 float dtype; they are widened to f64, which is exact for f32 and bf16 values.
@@ -155,6 +156,32 @@ def prefill(q, k, v, qw, kw, cos, sin, half: int, eps: float, pos0: int, scale: 
     else:
         out = attention_rows(qh, kh, v, scale, causal, sel)
     return out, kh
+
+
+def prefill_chunk(q, k_new, v_new, k_cache, v_cache, n_past: int, qw, kw, cos, sin, half: int,
+                  eps: float, scale: float, causal: bool = True, sel=None, prep: bool = True,
+                  prep_k: bool = True):
+    """A chunk of tq new tokens against a cache holding n_past prepped rows: the chunk's
+    keys are prepped at positions n_past + t and written with its values to cache rows
+    n_past .. n_past + tq - 1, then the chunk's queries (prepped at positions n_past + i)
+    attend the cache rows 0 .. n_past + tq - 1, causal aligned bottom-right (netops
+    attention with tq < tk).  Returns (out, k_cache', v_cache') (copies, f64); with
+    ``sel`` only those query rows of out.  prep=False: nothing is prepped;
+    prep_k=False: k_new is taken as already prepped."""
+    q, k_new, v_new = _f64(q), _f64(k_new), _f64(v_new)
+    kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
+    B, tq = q.shape[0], q.shape[1]
+    pos = (n_past + np.arange(tq, dtype=np.int64))[None, :].repeat(B, axis=0)
+    qh = headprep(q, qw, cos, sin, half, pos, eps) if prep else q
+    kh = headprep(k_new, kw, cos, sin, half, pos, eps) if (prep and prep_k) else k_new
+    kc[:, n_past:n_past + tq] = kh
+    vc[:, n_past:n_past + tq] = v_new
+    tk = n_past + tq
+    if sel is None:
+        out = attention(qh, kc[:, :tk], vc[:, :tk], scale, causal)
+    else:
+        out = attention_rows(qh, kc[:, :tk], vc[:, :tk], scale, causal, sel)
+    return out, kc, vc
 
 
 def decode(q, k_cache, v_cache, lens, pos, qw, cos, sin, half: int, eps: float,

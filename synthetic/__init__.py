@@ -53,6 +53,9 @@ WORKLOADS = {
     "decode_bf16": Workload("decode_bf16", "decode", "bf16", 32, 32, 8, 4096, 128, 64, 1e4, 4),
     "long_prefill_bf16": Workload("long_prefill_bf16", "prefill", "bf16", 1, 64, 8, 16384, 128,
                                   64, 1e6, 5, outlier_frac=0.01, outlier_scale=8.0),
+    # chunked prefill: the last 512 of 4096 tokens against a cache holding the first 3584
+    "chunk_prefill_bf16": Workload("chunk_prefill_bf16", "prefill", "bf16", 4, 32, 8, 4096, 128, 64,
+                                   1e4, 6, extra={"n_past": 3584, "tq": 512}),
 }
 
 

@@ -116,6 +116,44 @@ def test_prep_empty_is_a_no_op(lib):
     assert _prep_call(lib, seq=0) == A.ATTN_OK
 
 
+def _chunk(lib, **kw):
+    a = dict(q=FAKE, kn=FAKE + (1 << 32), vn=FAKE + (2 << 32), kc=FAKE + (3 << 32), vc=FAKE + (4 << 32),
+             out=FAKE + (5 << 32), batch=2, tq=16, hq=8, hkv=2, d=128, cap=1024, n_past=100,
+             prep=_prep(rows=4096), causal=1, scale=0.088, dtype=A.ATTN_BF16)
+    a.update(kw)
+    prep = ctypes.byref(a["prep"]) if a["prep"] is not None else None
+    return lib.attn_prefill_chunk(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["out"], a["batch"], a["tq"],
+                                  a["hq"], a["hkv"], a["d"], a["cap"], a["n_past"], prep, a["causal"],
+                                  a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), A.ATTN_ERR_UNSUPPORTED),
+    (dict(q=None), A.ATTN_ERR_ARG),
+    (dict(kc=None), A.ATTN_ERR_ARG),
+    (dict(vn=FAKE + (2 << 32) + 4), A.ATTN_ERR_ARG),      # misaligned
+    (dict(hq=7), A.ATTN_ERR_ARG),                         # hq not a multiple of hkv
+    (dict(n_past=-1), A.ATTN_ERR_ARG),
+    (dict(n_past=1010), A.ATTN_ERR_ARG),                  # n_past + tq > capacity
+    (dict(cap=0), A.ATTN_ERR_ARG),
+    (dict(tq=-1), A.ATTN_ERR_ARG),
+    (dict(prep=_prep(rows=115)), A.ATTN_ERR_ARG),         # table ends before n_past + tq
+    (dict(prep=_prep(qw=None)), A.ATTN_ERR_ARG),
+    (dict(scale=0.0), A.ATTN_ERR_ARG),
+    (dict(out=FAKE + (3 << 32) + 4096), A.ATTN_ERR_ARG),  # out inside the k cache
+    (dict(vc=FAKE + (3 << 32) + 8192), A.ATTN_ERR_ARG),   # the caches overlap
+    (dict(kn=FAKE + (4 << 32) + 512), A.ATTN_ERR_ARG),    # new keys inside the v cache
+])
+def test_prefill_chunk_rejects(lib, kw, code):
+    assert _chunk(lib, **kw) == code
+    assert lib.attn_last_error()
+
+
+def test_prefill_chunk_empty_is_a_no_op(lib):
+    assert _chunk(lib, tq=0) == A.ATTN_OK
+    assert _chunk(lib, batch=0) == A.ATTN_OK
+
+
 def _decode(lib, **kw):
     # splits=4: the call needs a workspace, so every case below fails on the host.
     a = dict(q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), out=FAKE + (3 << 32), batch=32, hq=32,

@@ -218,6 +218,103 @@ def test_prefill_softmax_max_stress():
     assert_close(host(out), oracle.attention(qh, kh, inp["v"], w.scale, True), "bf16", "stress")
 
 
+# ------------------------------------------------------------------- attn_prefill_chunk
+
+def _chunk_inputs(dtype, d, half, hq, hkv, n_past, tq, seed, batch=2, spare=9):
+    """A sequence of n_past + tq tokens: the cache holds the first n_past (keys prepped
+    by the oracle, stored in the dtype) and NaN in every row past n_past + tq; the
+    chunk is the last tq tokens."""
+    w = synthetic.Workload("c", "prefill", dtype, batch, hq, hkv, n_past + tq, d, half, 1e4, seed)
+    inp = synthetic.make_prefill(w)
+    cap = n_past + tq + spare
+    kc = np.full((batch, cap, hkv, d), np.nan)
+    vc = np.full((batch, cap, hkv, d), np.nan)
+    if n_past:
+        pos = np.arange(n_past)[None].repeat(batch, 0)
+        kc[:, :n_past] = synthetic.to_storage(
+            oracle.headprep(inp["k"][:, :n_past], inp["kw"], inp["cos"], inp["sin"], half, pos, w.eps), dtype)
+        vc[:, :n_past] = inp["v"][:, :n_past]
+    return w, inp, kc, vc
+
+
+def _run_chunk(w, inp, kc, vc, n_past, causal, prep_k=True, k_new=None):
+    dt = w.dtype
+    sl = slice(n_past, None)
+    kcd, vcd = dev(kc, dt), dev(vc, dt)
+    prep = _prep_dev(inp)
+    if not prep_k:
+        prep = tah.HeadPrep(prep.qw, None, prep.cos, prep.sin, prep.eps)
+    kn = inp["k"][:, sl] if k_new is None else k_new
+    out = tah.attn_prefill_chunk(dev(inp["q"][:, sl], dt), dev(kn, dt), dev(inp["v"][:, sl], dt), kcd, vcd,
+                                 n_past, prep=prep, causal=causal, scale=w.scale)
+    return host(out), host(kcd), host(vcd)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("dtype,d,half,hq,hkv,n_past,tq", [
+    ("bf16", 128, 64, 8, 2, 700, 300),     # ragged tiles on both sides
+    ("bf16", 128, 64, 16, 4, 128, 256),    # tile-aligned
+    ("bf16", 64, 32, 4, 4, 1000, 1),       # one token: a decode step through the prefill kernel
+    ("bf16", 128, 24, 8, 2, 333, 77),      # half the prologue cannot turn: q prepped into out first
+    ("bf16", 128, 64, 8, 2, 0, 200),       # empty cache: plain prefill
+    ("f32", 64, 32, 8, 2, 150, 70),
+    ("f32", 128, 64, 4, 1, 37, 5),
+])
+def test_prefill_chunk_parity(dtype, d, half, hq, hkv, n_past, tq, causal):
+    require_gpu()
+    w, inp, kc, vc = _chunk_inputs(dtype, d, half, hq, hkv, n_past, tq, seed=61 + n_past + tq)
+    got, kc_gpu, vc_gpu = _run_chunk(w, inp, kc, vc, n_past, causal)
+    sl = slice(n_past, None)
+    ref, kc_ref, vc_ref = oracle.prefill_chunk(inp["q"][:, sl], inp["k"][:, sl], inp["v"][:, sl], kc, vc, n_past,
+                                               inp["qw"], inp["kw"], inp["cos"], inp["sin"], half, w.eps,
+                                               w.scale, causal)
+    assert_close(got, ref, dtype, "chunk output")
+    end = n_past + tq
+    assert_close(kc_gpu[:, n_past:end], kc_ref[:, n_past:end], dtype, "appended keys")
+    np.testing.assert_array_equal(vc_gpu[:, n_past:end], inp["v"][:, sl])       # values copied exactly
+    np.testing.assert_array_equal(kc_gpu[:, :n_past], kc[:, :n_past])           # earlier rows untouched
+    np.testing.assert_array_equal(vc_gpu[:, :n_past], vc[:, :n_past])
+    assert np.isnan(kc_gpu[:, end:]).all() and np.isnan(vc_gpu[:, end:]).all()   # later rows untouched
+
+
+def test_prefill_chunk_with_prepped_keys():
+    """prep->kw NULL: the chunk's keys are already prepped and are copied as they are."""
+    require_gpu()
+    w, inp, kc, vc = _chunk_inputs("bf16", 128, 64, 8, 2, 260, 100, seed=71)
+    pos = (260 + np.arange(100))[None].repeat(2, 0)
+    kh = synthetic.bf16_round(oracle.headprep(inp["k"][:, 260:], inp["kw"], inp["cos"], inp["sin"], 64, pos, w.eps))
+    got, kc_gpu, _ = _run_chunk(w, inp, kc, vc, 260, True, prep_k=False, k_new=kh)
+    np.testing.assert_array_equal(kc_gpu[:, 260:360], kh)
+    ref, _, _ = oracle.prefill_chunk(inp["q"][:, 260:], kh, inp["v"][:, 260:], kc, vc, 260, inp["qw"], inp["kw"],
+                                     inp["cos"], inp["sin"], 64, w.eps, w.scale, True, prep_k=False)
+    assert_close(got, ref, "bf16", "chunk with prepped keys")
+
+
+def test_prefill_chunks_equal_one_shot_prefill():
+    """600 tokens fed through the cache in chunks of 256, 1 and 343 give attn_prefill's
+    output rows, and the cache ends up holding the keys attn_prefill preps in place
+    (bit for bit: the same HeadPrep kernel)."""
+    require_gpu()
+    w = synthetic.Workload("o", "prefill", "bf16", 2, 16, 4, 600, 128, 64, 1e4, 73)
+    inp = synthetic.make_prefill(w)
+    q, k, v = dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16")
+    prep = _prep_dev(inp)
+    full = host(tah.attn_prefill(q, k.clone(), v, prep=prep, causal=True, scale=w.scale))
+    k_prepped = k.clone()
+    tah.attn_prep(None, k_prepped, prep, pos0=0)
+    kc = torch.zeros(2, 640, 4, 128, dtype=torch.bfloat16, device="cuda:0")
+    vc = torch.zeros_like(kc)
+    n_past = 0
+    for tq in (256, 1, 343):
+        sl = slice(n_past, n_past + tq)
+        out = tah.attn_prefill_chunk(q[:, sl].contiguous(), k[:, sl].contiguous(), v[:, sl].contiguous(), kc, vc,
+                                     n_past, prep=prep, causal=True, scale=w.scale)
+        assert_close(host(out), full[:, sl], "bf16", "chunk at %d" % n_past)
+        n_past += tq
+    torch.testing.assert_close(kc[:, :600], k_prepped, rtol=0, atol=0)
+    torch.testing.assert_close(vc[:, :600], v, rtol=0, atol=0)
+
+
 # ------------------------------------------------------------------------- attn_decode
 
 def _decode_inputs(w, batch=None, cache=None, seed=None):

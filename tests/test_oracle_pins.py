@@ -281,6 +281,55 @@ def test_decode_equals_prefill_row():
         np.testing.assert_allclose(dec, out[:, p], rtol=0, atol=1e-14)
 
 
+def test_chunked_prefill_equals_one_shot_prefill():
+    """Chunked prefill (netops attention with tq < tk, bottom-right causal): feeding a
+    sequence through the cache in chunks of 16, 1 and 23 tokens gives the one-shot
+    prefill's output rows and leaves the one-shot prepped keys and the values in the
+    cache; rows past the chunks stay as they were."""
+    w = synthetic.WORKLOADS["prefill_f32"]
+    inp = synthetic.make_prefill(w, seq=40, batch=2)
+    full, kh = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["qw"], inp["kw"], inp["cos"],
+                              inp["sin"], w.half, w.eps, 0, w.scale, True)
+    cap = 48
+    kc = np.full((2, cap, w.hkv, w.d), 7.0)
+    vc = np.full((2, cap, w.hkv, w.d), -3.0)
+    n_past = 0
+    for tq in (16, 1, 23):
+        sl = slice(n_past, n_past + tq)
+        out, kc, vc = oracle.prefill_chunk(inp["q"][:, sl], inp["k"][:, sl], inp["v"][:, sl], kc, vc,
+                                           n_past, inp["qw"], inp["kw"], inp["cos"], inp["sin"],
+                                           w.half, w.eps, w.scale, True)
+        np.testing.assert_allclose(out, full[:, sl], rtol=0, atol=1e-14)
+        n_past += tq
+    np.testing.assert_allclose(kc[:, :40], kh, rtol=0, atol=0)
+    np.testing.assert_array_equal(vc[:, :40], inp["v"])
+    assert (kc[:, 40:] == 7.0).all() and (vc[:, 40:] == -3.0).all()
+
+
+def test_chunk_of_one_token_is_decode():
+    """A chunk of one token at n_past is the decode of position n_past over the first
+    n_past + 1 cache rows; a non-causal chunk sees every row up to n_past + tq - 1."""
+    w = synthetic.WORKLOADS["prefill_f32"]
+    inp = synthetic.make_prefill(w, seq=30, batch=2)
+    _, kh = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["qw"], inp["kw"], inp["cos"],
+                           inp["sin"], w.half, w.eps, 0, w.scale, True)
+    n_past = 29
+    out, kc, vc = oracle.prefill_chunk(inp["q"][:, 29:], inp["k"][:, 29:], inp["v"][:, 29:], kh, inp["v"],
+                                       n_past, inp["qw"], inp["kw"], inp["cos"], inp["sin"], w.half,
+                                       w.eps, w.scale, True)
+    dec = oracle.decode(inp["q"][:, 29], kc, vc, np.full(2, 30), np.full(2, 29), inp["qw"], inp["cos"],
+                        inp["sin"], w.half, w.eps, w.scale)
+    np.testing.assert_allclose(out[:, 0], dec, rtol=0, atol=1e-14)
+    # non-causal chunk of 4 at n_past 26: every query sees all 30 rows
+    out_nc, kc2, vc2 = oracle.prefill_chunk(inp["q"][:, 26:], inp["k"][:, 26:], inp["v"][:, 26:], kh, inp["v"],
+                                            26, inp["qw"], inp["kw"], inp["cos"], inp["sin"], w.half,
+                                            w.eps, w.scale, False)
+    for i in range(4):
+        dec = oracle.decode(inp["q"][:, 26 + i], kc2, vc2, np.full(2, 30), np.full(2, 26 + i), inp["qw"],
+                            inp["cos"], inp["sin"], w.half, w.eps, w.scale)
+        np.testing.assert_allclose(out_nc[:, i], dec, rtol=0, atol=1e-14)
+
+
 def test_tiny_workload_end_to_end_against_library_routines():
     """The tiny f32 workload: oracle prefill vs torch rms_norm + complex turn + SDPA."""
     w = synthetic.WORKLOADS["tiny_f32"]

@@ -11,6 +11,7 @@ from .attn import (  # noqa: F401
     EXPORTS,
     attn_decode,
     attn_prefill,
+    attn_prefill_chunk,
     attn_prep,
     attn_supported,
     decode_default_splits,

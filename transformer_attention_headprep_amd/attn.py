@@ -20,7 +20,7 @@ ATTN_F32, ATTN_BF16 = 0, 1
 ATTN_OK, ATTN_ERR_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 0, -1, -2, -3, -4
 
 # The entry points include/attn.h declares (checked by the CPU test suite).
-EXPORTS = ("attn_prep", "attn_prefill", "attn_decode", "attn_decode_workspace_size",
+EXPORTS = ("attn_prep", "attn_prefill", "attn_prefill_chunk", "attn_decode", "attn_decode_workspace_size",
            "attn_decode_default_splits", "attn_supported", "attn_status_str", "attn_last_error")
 
 
@@ -55,6 +55,8 @@ def load_library(path: str = LIB_PATH):
     lib.attn_prefill.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 10 + [hp, ctypes.c_int, _dbl,
                                                                          ctypes.c_int, _vp]
     lib.attn_prefill.restype = ctypes.c_int
+    lib.attn_prefill_chunk.argtypes = [_vp] * 6 + [_i64] * 7 + [hp, ctypes.c_int, _dbl, ctypes.c_int, _vp]
+    lib.attn_prefill_chunk.restype = ctypes.c_int
     lib.attn_decode.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 5 + [_vp, _vp, _i64, hp, _dbl, _i64,
                                                                     _vp, ctypes.c_size_t,
                                                                     ctypes.c_int, _vp]
@@ -175,6 +177,31 @@ def attn_prefill(q, k, v, out=None, prep: HeadPrep | None = None, pos0: int = 0,
                             _row_stride(out, "out"), pos0,
                             ctypes.byref(st) if st is not None else None, int(bool(causal)),
                             float(scale), _dtype_code(q), _stream(stream)))
+    return out
+
+
+def attn_prefill_chunk(q, k_new, v_new, k_cache, v_cache, n_past: int, out=None,
+                       prep: HeadPrep | None = None, causal: bool = True, scale: float | None = None,
+                       stream=None) -> torch.Tensor:
+    """A chunk q [B, tq, Hq, D] against caches [B, capacity, Hkv, D] holding n_past rows:
+    appends prep(k_new) and v_new at rows n_past .., then attends rows 0 .. n_past + tq - 1."""
+    lib = load_library()
+    B, tq, hq, D = q.shape
+    cap, hkv = k_cache.shape[1], k_cache.shape[2]
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if t.dtype != q.dtype:
+            raise TypeError("all operands must share a dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = prep.struct() if prep is not None else None
+    _check(lib.attn_prefill_chunk(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                  B, tq, hq, hkv, D, cap, n_past,
+                                  ctypes.byref(st) if st is not None else None, int(bool(causal)),
+                                  float(scale), _dtype_code(q), _stream(stream)))
     return out
 
 

@@ -201,6 +201,94 @@ attn_status_t attn_prefill(const void *q, void *k, const void *v, void *out, int
     return hip_status(attn::launch_prefill(a, s), "attn_prefill");
 }
 
+attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                                 void *out, int64_t batch, int64_t tq, int64_t hq, int64_t hkv, int64_t d,
+                                 int64_t capacity, int64_t n_past, const attn_headprep_t *prep, int causal,
+                                 double scale, attn_dtype_t dtype, void *stream) {
+    g_last_error[0] = 0;
+    attn_status_t st = check_dtype_d(dtype, d);
+    if (st) return st;
+    if (batch < 0 || tq < 0) return fail(ATTN_ERR_ARG, "negative batch or tq");
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
+        return fail(ATTN_ERR_ARG, "hq = %lld must be a positive multiple of hkv = %lld", (long long)hq, (long long)hkv);
+    if ((st = check_rows("q", q, hq, d, hq * d))) return st;
+    if ((st = check_rows("k_new", k_new, hkv, d, hkv * d))) return st;
+    if ((st = check_rows("v_new", v_new, hkv, d, hkv * d))) return st;
+    if ((st = check_rows("k_cache", k_cache, hkv, d, hkv * d))) return st;
+    if ((st = check_rows("v_cache", v_cache, hkv, d, hkv * d))) return st;
+    if ((st = check_rows("out", out, hq, d, hq * d))) return st;
+    if (capacity <= 0 || capacity >= ((int64_t)1 << 31)) return fail(ATTN_ERR_ARG, "capacity %lld outside [1, 2^31)", (long long)capacity);
+    if (n_past < 0 || n_past + tq > capacity)
+        return fail(ATTN_ERR_ARG, "n_past %lld + tq %lld outside [0, capacity %lld]", (long long)n_past, (long long)tq,
+                    (long long)capacity);
+    if (!std::isfinite(scale) || !(scale > 0.0)) return fail(ATTN_ERR_ARG, "scale must be finite and > 0");
+    const bool prep_k = prep && prep->kw;
+    if (prep && (st = check_prep(prep, d, true, false, n_past, tq))) return st;
+    if (prep_k && !aligned16(prep->kw)) return fail(ATTN_ERR_ARG, "prep weights are not 16-byte aligned");
+    if (batch == 0 || tq == 0) return ATTN_OK;
+    if ((int64_t)((tq + 127) / 128) * batch * hq >= (int64_t)1 << 31)
+        return fail(ATTN_ERR_ARG, "problem too large for one launch");
+    const size_t es = elem_size(dtype);
+    const Span so = span(out, batch * tq, hq * d, hq, d, es);
+    const Span sq = span(q, batch * tq, hq * d, hq, d, es);
+    const Span skn = span(k_new, batch * tq, hkv * d, hkv, d, es);
+    const Span svn = span(v_new, batch * tq, hkv * d, hkv, d, es);
+    const Span skc = span(k_cache, batch * capacity, hkv * d, hkv, d, es);
+    const Span svc = span(v_cache, batch * capacity, hkv * d, hkv, d, es);
+    if (overlap(so, sq) || overlap(so, skn) || overlap(so, svn) || overlap(so, skc) || overlap(so, svc))
+        return fail(ATTN_ERR_ARG, "out overlaps another buffer");
+    if (overlap(skc, svc) || overlap(skn, skc) || overlap(skn, svc) || overlap(svn, skc) || overlap(svn, svc))
+        return fail(ATTN_ERR_ARG, "the caches overlap each other or the new rows");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf16 = dtype == ATTN_BF16;
+    const int64_t crs = hkv * d, cbs = capacity * crs;    // cache row and sequence strides
+
+    // 1-2. Append: prepped keys and values into cache rows n_past .. n_past + tq - 1.
+    attn::CopyRowsLaunch cv{};
+    cv.src = v_new; cv.dst = static_cast<uint8_t *>(v_cache) + (size_t)(n_past * crs) * es;
+    cv.src_bs = tq * crs; cv.src_rs = crs; cv.dst_bs = cbs; cv.dst_rs = crs;
+    cv.batch = batch; cv.rows = tq; cv.row_elems = crs; cv.elem = (int64_t)es;
+    void *k_dst = static_cast<uint8_t *>(k_cache) + (size_t)(n_past * crs) * es;
+    if (prep_k) {
+        attn::PrepLaunch pk{};
+        pk.k_src = k_new; pk.k_dst = k_dst; pk.k_src_rs = crs; pk.k_dst_rs = crs; pk.hkv = hkv;
+        pk.k_src_bs = tq * crs; pk.k_dst_bs = cbs;
+        pk.batch = batch; pk.seq = tq; pk.d = d; pk.pos0 = n_past;
+        pk.qw = prep->qw; pk.kw = prep->kw; pk.cos = prep->cos; pk.sin = prep->sin;
+        pk.half = prep->half; pk.eps = (float)prep->eps; pk.bf16 = bf16;
+        if ((st = hip_status(attn::launch_prep(pk, s), "attn_prefill_chunk (k prep)"))) return st;
+    } else {
+        attn::CopyRowsLaunch ck = cv;
+        ck.src = k_new; ck.dst = k_dst;
+        if ((st = hip_status(attn::launch_copy_rows(ck, s), "attn_prefill_chunk (k copy)"))) return st;
+    }
+    if ((st = hip_status(attn::launch_copy_rows(cv, s), "attn_prefill_chunk (v copy)"))) return st;
+
+    // 3. Attention of the chunk's queries over cache rows 0 .. n_past + tq - 1.
+    attn::PrefillLaunch a{};
+    a.q = q; a.k = k_cache; a.v = v_cache; a.out = out;
+    a.q_rs = hq * d; a.k_rs = crs; a.v_rs = crs; a.o_rs = hq * d;
+    a.k_bs = cbs; a.v_bs = cbs;
+    a.batch = batch; a.seq = tq; a.tk = n_past + tq; a.hq = hq; a.hkv = hkv; a.d = d; a.pos0 = n_past;
+    a.causal = causal != 0; a.scale = (float)scale; a.bf16 = bf16;
+    if (prep) {
+        if (attn::prefill_fuses_half(d, prep->half, bf16)) {
+            a.prep_q = true;
+            a.qw = prep->qw; a.cos = prep->cos; a.sin = prep->sin; a.half = prep->half; a.eps = (float)prep->eps;
+        } else {
+            // q prepped into out first; each attention block reads exactly the rows it writes.
+            attn::PrepLaunch pq{};
+            pq.q_src = q; pq.q_dst = out; pq.q_src_rs = hq * d; pq.q_dst_rs = hq * d; pq.hq = hq;
+            pq.batch = batch; pq.seq = tq; pq.d = d; pq.pos0 = n_past;
+            pq.qw = prep->qw; pq.cos = prep->cos; pq.sin = prep->sin;
+            pq.half = prep->half; pq.eps = (float)prep->eps; pq.bf16 = bf16;
+            if ((st = hip_status(attn::launch_prep(pq, s), "attn_prefill_chunk (q prep)"))) return st;
+            a.q = out;
+        }
+    }
+    return hip_status(attn::launch_prefill(a, s), "attn_prefill_chunk");
+}
+
 int64_t attn_decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len) {
     if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || max_len <= 0) return 0;
     return attn::decode_default_splits(batch, hq, hkv, max_len);

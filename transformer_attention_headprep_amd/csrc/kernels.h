@@ -11,10 +11,12 @@
 namespace attn {
 
 // HeadPrep of the tokens [0, seq) of `batch` sequences, for q and/or k.  src and dst
-// may be the same buffer (in place).  Token t uses table row pos0 + t.
+// may be the same buffer (in place).  Token t uses table row pos0 + t.  Token t of
+// sequence b sits at b * bs + t * rs (elements); a batch stride of 0 means seq * rs.
 struct PrepLaunch {
     const void *q_src; void *q_dst; int64_t q_src_rs, q_dst_rs; int64_t hq;
     const void *k_src; void *k_dst; int64_t k_src_rs, k_dst_rs; int64_t hkv;
+    int64_t q_src_bs, q_dst_bs, k_src_bs, k_dst_bs;
     int64_t batch, seq, d, pos0;
     const float *qw, *kw, *cos, *sin;
     int64_t half;
@@ -23,12 +25,17 @@ struct PrepLaunch {
 };
 hipError_t launch_prep(const PrepLaunch &a, hipStream_t stream);
 
-// Attention of whole sequences.  When q_prepped is false and prep tables are given,
-// q's HeadPrep is applied as the q rows are read (k must already be prepped).
+// Attention of `seq` query rows per sequence against `tk` key rows (tk >= seq; 0 means
+// tk = seq).  Query row i sits at position tk - seq + i (bottom-right alignment): with
+// causal, it sees keys j <= i + tk - seq.  When prep_q is set, q's HeadPrep is applied
+// as the q rows are read, query row i at table row pos0 + i (k must already be
+// prepped).  Row t of sequence b sits at b * bs + t * rs (elements); a batch stride of
+// 0 means rows * rs.
 struct PrefillLaunch {
     const void *q; const void *k; const void *v; void *out;
     int64_t q_rs, k_rs, v_rs, o_rs;
-    int64_t batch, seq, hq, hkv, d, pos0;
+    int64_t q_bs, k_bs, v_bs, o_bs;
+    int64_t batch, seq, tk, hq, hkv, d, pos0;
     bool prep_q;                 // apply HeadPrep to q in the prologue
     const float *qw, *cos, *sin;
     int64_t half;
@@ -40,6 +47,18 @@ struct PrefillLaunch {
 hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream);
 // true if the fused q prologue of the chosen kernel can turn pairs `half` apart.
 bool prefill_fuses_half(int64_t d, int64_t half, bool bf16);
+// Fill the zero batch strides and tk of a prefill launch with their defaults.
+void prefill_defaults(PrefillLaunch &a);
+
+// Copy `rows` rows of `row_elems` elements of `batch` sequences (16-byte multiples,
+// 16-byte aligned): row t of sequence b from src + b * src_bs + t * src_rs to
+// dst + b * dst_bs + t * dst_rs (strides in elements of `elem` bytes).
+struct CopyRowsLaunch {
+    const void *src; void *dst;
+    int64_t src_bs, src_rs, dst_bs, dst_rs;
+    int64_t batch, rows, row_elems, elem;
+};
+hipError_t launch_copy_rows(const CopyRowsLaunch &a, hipStream_t stream);
 
 struct DecodeLaunch {
     const void *q; const void *k; const void *v; void *out;

@@ -132,6 +132,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     // ---- which (batch, q head, query tile) this block owns
     const int nq_tiles = (int)((p.seq + kBM - 1) / kBM);
+    const int tq = (int)p.seq, tk = (int)p.tk, qoff = tk - tq;   // query i sits at key position i + qoff
     const int group = (int)(p.hq / p.hkv);
     const int pairs = (int)(p.batch * p.hkv);
     int b, h, qtile;
@@ -160,10 +161,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int kvh = h / group;
 
     const int64_t r = (int64_t)qtile * kBM + 32 * w + n;
-    const bool row_ok = r < p.seq;
-    const int seq = (int)p.seq;
+    const bool row_ok = r < tq;
 
-    const int64_t last_key = CAUSAL ? min<int64_t>(p.seq - 1, (int64_t)qtile * kBM + kBM - 1) : p.seq - 1;
+    const int64_t last_key = CAUSAL ? min<int64_t>(tk - 1, (int64_t)qtile * kBM + kBM - 1 + qoff) : tk - 1;
     const int ntiles = (int)(last_key / kBN) + 1;
 
     // ---- tile loads: waves 0 and 1 move K, waves 2 and 3 move V; load t of a wave
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int nloads = loads_k ? (G::kKLoads - wl + 1) / 2 : (G::kVLoads - wl + 1) / 2;
     const int64_t rs = loads_k ? p.k_rs : p.v_rs;
     const uint16_t *src = static_cast<const uint16_t *>(loads_k ? p.k : p.v) +
-                          (int64_t)b * p.seq * rs + (int64_t)kvh * D;
+                          (int64_t)b * (loads_k ? p.k_bs : p.v_bs) + (int64_t)kvh * D;
     const int slots = loads_k ? G::kKSlots : G::kVSlots;
     int voff[G::kPerWave];
 #pragma unroll
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     auto load_tile = [&](int kt, int bsel) {
         const int key0 = kt * kBN;
-        const __amdgpu_buffer_rsrc_t rsrc = seq_rsrc(src + (int64_t)key0 * rs, ((int64_t)(seq - 1 - key0) * rs + D) * 2);
+        const __amdgpu_buffer_rsrc_t rsrc = seq_rsrc(src + (int64_t)key0 * rs, ((int64_t)(tk - 1 - key0) * rs + D) * 2);
         unsigned char *dst = smem + bsel * G::kBufBytes + (loads_k ? 0 : G::kKBytes);
 #pragma unroll
         for (int t = 0; t < G::kPerWave; ++t) {
@@ -202,8 +202,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // ---- q prologue: load this lane's 64 (or 32) values of its row, HeadPrep, bf16.
     bf16x8 qf[NC];
     {
-        const uint16_t *qrow = static_cast<const uint16_t *>(p.q) +
-                               ((int64_t)b * p.seq + (row_ok ? r : 0)) * p.q_rs + (int64_t)h * D;
+        const uint16_t *qrow = static_cast<const uint16_t *>(p.q) + (int64_t)b * p.q_bs +
+                               (row_ok ? r : 0) * p.q_rs + (int64_t)h * D;
         uint4 raw[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c)
@@ -299,9 +299,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
         // Mask: register 4i+jj of block kb holds key key0 + 32 kb + 8 i + 4 g + jj.
-        const bool need_mask = (key0 + kBN > seq) || (CAUSAL && key0 + kBN - 1 > qtile * kBM);
+        const bool need_mask = (key0 + kBN > tk) || (CAUSAL && key0 + kBN - 1 > qtile * kBM + qoff);
         if (need_mask) {
-            const int lim = (CAUSAL ? min(seq - 1, (int)r) : seq - 1) - (key0 + 4 * g);   // last visible
+            const int lim = (CAUSAL ? min(tk - 1, (int)r + qoff) : tk - 1) - (key0 + 4 * g);   // last visible
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (row_ok) {
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-        uint16_t *orow = static_cast<uint16_t *>(p.out) + ((int64_t)b * p.seq + r) * p.o_rs + (int64_t)h * D;
+        uint16_t *orow = static_cast<uint16_t *>(p.out) + (int64_t)b * p.o_bs + r * p.o_rs + (int64_t)h * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -405,7 +405,17 @@ bool prefill_fuses_half(int64_t d, int64_t half, bool bf16) {
     return half == 0 || half % 16 == 0;   // pairs 1, 2, 3 or 4 chunks of 16 apart
 }
 
-hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream) {
+void prefill_defaults(PrefillLaunch &a) {
+    if (a.tk == 0) a.tk = a.seq;
+    if (a.q_bs == 0) a.q_bs = a.seq * a.q_rs;
+    if (a.o_bs == 0) a.o_bs = a.seq * a.o_rs;
+    if (a.k_bs == 0) a.k_bs = a.tk * a.k_rs;
+    if (a.v_bs == 0) a.v_bs = a.tk * a.v_rs;
+}
+
+hipError_t launch_prefill(const PrefillLaunch &a0, hipStream_t stream) {
+    PrefillLaunch a = a0;
+    prefill_defaults(a);
     if (!a.bf16) return launch_prefill_f32(a, stream);
     if (a.d == 64) {
         if (a.causal) launch_bf16_d<64, true>(a, stream); else launch_bf16_d<64, false>(a, stream);

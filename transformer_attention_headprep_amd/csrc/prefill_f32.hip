@@ -1,7 +1,7 @@
 // prefill_f32.hip -- f32 attention of whole sequences on the vector ALUs.
 //
-// softmax(q k^T scale [+ causal mask]) v (gizml:netops reference page, Functions >
-// attention) without a score matrix: keys go in tiles of 32 through LDS and each
+// softmax(q k^T scale [+ causal mask, bottom-right when there are more keys than
+// queries]) v (gizml:netops reference page, Functions > attention) without a score matrix: keys go in tiles of 32 through LDS and each
 // query row keeps a running maximum m, sum l and output a, rescaled by
 // c = e^(m_old - m_new) when the maximum moves (the blocked online softmax that
 // page describes for its own f32 kernel).  One lane owns one query row, so the q
@@ -27,8 +27,9 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(const PrefillLaunch 
     const int qtile = gridDim.x - 1 - blockIdx.x;         // longest causal rows first
     const int64_t r = (int64_t)qtile * kRows + threadIdx.x;
     const bool row_ok = r < p.seq;
+    const int64_t tk = p.tk, qoff = p.tk - p.seq;          // query r sits at key position r + qoff
     const int g = h / (p.hq / p.hkv);
-    const float *qbase = static_cast<const float *>(p.q) + (b * p.seq + (row_ok ? r : 0)) * p.q_rs + h * D;
+    const float *qbase = static_cast<const float *>(p.q) + b * p.q_bs + (row_ok ? r : 0) * p.q_rs + h * D;
 
     float q[D];
 #pragma unroll
@@ -61,10 +62,10 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(const PrefillLaunch 
 #pragma unroll
     for (int e = 0; e < D; ++e) o[e] = 0.f;
 
-    const int64_t last_key = CAUSAL ? min<int64_t>(p.seq - 1, (int64_t)qtile * kRows + kRows - 1) : p.seq - 1;
+    const int64_t last_key = CAUSAL ? min<int64_t>(tk - 1, (int64_t)qtile * kRows + kRows - 1 + qoff) : tk - 1;
     const int ntiles = (int)(last_key / kKeys) + 1;
-    const float *kb = static_cast<const float *>(p.k) + (int64_t)b * p.seq * p.k_rs + g * D;
-    const float *vb = static_cast<const float *>(p.v) + (int64_t)b * p.seq * p.v_rs + g * D;
+    const float *kb = static_cast<const float *>(p.k) + (int64_t)b * p.k_bs + g * D;
+    const float *vb = static_cast<const float *>(p.v) + (int64_t)b * p.v_bs + g * D;
 
     for (int kt = 0; kt < ntiles; ++kt) {
         __syncthreads();
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(const PrefillLaunch 
             const int key = idx / (D / 4), seg = idx % (D / 4);
             const int64_t j = (int64_t)kt * kKeys + key;
             float4 kv = make_float4(0, 0, 0, 0), vv = make_float4(0, 0, 0, 0);
-            if (j < p.seq) {
+            if (j < tk) {
                 kv = *reinterpret_cast<const float4 *>(kb + j * p.k_rs + 4 * seg);
                 vv = *reinterpret_cast<const float4 *>(vb + j * p.v_rs + 4 * seg);
             }
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(const PrefillLaunch 
                 acc = fmaf(q[4 * e + 3], kk.w, acc);
             }
             const int64_t j = (int64_t)kt * kKeys + jj;
-            const bool vis = j < p.seq && (!CAUSAL || j <= r);
+            const bool vis = j < tk && (!CAUSAL || j <= r + qoff);
             s[jj] = vis ? acc * C : -INFINITY;
             mx = fmaxf(mx, s[jj]);
         }
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(const PrefillLaunch 
     }
     if (row_ok) {
         const float inv = l > 0.f ? 1.0f / l : 0.f;
-        float *ob = static_cast<float *>(p.out) + (b * p.seq + r) * p.o_rs + h * D;
+        float *ob = static_cast<float *>(p.out) + b * p.o_bs + r * p.o_rs + h * D;
 #pragma unroll
         for (int e = 0; e < D; e += 4)
             *reinterpret_cast<float4 *>(ob + e) =

@@ -10,6 +10,8 @@
 // 4i.. and the 4 values at d/2 + 4i.., so each wave reads 2 x 64 contiguous 8-byte
 // (bf16) or 16-byte (f32) pieces and, when half = d/2, every turned pair sits in one
 // lane.  Other halves go through LDS.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -21,6 +23,7 @@ constexpr int kPrepThreads = 256;
 struct PrepParams {
     const void *q_src; void *q_dst; int64_t q_src_rs, q_dst_rs; int64_t hq;
     const void *k_src; void *k_dst; int64_t k_src_rs, k_dst_rs; int64_t hkv;
+    int64_t q_src_bs, q_dst_bs, k_src_bs, k_dst_bs;
     int64_t seq, pos0, n_q_units, n_units;
     const float *qw, *kw, *cos, *sin;
     int half;
@@ -72,17 +75,17 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepParams p) 
     if (is_q) {
         const int64_t u = valid ? unit : 0;
         row = u / p.hq;
-        const int64_t h = u % p.hq;
+        const int64_t h = u % p.hq, bb = row / p.seq, t = row % p.seq;
         src = p.q_src; dst = p.q_dst; w = p.qw;
-        src_off = row * p.q_src_rs + h * D;
-        dst_off = row * p.q_dst_rs + h * D;
+        src_off = bb * p.q_src_bs + t * p.q_src_rs + h * D;
+        dst_off = bb * p.q_dst_bs + t * p.q_dst_rs + h * D;
     } else {
         const int64_t u = valid ? unit - p.n_q_units : 0;
         row = u / p.hkv;
-        const int64_t h = u % p.hkv;
+        const int64_t h = u % p.hkv, bb = row / p.seq, t = row % p.seq;
         src = p.k_src; dst = p.k_dst; w = p.kw;
-        src_off = row * p.k_src_rs + h * D;
-        dst_off = row * p.k_dst_rs + h * D;
+        src_off = bb * p.k_src_bs + t * p.k_src_rs + h * D;
+        dst_off = bb * p.k_dst_bs + t * p.k_dst_rs + h * D;
     }
     const int e_lo = 4 * li, e_hi = D / 2 + 4 * li;
 
@@ -164,7 +167,31 @@ hipError_t launch_prep_d(const PrepParams &p, int mode, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Row copy (16 bytes per lane, grid-stride): row t of sequence b.
+__global__ __launch_bounds__(256) void copy_rows_kernel(const uint8_t *src, uint8_t *dst, int64_t src_bs,
+                                                        int64_t src_rs, int64_t dst_bs, int64_t dst_rs,
+                                                        int64_t rows, int64_t row_bytes, int64_t total16) {
+    const int64_t per_row = row_bytes / 16;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total16; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t rr = i / per_row, c = i % per_row;
+        const int64_t bb = rr / rows, t = rr % rows;
+        const uint4 v = *reinterpret_cast<const uint4 *>(src + bb * src_bs + t * src_rs + 16 * c);
+        *reinterpret_cast<uint4 *>(dst + bb * dst_bs + t * dst_rs + 16 * c) = v;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_copy_rows(const CopyRowsLaunch &a, hipStream_t stream) {
+    const int64_t row_bytes = a.row_elems * a.elem;
+    const int64_t total16 = a.batch * a.rows * (row_bytes / 16);
+    if (total16 == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((total16 + 255) / 256, 4096);
+    hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint8_t *>(a.src), static_cast<uint8_t *>(a.dst), a.src_bs * a.elem,
+                       a.src_rs * a.elem, a.dst_bs * a.elem, a.dst_rs * a.elem, a.rows, row_bytes, total16);
+    return hipGetLastError();
+}
 
 hipError_t launch_prep(const PrepLaunch &a, hipStream_t stream) {
     PrepParams p;
@@ -172,6 +199,10 @@ hipError_t launch_prep(const PrepLaunch &a, hipStream_t stream) {
     p.hq = a.q_src ? a.hq : 1;
     p.k_src = a.k_src; p.k_dst = a.k_dst; p.k_src_rs = a.k_src_rs; p.k_dst_rs = a.k_dst_rs;
     p.hkv = a.k_src ? a.hkv : 1;
+    p.q_src_bs = a.q_src_bs ? a.q_src_bs : a.seq * a.q_src_rs;
+    p.q_dst_bs = a.q_dst_bs ? a.q_dst_bs : a.seq * a.q_dst_rs;
+    p.k_src_bs = a.k_src_bs ? a.k_src_bs : a.seq * a.k_src_rs;
+    p.k_dst_bs = a.k_dst_bs ? a.k_dst_bs : a.seq * a.k_dst_rs;
     p.seq = a.seq;
     p.pos0 = a.pos0;
     p.n_q_units = a.q_src ? a.batch * a.seq * a.hq : 0;

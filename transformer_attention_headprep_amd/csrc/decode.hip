@@ -230,6 +230,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
     const int start = split * (int)p.per_split;
     const int end = min(len, start + (int)p.per_split);
 
+    const int64_t rowb = p.hkv * D * 2;       // bytes between consecutive cache rows
+    const uint8_t *kbase = static_cast<const uint8_t *>(p.k) + ((int64_t)b * p.capacity * p.hkv + bc.kvh) * D * 2;
+    const uint8_t *vbase = static_cast<const uint8_t *>(p.v) + ((int64_t)b * p.capacity * p.hkv + bc.kvh) * D * 2;
+    unsigned char *kbuf = smem + w * 2 * G::kBuf;    // this wave's K chunk
+    unsigned char *vbuf = kbuf + G::kBuf;            // and V chunk
+
+    // Load i of a chunk: lane L reads 16 bytes (chunk L % kCpr) of row kRpi i + L / kCpr,
+    // kRpi whole rows per instruction.  The row offset stays in the VGPR offset (the part
+    // the descriptor's range check covers); each load has its own descriptor.
+    const int lrow = lane / G::kCpr, lchunk = lane % G::kCpr;
+    const int loff = lrow * (int)rowb + 16 * lchunk;
+
+    // This wave's chunks: keys start + 16 (w + 4 j) .. +15, j < nch.
+    const int first = start + kChunk * w;
+    const int nch = end > first ? (end - first + kChunk * kWaves - 1) / (kChunk * kWaves) : 0;
+
+    struct Regs {
+        u32x4 k[G::kLoads];
+        u32x4 v[G::kLoads];
+    };
+    // Chunk j's rows, read through descriptors that end at the cache's last valid row
+    // (rows past it, and every row of a chunk past the end, read as zero without a fetch).
+    auto issue = [&](int j, Regs &r) {
+        const int key0 = first + kChunk * kWaves * j;
+        const int64_t bytes = (int64_t)min(kChunk, end - key0) * rowb;
+#pragma unroll
+        for (int i = 0; i < G::kLoads; ++i) {
+            const int64_t skip = (int64_t)(G::kRpi * i) * rowb;
+            r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(seq_rsrc(kbase + key0 * rowb + skip, bytes - skip), loff, 0, 0);
+            r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(seq_rsrc(vbase + key0 * rowb + skip, bytes - skip), loff, 0, 0);
+        }
+    };
+
+    // The first chunk's rows are on their way (into registers) during the q prologue.
+    Regs ra, rb;
+    issue(0, ra);
+
     float (*qs)[D] = reinterpret_cast<float (*)[D]>(smem);
     float (*qh)[D] = reinterpret_cast<float (*)[D]>(smem + GB * D * 4);
     q_prologue<true, D, GB>(p, b, h0, nh, qs, qh, reinterpret_cast<float *>(smem + 2 * GB * D * 4));
@@ -261,43 +298,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
     }
     __syncthreads();     // q rows are dead: the LDS now holds K and V chunks
 
-    const int64_t rowb = p.hkv * D * 2;       // bytes between consecutive cache rows
-    const uint8_t *kbase = static_cast<const uint8_t *>(p.k) + ((int64_t)b * p.capacity * p.hkv + bc.kvh) * D * 2;
-    const uint8_t *vbase = static_cast<const uint8_t *>(p.v) + ((int64_t)b * p.capacity * p.hkv + bc.kvh) * D * 2;
-    unsigned char *kbuf = smem + w * 2 * G::kBuf;    // this wave's K chunk
-    unsigned char *vbuf = kbuf + G::kBuf;            // and V chunk
-
-    // Load i of a chunk: lane L reads 16 bytes (chunk L % kCpr) of row kRpi i + L / kCpr,
-    // kRpi whole rows per instruction.  The row offset stays in the VGPR offset (the part
-    // the descriptor's range check covers); each load has its own descriptor.
-    const int lrow = lane / G::kCpr, lchunk = lane % G::kCpr;
-    const int loff = lrow * (int)rowb + 16 * lchunk;
-
     f32x4 acc[G::kNT];
 #pragma unroll
     for (int t = 0; t < G::kNT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, thr = -INFINITY, l_lane = 0.f;
-
-    // This wave's chunks: keys start + 16 (w + 4 j) .. +15, j < nch.
-    const int first = start + kChunk * w;
-    const int nch = end > first ? (end - first + kChunk * kWaves - 1) / (kChunk * kWaves) : 0;
-
-    struct Regs {
-        u32x4 k[G::kLoads];
-        u32x4 v[G::kLoads];
-    };
-    // Chunk j's rows, read through descriptors that end at the cache's last valid row
-    // (rows past it, and every row of a chunk past the end, read as zero without a fetch).
-    auto issue = [&](int j, Regs &r) {
-        const int key0 = first + kChunk * kWaves * j;
-        const int64_t bytes = (int64_t)min(kChunk, end - key0) * rowb;
-#pragma unroll
-        for (int i = 0; i < G::kLoads; ++i) {
-            const int64_t skip = (int64_t)(G::kRpi * i) * rowb;
-            r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(seq_rsrc(kbase + key0 * rowb + skip, bytes - skip), loff, 0, 0);
-            r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(seq_rsrc(vbase + key0 * rowb + skip, bytes - skip), loff, 0, 0);
-        }
-    };
 
     // A wave's LDS operations run in order, so chunk j+1's stores cannot overtake
     // chunk j's reads of the same buffers.
@@ -354,8 +358,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
     // chunk j+1 is in flight while chunk j is computed.  The chunk after the last one
     // is issued with empty descriptors (nothing fetched), which keeps the loop free of
     // branches around the loads.
-    Regs ra, rb;
-    issue(0, ra);
     for (int j = 0; j < nch; j += 2) {
         issue(j + 1, rb);
         compute(j, ra);

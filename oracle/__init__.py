@@ -9,7 +9,9 @@ The arithmetic lives in ``oracle.c`` (f64, plain loops).  This module only marsh
 numpy arrays into it and composes the steps the way the attention path does (prefill,
 chunked prefill against a KV cache, decode):
 
-* HeadPrep -- gizml:netops reference page, "Types > HeadPrep".
+* HeadPrep -- gizml:netops reference page, "Types > HeadPrep" (split halves, and
+  FLUX.3's adjacent pairs).
+* the whole-row norm and rotary -- same page, "Functions > rowNormRopeInto".
 * attention and its causal mask -- same page, "Functions > attention" and
   "Functions > causalMask".
 * headPrepInPlace's position rule (the table row of a token is its sequence row,
@@ -19,6 +21,7 @@ from .oracle import (  # noqa: F401
     build,
     library_path,
     headprep,
+    row_norm_rope,
     attention,
     attention_rows,
     prefill,

@@ -86,6 +86,101 @@ int oracle_headprep(double *x, int64_t rows, int64_t heads, int64_t d,
  * Visible keys: j < n, and j <= i + n - tq when causal.  No visible key: zeros.
  * s is scratch of at least n doubles.
  */
+/*
+ * The same HeadPrep with the turned values taken as adjacent pairs (gizml:netops
+ * reference page, Types > HeadPrep: FLUX.3's pairs, loaded even values first): the
+ * head's values are read even ones first, so value 2i plays the part of value i and
+ * value 2i + 1 that of value i + half.  Pair (2i, 2i + 1), i < half, turns by table
+ * entry i:  a' = a cos - b sin,  b' = b cos + a sin,  a = x_{2i},  b = x_{2i+1}.
+ * Values from 2*half on are left as they are.
+ */
+static void prep_one_head_pairs(double *x, int64_t d, const double *w,
+                                const double *cos_row, const double *sin_row, int64_t half,
+                                double eps)
+{
+    double sq = 0.0;
+    for (int64_t e = 0; e < d; ++e)
+        sq += x[e] * x[e];
+    const double rt = sqrt(sq / (double)d + eps);
+    for (int64_t e = 0; e < d; ++e)
+        x[e] = x[e] * w[e] / rt;
+    for (int64_t i = 0; i < half; ++i) {
+        const double a = x[2 * i], b = x[2 * i + 1];
+        const double c = cos_row[i], s = sin_row[i];
+        x[2 * i] = a * c - b * s;
+        x[2 * i + 1] = b * c + a * s;
+    }
+}
+
+int oracle_headprep_pairs(double *x, int64_t rows, int64_t heads, int64_t d,
+                          const double *w, const double *cos_t, const double *sin_t,
+                          int64_t half, int64_t table_rows, const int64_t *pos, double eps)
+{
+    if (!x || !w || rows < 0 || heads < 0 || d <= 0 || half < 0 || 2 * half > d || eps < 0)
+        return -1;
+    if (half > 0) {
+        if (!cos_t || !sin_t || !pos || table_rows <= 0)
+            return -1;
+        for (int64_t r = 0; r < rows; ++r)
+            if (pos[r] < 0 || pos[r] >= table_rows)
+                return -2;
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t item = 0; item < rows * heads; ++item) {
+        const int64_t r = item / heads;
+        const double *c = half > 0 ? cos_t + half * pos[r] : NULL;
+        const double *s = half > 0 ? sin_t + half * pos[r] : NULL;
+        prep_one_head_pairs(x + item * d, d, w, c, s, half, eps);
+    }
+    return 0;
+}
+
+/*
+ * The whole-row norm and rotary of LTX (gizml:netops reference page, Functions >
+ * rowNormRopeInto), in place on x [rows, width]:
+ *   1. each row over the RMS of all its width values, eps inside the root, times w[e];
+ *   2. with tables (cos_t, sin_t [table_rows, width/2]): each head of `head` values
+ *      turned by split halves, value j < head/2 of head h with value j + head/2 by
+ *      the angle of pair h*head/2 + j of the row's table row pos[row].
+ */
+int oracle_row_norm_rope(double *x, int64_t rows, int64_t width, int64_t head, const double *w,
+                         const double *cos_t, const double *sin_t, int64_t table_rows,
+                         const int64_t *pos, double eps)
+{
+    if (!x || !w || rows < 0 || width <= 0 || head <= 0 || head % 2 != 0 || width % head != 0 || eps < 0)
+        return -1;
+    if (cos_t || sin_t) {
+        if (!cos_t || !sin_t || !pos || table_rows <= 0)
+            return -1;
+        for (int64_t r = 0; r < rows; ++r)
+            if (pos[r] < 0 || pos[r] >= table_rows)
+                return -2;
+    }
+    const int64_t half = head / 2, tw = width / 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double *xr = x + r * width;
+        double acc = 0.0;
+        for (int64_t e = 0; e < width; ++e)
+            acc += xr[e] * xr[e];
+        acc /= (double)width;
+        const double nrm = sqrt(acc + eps);
+        for (int64_t e = 0; e < width; ++e)
+            xr[e] = xr[e] * w[e] / nrm;
+        if (!cos_t)
+            continue;
+        const double *c = cos_t + pos[r] * tw, *s = sin_t + pos[r] * tw;
+        for (int64_t h = 0; h < width / head; ++h)
+            for (int64_t j = 0; j < half; ++j) {
+                const int64_t ia = h * head + j, ib = ia + half, t = h * half + j;
+                const double a = xr[ia], b = xr[ib];
+                xr[ia] = a * c[t] - b * s[t];
+                xr[ib] = b * c[t] + a * s[t];
+            }
+    }
+    return 0;
+}
+
 static void attend_one(const double *q, const double *k, const double *v, double *out,
                        int64_t b, int64_t i, int64_t h,
                        int64_t tq, int64_t tk, int64_t hq, int64_t hkv,

@@ -7,7 +7,9 @@
  * the GPU library, and the GPU library never calls it.
  *
  * Everything is f64 and follows the plain definitions:
- *   - HeadPrep: gizml:netops reference page, "Types > HeadPrep".
+ *   - HeadPrep: gizml:netops reference page, "Types > HeadPrep" (split halves, and
+ *     FLUX.3's adjacent pairs);
+ *   - the whole-row norm and rotary: same page, "Functions > rowNormRopeInto".
  *   - attention, causal mask: gizml:netops reference page, "Functions > attention"
  *     and "Functions > causalMask".
  * Layouts are row-major, token rows with heads contiguous inside a row.
@@ -35,6 +37,26 @@ extern "C" {
 int oracle_headprep(double *x, int64_t rows, int64_t heads, int64_t d,
                     const double *w, const double *cos_t, const double *sin_t,
                     int64_t half, int64_t table_rows, const int64_t *pos, double eps);
+
+/*
+ * HeadPrep with the turned values as adjacent pairs (FLUX.3's layout, "even values
+ * first"): pair (2i, 2i+1), i < half, turns by table entry i of the row; values from
+ * 2*half on keep their normalised, weighted value.  Arguments as oracle_headprep.
+ */
+int oracle_headprep_pairs(double *x, int64_t rows, int64_t heads, int64_t d,
+                          const double *w, const double *cos_t, const double *sin_t,
+                          int64_t half, int64_t table_rows, const int64_t *pos, double eps);
+
+/*
+ * LTX's whole-row norm and rotary, in place on x [rows, width] (width a multiple of
+ * head, head even): each row over the RMS of its width values (eps inside the root),
+ * times w[e]; then, if cos_t and sin_t are given ([table_rows, width/2], row pos[row]),
+ * value j < head/2 of each head h turned with value j + head/2 by pair h*head/2 + j.
+ * Returns -1 on a bad size, -2 if a position lies outside [0, table_rows).
+ */
+int oracle_row_norm_rope(double *x, int64_t rows, int64_t width, int64_t head, const double *w,
+                         const double *cos_t, const double *sin_t, int64_t table_rows,
+                         const int64_t *pos, double eps);
 
 /*
  * Scaled-dot-product attention, plain definition.

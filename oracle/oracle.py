@@ -48,6 +48,11 @@ def _load():
                                         _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64, _lp,
                                         ctypes.c_double]
         lib.oracle_headprep.restype = ctypes.c_int
+        lib.oracle_headprep_pairs.argtypes = lib.oracle_headprep.argtypes
+        lib.oracle_headprep_pairs.restype = ctypes.c_int
+        lib.oracle_row_norm_rope.argtypes = [_dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _dp,
+                                             _dp, _dp, ctypes.c_int64, _lp, ctypes.c_double]
+        lib.oracle_row_norm_rope.restype = ctypes.c_int
         att = [_dp, _dp, _dp, _dp] + [ctypes.c_int64] * 7 + [ctypes.c_double, ctypes.c_int, _lp]
         lib.oracle_attention.argtypes = att
         lib.oracle_attention.restype = ctypes.c_int
@@ -75,9 +80,11 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(_lp)
 
 
-def headprep(x, w, cos, sin, half: int, pos, eps: float) -> np.ndarray:
+def headprep(x, w, cos, sin, half: int, pos, eps: float, pairs: bool = False) -> np.ndarray:
     """HeadPrep of x [..., heads, d] (gizml:netops, Types > HeadPrep), returned as a new
-    f64 array.  ``pos`` gives the table row of each leading index (shape x.shape[:-2])."""
+    f64 array.  ``pos`` gives the table row of each leading index (shape x.shape[:-2]).
+    pairs=False: value e < half turns with e + half (split halves); pairs=True: value 2i
+    with 2i + 1 (FLUX.3's pairs, loaded even values first)."""
     x = _f64(x).copy()
     d = x.shape[-1]
     heads = x.shape[-2]
@@ -95,10 +102,33 @@ def headprep(x, w, cos, sin, half: int, pos, eps: float) -> np.ndarray:
         cos = sin = None
         table_rows = 0
         pos = None
-    rc = _load().oracle_headprep(_ptr(x), rows, heads, d, _ptr(w), _ptr(cos), _ptr(sin),
-                                 half, table_rows, _ptr(pos), float(eps))
+    fn = _load().oracle_headprep_pairs if pairs else _load().oracle_headprep
+    rc = fn(_ptr(x), rows, heads, d, _ptr(w), _ptr(cos), _ptr(sin), half, table_rows, _ptr(pos), float(eps))
     if rc != 0:
         raise ValueError("oracle_headprep rejected its arguments (code %d)" % rc)
+    return x
+
+
+def row_norm_rope(x, w, cos, sin, head: int, pos, eps: float) -> np.ndarray:
+    """LTX's whole-row norm and rotary (gizml:netops, Functions > rowNormRopeInto) of
+    x [rows, width], returned as a new f64 array; cos/sin [table_rows, width/2] or None
+    (norm only); ``pos`` the table row of each row."""
+    x = _f64(x).copy()
+    rows, width = x.shape
+    w = _f64(w)
+    assert w.shape == (width,)
+    if cos is not None:
+        cos, sin = _f64(cos), _f64(sin)
+        assert cos.shape == sin.shape and cos.shape[1] == width // 2
+        table_rows = cos.shape[0]
+        pos = np.ascontiguousarray(np.broadcast_to(np.asarray(pos, dtype=np.int64), (rows,)))
+    else:
+        cos = sin = pos = None
+        table_rows = 0
+    rc = _load().oracle_row_norm_rope(_ptr(x), rows, width, head, _ptr(w), _ptr(cos), _ptr(sin), table_rows,
+                                      _ptr(pos), float(eps))
+    if rc != 0:
+        raise ValueError("oracle_row_norm_rope rejected its arguments (code %d)" % rc)
     return x
 
 

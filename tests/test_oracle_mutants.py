@@ -34,6 +34,13 @@ MUTANTS = {
                                 "const int64_t g = h % hkv;"),
     "max not subtracted consistently": ("const double wj = exp(s[j] - m);",
                                         "const double wj = exp(s[j] - m) * (j == 0 ? 2.0 : 1.0);"),
+    "pairs: wrong turn sign": ("x[2 * i + 1] = b * c + a * s;", "x[2 * i + 1] = b * c - a * s;"),
+    "pairs: wrong table entry": ("const double c = cos_row[i], s = sin_row[i];",
+                                 "const double c = cos_row[i / 2], s = sin_row[i / 2];"),
+    "pairs: partner half away": ("const double a = x[2 * i], b = x[2 * i + 1];",
+                                 "const double a = x[2 * i], b = x[i + half];"),
+    "row norm over one head": ("acc /= (double)width;", "acc /= (double)head;"),
+    "row rotary: same angles for every head": ("t = h * half + j;", "t = j;"),
     "value of wrong key": ("const double *vj = v + ((b * tk + j) * hkv + g) * dv;",
                            "const double *vj = v + ((b * tk + (j ? j - 1 : 0)) * hkv + g) * dv;"),
 }

@@ -265,6 +265,93 @@ def test_rows_sample_equals_full():
         np.testing.assert_array_equal(got[r], full[b, i, h])
 
 
+# ----------------------------------------------------- HeadPrep variants (adjacent pairs)
+
+def _even_first(x, half):
+    """Permutation reading the first 2*half values of a head even ones first."""
+    idx = np.concatenate([np.arange(0, 2 * half, 2), np.arange(1, 2 * half, 2), np.arange(2 * half, x.shape[-1])])
+    return idx
+
+
+@pytest.mark.parametrize("d,half", [(16, 8), (16, 5), (8, 0), (64, 32), (64, 24)])
+def test_pairs_are_split_halves_of_the_even_first_reading(d, half):
+    """FLUX.3's pairs "loaded even values first": HeadPrep with adjacent pairs is the
+    split-halves HeadPrep of the values read even ones first (weights read the same
+    way), put back in place."""
+    x = RNG.standard_normal((5, 3, d))
+    w = RNG.uniform(0.5, 1.5, d)
+    cos, sin = _rand_tables(9, half)
+    pos = np.array([0, 8, 3, 5, 1])
+    idx = _even_first(x, half)
+    got = oracle.headprep(x, w, cos, sin, half, pos, 1e-6, pairs=True)
+    ref = np.empty_like(got)
+    ref[..., idx] = oracle.headprep(x[..., idx], w[idx], cos, sin, half, pos, 1e-6)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-14)
+
+
+def test_pairs_turn_is_complex_multiplication():
+    """Pair (2i, 2i+1) as the complex number x_2i + i x_2i+1 times e^{i theta_i}."""
+    d, half = 12, 6
+    x = RNG.standard_normal((4, 2, d))
+    ang = RNG.uniform(-np.pi, np.pi, (4, half))
+    got = oracle.headprep(x, np.ones(d), np.cos(ang), np.sin(ang), half, np.arange(4), 0.0, pairs=True)
+    n = x / np.sqrt((x ** 2).mean(-1, keepdims=True))
+    z = (n[..., 0::2] + 1j * n[..., 1::2]) * np.exp(1j * ang)[:, None, :]
+    np.testing.assert_allclose(got[..., 0::2], z.real, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(got[..., 1::2], z.imag, rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------- whole-row norm and rotary (LTX)
+
+def _rand_tables(rows, half):
+    ang = RNG.uniform(-np.pi, np.pi, (rows, half))
+    return np.cos(ang), np.sin(ang)
+
+
+def test_row_norm_rope_of_one_head_is_headprep():
+    """With width = head the whole-row norm is the head's norm: rowNormRopeInto equals
+    HeadPrep (split halves, half = head / 2) with w as the norm weight."""
+    rows, head = 6, 16
+    x = RNG.standard_normal((rows, head))
+    w = RNG.uniform(0.5, 1.5, head)
+    cos, sin = _rand_tables(10, head // 2)
+    pos = np.array([3, 0, 9, 1, 4, 4])
+    got = oracle.row_norm_rope(x, w, cos, sin, head, pos, 1e-6)
+    ref = oracle.headprep(x[:, None, :], w, cos, sin, head // 2, pos, 1e-6)[:, 0, :]
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-14)
+
+
+def test_row_norm_rope_equal_heads_is_headprep_per_head():
+    """Rows whose heads all have the same sum of squares: the whole-row RMS equals each
+    head's RMS, so every head comes out as HeadPrep with the row's table entries
+    h*head/2 .. of that head (every head turns by its own angles)."""
+    rows, heads, head = 4, 3, 8
+    x = RNG.standard_normal((rows, heads, head))
+    x /= np.sqrt((x ** 2).sum(-1, keepdims=True))          # every head: sum of squares 1
+    w = RNG.uniform(0.5, 1.5, heads * head)
+    cos, sin = _rand_tables(5, heads * head // 2)
+    pos = np.array([4, 2, 0, 1])
+    got = oracle.row_norm_rope(x.reshape(rows, -1), w, cos, sin, head, pos, 1e-6).reshape(rows, heads, head)
+    for h in range(heads):
+        tc, ts = cos[:, h * head // 2:(h + 1) * head // 2], sin[:, h * head // 2:(h + 1) * head // 2]
+        ref = oracle.headprep(x[:, h:h + 1, :], w[h * head:(h + 1) * head], tc, ts, head // 2, pos, 1e-6)
+        np.testing.assert_allclose(got[:, h], ref[:, 0], rtol=0, atol=1e-14)
+
+
+def test_row_norm_unit_rms_and_pair_norms():
+    """Without weight and tables the row comes out with RMS sqrt(ms / (ms + eps)); the
+    turn keeps every (j, j + head/2) pair's norm."""
+    rows, width, head, eps = 5, 48, 16, 1e-3
+    x = RNG.standard_normal((rows, width))
+    ms = (x ** 2).mean(-1)
+    n = oracle.row_norm_rope(x, np.ones(width), None, None, head, None, eps)
+    np.testing.assert_allclose(np.sqrt((n ** 2).mean(-1)), np.sqrt(ms / (ms + eps)), rtol=1e-13)
+    cos, sin = _rand_tables(rows, width // 2)
+    t = oracle.row_norm_rope(x, np.ones(width), cos, sin, head, np.arange(rows), eps)
+    a, b = n.reshape(rows, -1, 2, head // 2), t.reshape(rows, -1, 2, head // 2)
+    np.testing.assert_allclose((b ** 2).sum(2), (a ** 2).sum(2), rtol=1e-12)
+
+
 # -------------------------------------------------------------------------- the path
 
 def test_decode_equals_prefill_row():

@@ -14,7 +14,11 @@ not served from the 256 MB last-level cache.
 After the timed steps: the long prefill workload (batch 1 x 16384 tokens, 64 q / 8 kv
 heads, rotary base 1e6, 1 % outlier key rows), k HeadPrep + attention per call; the
 chunked prefill workload (batch 4: 512 new tokens appended to a 3584-row cache, 32 q / 8
-kv heads, attention over all 4096 rows) per attn_prefill_chunk call; then two
+kv heads, attention over all 4096 rows) per attn_prefill_chunk call; packed rows of an
+image model (attn_rows: 4608 rows of 24 heads of 128, HeadPrep with adjacent pairs in
+place -- repeated calls re-prep the same buffer, which changes values, not work -- then
+full attention); the whole-row norm + per-head rotary of 6240 rows of 4096
+(attn_row_norm_rope, in place, GB/s of one read and one write plus the tables); then two
 calibration kernels (libpeak.so: a bf16 MFMA loop and a streaming read) give measured
 ceilings next to the published ones.
 
@@ -142,6 +146,8 @@ def main() -> int:
     ap.add_argument("--cache-copies", type=int, default=3)
     ap.add_argument("--long-calls", type=int, default=20, help="timed calls of the long prefill (0: skip)")
     ap.add_argument("--chunk-calls", type=int, default=20, help="timed calls of the chunked prefill (0: skip)")
+    ap.add_argument("--rows-calls", type=int, default=20,
+                    help="timed calls of the packed-rows attention and the row norm (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the calibration kernels")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -314,6 +320,68 @@ def main() -> int:
         del q6, kn6, vn6, out6, kc6, vc6
         torch.cuda.empty_cache()
 
+    def time_calls(fn, calls):
+        for _ in range(3):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
+    # ---- packed image-model rows: HeadPrep (adjacent pairs) in place + full attention
+    rows_line = None
+    if args.rows_calls > 0:
+        n7, heads7, head7 = 4608, 24, 128
+        rng7 = np.random.default_rng(7)
+        qkv7 = to(synthetic.bf16_round(rng7.standard_normal((n7, 3 * heads7 * head7))))
+        cos7, sin7 = synthetic.rope_tables(n7, head7 // 2, head7, 1e4)
+        prep7 = tah.HeadPrep(to(rng7.uniform(0.5, 1.5, head7), "f32"), to(rng7.uniform(0.5, 1.5, head7), "f32"),
+                             to(cos7, "f32"), to(sin7, "f32"), 1e-6, pairs=True)
+        out7 = torch.empty(n7, heads7 * head7, dtype=torch.bfloat16, device=dev)
+        ms7 = time_calls(lambda: tah.attn_rows(qkv7, heads7, head7, out=out7, prep=prep7, stream=stream),
+                         args.rows_calls)
+        flops7 = 4 * head7 * n7 * n7 * heads7
+        tf7 = flops7 / (ms7.mean() * 1e-3) / 1e12
+        rows_line = {"workload": "bf16 packed rows of an image model (4608 rows = 4096 image + 512 text, 24 heads "
+                                 "of 128, full attention, HeadPrep with adjacent pairs in place)",
+                     "value": round(tf7, 3), "unit": "TFLOP/s", "calls": args.rows_calls,
+                     "ms": stats_ms(ms7), "flops": flops7, "frac_of_bf16_peak": round(tf7 / PEAK_BF16_TFLOPS, 4)}
+        del qkv7, out7
+        torch.cuda.empty_cache()
+
+    # ---- whole-row norm + per-head rotary of a video model's q (HBM-bound, in place)
+    rownorm_line = None
+    if args.rows_calls > 0:
+        r8, w8, h8 = 6240, 4096, 128
+        rng8 = np.random.default_rng(8)
+        ang8 = rng8.uniform(-np.pi, np.pi, (r8, w8 // 2))
+        wt8 = to(rng8.uniform(0.5, 1.5, w8), "f32")
+        # three copies of rows and tables in turn (613 MB), so no call finds its operands in the
+        # 256 MB last-level cache
+        x8s = [to(synthetic.bf16_round(rng8.standard_normal((r8, w8)))) for _ in range(3)]
+        cos8s = [to(np.cos(ang8), "f32") for _ in range(3)]
+        sin8s = [to(np.sin(ang8), "f32") for _ in range(3)]
+        turn8 = [0]
+
+        def call8():
+            i = turn8[0] % 3
+            turn8[0] += 1
+            tah.attn_row_norm_rope(x8s[i], wt8, 1e-6, cos8s[i], sin8s[i], head=h8, stream=stream)
+
+        ms8 = time_calls(call8, args.rows_calls)
+        bytes8 = r8 * w8 * 2 * 2 + r8 * (w8 // 2) * 4 * 2 + w8 * 4
+        gb8 = bytes8 / (ms8.mean() * 1e-3) / 1e9
+        rownorm_line = {"workload": "bf16 whole-row norm + per-head rotary in place (6240 rows of 4096 = 32 heads "
+                                    "of 128: an 832 x 480, 124-frame video's latent rows)",
+                        "value": round(gb8, 2), "unit": "GB/s", "calls": args.rows_calls, "ms": stats_ms(ms8),
+                        "bytes": bytes8, "frac_of_hbm_peak": round(gb8 / PEAK_HBM_GBPS, 4)}
+        del x8s, cos8s, sin8s
+        torch.cuda.empty_cache()
+
     peaks = None if args.no_peaks else measured_peaks(torch, dev)
 
     line = {
@@ -354,6 +422,10 @@ def main() -> int:
         line["long_prefill"] = long_line
     if chunk_line is not None:
         line["chunk_prefill"] = chunk_line
+    if rows_line is not None:
+        line["image_rows"] = rows_line
+    if rownorm_line is not None:
+        line["row_norm_rope"] = rownorm_line
     if peaks is not None:
         peaks["prefill_attention_frac"] = round(attn_tflops / peaks["mfma_bf16_tflops"], 4)
         peaks["decode_frac"] = round(dec_gbps / peaks["hbm_read_gbps"], 4)

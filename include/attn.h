@@ -74,6 +74,14 @@ typedef enum attn_status {
  *               sin are then not read and may be NULL).
  *   table_rows  number of rows in cos and sin; every position used must be below it.
  *   eps         added to the mean of squares under the root (taken as f32).
+ *   pairs       which values turn together with table entry i < half:
+ *                 0  split halves: value i with value i + half (the HeadPrep above);
+ *                 1  adjacent pairs: value 2i with value 2i + 1, the even value
+ *                    playing a and the odd b (FLUX.3's rotary, gizml:netops, Types >
+ *                    HeadPrep: loaded with its even values first, a head turns as
+ *                    split halves; pairs = 1 takes the head as stored, interleaved).
+ *               Values from 2 * half on keep their normed, weighted value either way.
+ *               A zero-initialised record is the split-halves HeadPrep.
  */
 typedef struct attn_headprep {
     const float *qw;
@@ -83,6 +91,7 @@ typedef struct attn_headprep {
     int64_t half;
     int64_t table_rows;
     double eps;
+    int64_t pairs;
 } attn_headprep_t;
 
 /*
@@ -180,6 +189,55 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
                           const attn_headprep_t *prep, double scale, int64_t splits,
                           void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
                           void *stream);
+
+/*
+ * attn_rows -- full attention of packed rows, for image and video models (gizml:netops,
+ * Functions > attentionRows, its BF16 path, and attendedRows for `queries`).
+ *   qkv      [n, 3 * heads * head]: row r holds q, k and v of `heads` heads of `head`
+ *            values each, in that order; contiguous.  With prep, the q heads of the
+ *            query rows and the k heads of every row are prepped IN PLACE first (row r
+ *            at table row r; prep->pairs selects split halves or adjacent pairs), so
+ *            qkv changes; v is never written.
+ *   group    0: every query sees every row's key.  > 0: the rows form groups of
+ *            `group` consecutive rows (the last may be shorter) and a query sees only
+ *            the keys of its own group (a block-diagonal mask).
+ *   queries  0: every row is a query and out has n rows.  1 .. n: only the first
+ *            `queries` rows are queries (each still sees the keys of its group, which
+ *            may reach past row queries - 1) and out has `queries` rows.
+ *   out      [queries or n, heads * head] contiguous; must not overlap qkv.
+ *   The scale is 1 / sqrt(head); nothing is masked inside a group (no causal mask).
+ *   head in {64, 128} (else ATTN_ERR_UNSUPPORTED); prep->table_rows >= n.  n == 0 is
+ *   a no-op.  Up to three launches are enqueued (prep, the groups wholly made of
+ *   queries, and the group holding the last queries).
+ */
+attn_status_t attn_rows(void *qkv, int64_t n, int64_t heads, int64_t head, int64_t group,
+                        int64_t queries, void *out, const attn_headprep_t *prep,
+                        attn_dtype_t dtype, void *stream);
+
+/*
+ * attn_row_norm_rope -- a norm over the whole row followed by a per-head rotary, in
+ * place (gizml:netops, Functions > rowNormRopeInto: LTX's QK norm, which spans every
+ * head of a row, then its rotary).  For each row r of x:
+ *   x[r, :] = x[r, :] / sqrt(mean over the width of x[r, :]^2 + eps) * w,
+ *   then, if cos is given, each head h of `head` values turned by split halves: value
+ *   d < head / 2 (a) with value d + head / 2 (b) as a' = a c - b s, b' = b c + a s,
+ *   c = cos[r, h * head / 2 + d], s = sin[r, h * head / 2 + d].
+ *   x          [rows, width] with rows row_stride elements apart; 16-byte aligned.
+ *   width      8 <= width <= 8192, a multiple of 8.
+ *   head       a multiple of 8 that divides width.
+ *   row_stride >= width, a multiple of 8.
+ *   w          device f32 [width], 16-byte aligned.
+ *   cos, sin   device f32 [rows, width / 2] (row r serves row r of x), 16-byte aligned;
+ *              both NULL: the norm only.
+ *   eps        finite and >= 0 (taken as f32).
+ *   dtype      storage type of x (the page's kernel is BF16; f32 is offered for exact
+ *              checks); arithmetic is f32, rounded once to the storage type.
+ *   rows == 0 is a no-op.  Errors: ATTN_ERR_ARG for the conditions above or
+ *   rows >= 2^24; ATTN_ERR_UNSUPPORTED for an unknown dtype.
+ */
+attn_status_t attn_row_norm_rope(void *x, int64_t rows, int64_t width, int64_t head,
+                                 int64_t row_stride, const float *w, const float *cos,
+                                 const float *sin, double eps, attn_dtype_t dtype, void *stream);
 
 /* 1 if head dim d and dtype are built into this library, else 0 (asked before
  * allocating, like gpukit's gkd_attention_ok). */

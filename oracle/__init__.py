@@ -13,7 +13,8 @@ chunked prefill against a KV cache, decode):
   FLUX.3's adjacent pairs).
 * the whole-row norm and rotary -- same page, "Functions > rowNormRopeInto".
 * attention and its causal mask -- same page, "Functions > attention" and
-  "Functions > causalMask".
+  "Functions > causalMask"; packed rows with block-diagonal groups -- same page,
+  "Functions > attentionRows" and "Functions > attendedRows".
 * headPrepInPlace's position rule (the table row of a token is its sequence row,
   ``row0`` being the row of the first) -- same page, "Functions > headPrepInPlace".
 """
@@ -26,6 +27,7 @@ from .oracle import (  # noqa: F401
     attention_rows,
     prefill,
     prefill_chunk,
+    attended_rows,
     decode,
     threads,
 )

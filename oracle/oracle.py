@@ -214,6 +214,32 @@ def prefill_chunk(q, k_new, v_new, k_cache, v_cache, n_past: int, qw, kw, cos, s
     return out, kc, vc
 
 
+def attended_rows(qkv, heads: int, head: int, group: int = 0, queries: int = 0, prep=None):
+    """attentionRows / attendedRows (gizml:netops, Functions > attentionRows): qkv [n, 3 heads
+    head] holds each row's q, k and v; with ``prep`` (a dict qw, kw, cos, sin, half, eps and
+    optionally pairs) q and k are prepped first, row r at table row r.  Query row i (the
+    first ``queries`` rows, all when 0) attends the keys of its group of ``group`` rows (all
+    rows when 0) with scale 1/sqrt(head) and no mask inside the group.  Returns (out [nq,
+    heads head], q prepped [n, heads, head], k prepped [n, heads, head]) in f64."""
+    x = _f64(qkv)
+    n = x.shape[0]
+    x = x.reshape(n, 3, heads, head)
+    q, k, v = x[:, 0], x[:, 1], x[:, 2]
+    if prep is not None:
+        pos = np.arange(n, dtype=np.int64)
+        args = (prep["cos"], prep["sin"], prep["half"], pos, prep["eps"])
+        q = headprep(q, prep["qw"], *args, pairs=prep.get("pairs", False))
+        k = headprep(k, prep["kw"], *args, pairs=prep.get("pairs", False))
+    nq = queries if queries else n
+    g = group if 0 < group < n else n
+    out = np.zeros((nq, heads, head), dtype=np.float64)
+    for lo in range(0, nq, g):
+        hi = min(lo + g, n)
+        qhi = min(lo + g, nq)
+        out[lo:qhi] = attention(q[None, lo:qhi], k[None, lo:hi], v[None, lo:hi], 1.0 / np.sqrt(head), False)[0]
+    return out.reshape(nq, heads * head), q, k
+
+
 def decode(q, k_cache, v_cache, lens, pos, qw, cos, sin, half: int, eps: float,
            scale: float) -> np.ndarray:
     """One new query row per sequence: q [B, hq, d] prepped at table row pos[b], then

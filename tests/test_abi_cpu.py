@@ -41,8 +41,8 @@ def test_status_strings(lib):
     assert lib.attn_supported(128, 7) == 0
 
 
-def _prep(half=64, rows=4096, qw=FAKE, kw=FAKE, cos=FAKE, sin=FAKE, eps=1e-6):
-    return A.attn_headprep_t(qw, kw, cos, sin, half, rows, eps)
+def _prep(half=64, rows=4096, qw=FAKE, kw=FAKE, cos=FAKE, sin=FAKE, eps=1e-6, pairs=0):
+    return A.attn_headprep_t(qw, kw, cos, sin, half, rows, eps, pairs)
 
 
 def _prefill(lib, **kw):
@@ -107,6 +107,8 @@ def _prep_call(lib, **kw):
     (dict(prep=_prep(half=32, kw=None)), A.ATTN_ERR_ARG),
     (dict(pos0=4090, prep=_prep(half=32, rows=4096)), A.ATTN_ERR_ARG),
     (dict(k=FAKE + 64), A.ATTN_ERR_ARG),                 # k lands on q's heads
+    (dict(prep=_prep(half=32, pairs=2)), A.ATTN_ERR_ARG),  # pairs is 0 or 1
+    (dict(prep=_prep(half=33, pairs=1)), A.ATTN_ERR_ARG),  # 2 * half > d in either layout
 ])
 def test_prep_rejects(lib, kw, code):
     assert _prep_call(lib, **kw) == code
@@ -218,3 +220,39 @@ def test_peak_library_exports_what_peak_h_declares():
     lib.peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     assert lib.peak_stream_read(FAKE, 1000, FAKE, None) == -1       # not a multiple of 16
     assert lib.peak_stream_read(FAKE + 8, 1024, FAKE, None) == -1   # misaligned
+
+
+def _row_norm(lib, **kw):
+    a = dict(x=FAKE, rows=16, width=2048, head=64, rs=2048, w=FAKE + (1 << 32), cos=FAKE + (2 << 32),
+             sin=FAKE + (3 << 32), eps=1e-6, dtype=A.ATTN_BF16)
+    a.update(kw)
+    return lib.attn_row_norm_rope(a["x"], a["rows"], a["width"], a["head"], a["rs"], a["w"], a["cos"],
+                                  a["sin"], a["eps"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), A.ATTN_ERR_UNSUPPORTED),
+    (dict(x=None), A.ATTN_ERR_ARG),
+    (dict(w=None), A.ATTN_ERR_ARG),
+    (dict(x=FAKE + 8), A.ATTN_ERR_ARG),                  # misaligned
+    (dict(rows=-1), A.ATTN_ERR_ARG),
+    (dict(width=2044, rs=2048), A.ATTN_ERR_ARG),         # width not a multiple of 8
+    (dict(width=16384, rs=16384), A.ATTN_ERR_ARG),       # wider than 8192
+    (dict(head=60), A.ATTN_ERR_ARG),                     # head not a multiple of 8
+    (dict(head=96), A.ATTN_ERR_ARG),                     # head does not divide width
+    (dict(rs=2040), A.ATTN_ERR_ARG),                     # stride below the width
+    (dict(rs=2052), A.ATTN_ERR_ARG),                     # stride not a multiple of 8
+    (dict(sin=None), A.ATTN_ERR_ARG),                    # cos without sin
+    (dict(cos=FAKE + (2 << 32) + 4), A.ATTN_ERR_ARG),    # misaligned table
+    (dict(eps=-1.0), A.ATTN_ERR_ARG),
+    (dict(eps=float("inf")), A.ATTN_ERR_ARG),
+    (dict(rows=1 << 24), A.ATTN_ERR_ARG),
+])
+def test_row_norm_rope_rejects(lib, kw, code):
+    assert _row_norm(lib, **kw) == code
+    assert lib.attn_last_error()
+
+
+def test_row_norm_rope_empty_is_a_no_op(lib):
+    assert _row_norm(lib, rows=0) == A.ATTN_OK
+    assert _row_norm(lib, rows=0, cos=None, sin=None) == A.ATTN_OK

@@ -439,6 +439,44 @@ def test_tiny_workload_end_to_end_against_library_routines():
     np.testing.assert_allclose(out, ref.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-13)
 
 
+# ------------------------------------------------------------ packed rows with groups
+
+@pytest.mark.parametrize("n,group,queries", [(11, 0, 0), (11, 4, 0), (11, 4, 6), (12, 3, 12), (9, 20, 5)])
+def test_attended_rows_is_block_diagonal_sdpa(n, group, queries):
+    """attentionRows' groups: torch SDPA over all n rows with an explicit block-diagonal
+    boolean mask (query i sees key j iff i // group == j // group), scale 1/sqrt(head),
+    after torch rms_norm + complex turn of q and k at table row r; out keeps the first
+    `queries` rows."""
+    heads, head, half = 2, 8, 4
+    rng = np.random.default_rng(n * 100 + group * 10 + queries)
+    qkv = rng.standard_normal((n, 3 * heads * head))
+    qw, kw = rng.uniform(0.5, 1.5, head), rng.uniform(0.5, 1.5, head)
+    cos, sin = _angles_tables(n, half, head)
+    prep = dict(qw=qw, kw=kw, cos=cos, sin=sin, half=half, eps=1e-6)
+    out, qh, kh = oracle.attended_rows(qkv, heads, head, group, queries, prep)
+
+    x = qkv.reshape(n, 3, heads, head)
+
+    def turn(y, wt):
+        m = _torch_rmsnorm(y, wt, 1e-6)
+        z = (m[..., :half] + 1j * m[..., half:]) * (cos + 1j * sin)[:, None, :]
+        return np.concatenate([z.real, z.imag], axis=-1)
+
+    q_ref, k_ref = turn(x[:, 0], qw), turn(x[:, 1], kw)
+    np.testing.assert_allclose(qh, q_ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(kh, k_ref, rtol=0, atol=1e-13)
+    g = group if group else n
+    idx = np.arange(n)
+    mask = (idx[:, None] // g) == (idx[None, :] // g)
+    ref = F.scaled_dot_product_attention(
+        torch.from_numpy(q_ref).permute(1, 0, 2), torch.from_numpy(k_ref).permute(1, 0, 2),
+        torch.from_numpy(x[:, 2].copy()).permute(1, 0, 2), attn_mask=torch.from_numpy(mask),
+        scale=1 / math.sqrt(head)).permute(1, 0, 2).reshape(n, heads * head).numpy()
+    nq = queries if queries else n
+    assert out.shape == (nq, heads * head)
+    np.testing.assert_allclose(out, ref[:nq], rtol=0, atol=1e-13)
+
+
 # ------------------------------------------------------------------- input generation
 
 def test_bf16_rounding_matches_torch():

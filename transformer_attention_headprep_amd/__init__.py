@@ -13,6 +13,8 @@ from .attn import (  # noqa: F401
     attn_prefill,
     attn_prefill_chunk,
     attn_prep,
+    attn_row_norm_rope,
+    attn_rows,
     attn_supported,
     decode_default_splits,
     decode_workspace_size,

@@ -21,7 +21,8 @@ ATTN_OK, ATTN_ERR_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 
 
 # The entry points include/attn.h declares (checked by the CPU test suite).
 EXPORTS = ("attn_prep", "attn_prefill", "attn_prefill_chunk", "attn_decode", "attn_decode_workspace_size",
-           "attn_decode_default_splits", "attn_supported", "attn_status_str", "attn_last_error")
+           "attn_decode_default_splits", "attn_rows", "attn_row_norm_rope", "attn_supported", "attn_status_str",
+           "attn_last_error")
 
 
 class AttnError(RuntimeError):
@@ -33,7 +34,7 @@ class AttnError(RuntimeError):
 class attn_headprep_t(ctypes.Structure):
     _fields_ = [("qw", ctypes.c_void_p), ("kw", ctypes.c_void_p), ("cos", ctypes.c_void_p),
                 ("sin", ctypes.c_void_p), ("half", ctypes.c_int64), ("table_rows", ctypes.c_int64),
-                ("eps", ctypes.c_double)]
+                ("eps", ctypes.c_double), ("pairs", ctypes.c_int64)]
 
 
 _lib = None
@@ -65,6 +66,10 @@ def load_library(path: str = LIB_PATH):
     lib.attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.attn_decode_default_splits.argtypes = [_i64] * 4
     lib.attn_decode_default_splits.restype = _i64
+    lib.attn_rows.argtypes = [_vp] + [_i64] * 5 + [_vp, hp, ctypes.c_int, _vp]
+    lib.attn_rows.restype = ctypes.c_int
+    lib.attn_row_norm_rope.argtypes = [_vp] + [_i64] * 4 + [_vp, _vp, _vp, _dbl, ctypes.c_int, _vp]
+    lib.attn_row_norm_rope.restype = ctypes.c_int
     lib.attn_supported.argtypes = [_i64, ctypes.c_int]
     lib.attn_supported.restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
@@ -114,12 +119,14 @@ def _row_stride(t: torch.Tensor, name: str) -> int:
 
 @dataclass
 class HeadPrep:
-    """The HeadPrep record {qw, kw, cos, sin, eps} as device f32 tensors."""
+    """The HeadPrep record {qw, kw, cos, sin, eps} as device f32 tensors; pairs=True turns
+    adjacent values (2i, 2i + 1) rather than split halves (i, i + half)."""
     qw: torch.Tensor
     kw: torch.Tensor
     cos: torch.Tensor | None
     sin: torch.Tensor | None
     eps: float
+    pairs: bool = False
 
     @property
     def half(self) -> int:
@@ -135,7 +142,7 @@ class HeadPrep:
             self.qw.data_ptr() if self.qw is not None else None,
             self.kw.data_ptr() if self.kw is not None else None,
             self.cos.data_ptr() if half else None, self.sin.data_ptr() if half else None,
-            half, int(self.cos.shape[0]) if half else 0, float(self.eps))
+            half, int(self.cos.shape[0]) if half else 0, float(self.eps), int(bool(self.pairs)))
 
 
 def attn_supported(d: int, dtype: torch.dtype) -> bool:
@@ -203,6 +210,47 @@ def attn_prefill_chunk(q, k_new, v_new, k_cache, v_cache, n_past: int, out=None,
                                   ctypes.byref(st) if st is not None else None, int(bool(causal)),
                                   float(scale), _dtype_code(q), _stream(stream)))
     return out
+
+
+def attn_rows(qkv, heads: int, head: int, group: int = 0, queries: int = 0, out=None,
+              prep: HeadPrep | None = None, stream=None) -> torch.Tensor:
+    """Full attention of packed rows qkv [n, 3 * heads * head] (q, k, v of every head), each
+    query seeing the keys of its group of `group` rows (0: all); out [queries or n, heads * head].
+    With prep, q and k are prepped in place in qkv first (row r at table row r)."""
+    lib = load_library()
+    if qkv.dim() != 2 or not qkv.is_contiguous() or qkv.shape[1] != 3 * heads * head:
+        raise ValueError("qkv must be a contiguous [n, 3 * heads * head] tensor")
+    n = qkv.shape[0]
+    nq = queries if queries else n
+    if out is None:
+        out = torch.empty(nq, heads * head, dtype=qkv.dtype, device=qkv.device)
+    if out.dtype != qkv.dtype or not out.is_contiguous() or tuple(out.shape) != (nq, heads * head):
+        raise ValueError("out must be a contiguous [queries or n, heads * head] tensor of qkv's dtype")
+    st = prep.struct() if prep is not None else None
+    _check(lib.attn_rows(_ptr(qkv), n, heads, head, group, queries, _ptr(out),
+                         ctypes.byref(st) if st is not None else None, _dtype_code(qkv), _stream(stream)))
+    return out
+
+
+def attn_row_norm_rope(x, w, eps: float, cos=None, sin=None, head: int | None = None, stream=None) -> None:
+    """In place on x [rows, width] (row-strided, values contiguous): whole-row RMS norm times w,
+    then with cos/sin [rows, width / 2] each head of `head` values turned by split halves."""
+    lib = load_library()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [rows, width] with contiguous rows")
+    rows, width = x.shape
+    for name, t in (("w", w), ("cos", cos), ("sin", sin)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("%s must be a contiguous float32 tensor" % name)
+    if cos is not None and tuple(cos.shape) != (rows, width // 2):
+        raise ValueError("cos/sin must be [rows, width / 2]")
+    if (cos is None) != (sin is None) or (sin is not None and sin.shape != cos.shape):
+        raise ValueError("cos and sin go together, of one shape")
+    if head is None:
+        head = width
+    rs = x.stride(0) if rows > 1 else width
+    _check(lib.attn_row_norm_rope(_ptr(x), rows, width, head, rs, _ptr(w), _ptr(cos), _ptr(sin), float(eps),
+                                  _dtype_code(x), _stream(stream)))
 
 
 def decode_workspace_size(batch: int, hq: int, hkv: int, d: int, max_len: int, splits: int = 0) -> int:

@@ -6,6 +6,7 @@
 // wrappers).  Nothing here allocates or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -70,6 +71,7 @@ attn_status_t check_prep(const attn_headprep_t *p, int64_t d, bool need_qw, bool
     if ((need_qw && !aligned16(p->qw)) || (need_kw && !aligned16(p->kw)))
         return fail(ATTN_ERR_ARG, "prep weights are not 16-byte aligned");
     if (!(p->eps >= 0.0) || !std::isfinite(p->eps)) return fail(ATTN_ERR_ARG, "prep->eps must be finite and >= 0");
+    if (p->pairs != 0 && p->pairs != 1) return fail(ATTN_ERR_ARG, "prep->pairs = %lld not 0 or 1", (long long)p->pairs);
     if (p->half < 0 || 2 * p->half > d)
         return fail(ATTN_ERR_ARG, "prep->half = %lld outside [0, d/2]", (long long)p->half);
     if (p->half > 0) {
@@ -133,7 +135,7 @@ attn_status_t attn_prep(void *q, void *k, int64_t batch, int64_t seq, int64_t hq
     a.k_src = k; a.k_dst = k; a.k_src_rs = k_row_stride; a.k_dst_rs = k_row_stride; a.hkv = hkv;
     a.batch = batch; a.seq = seq; a.d = d; a.pos0 = pos0;
     a.qw = prep->qw; a.kw = prep->kw; a.cos = prep->cos; a.sin = prep->sin;
-    a.half = prep->half; a.eps = (float)prep->eps; a.bf16 = dtype == ATTN_BF16;
+    a.half = prep->half; a.pairs = prep->pairs != 0; a.eps = (float)prep->eps; a.bf16 = dtype == ATTN_BF16;
     return hip_status(attn::launch_prep(a, static_cast<hipStream_t>(stream)), "attn_prep");
 }
 
@@ -174,7 +176,7 @@ attn_status_t attn_prefill(const void *q, void *k, const void *v, void *out, int
     a.batch = batch; a.seq = seq; a.hq = hq; a.hkv = hkv; a.d = d; a.pos0 = pos0;
     a.causal = causal != 0; a.scale = (float)scale; a.bf16 = bf16;
     if (prep) {
-        const bool fused = attn::prefill_fuses_half(d, prep->half, bf16);
+        const bool fused = !prep->pairs && attn::prefill_fuses_half(d, prep->half, bf16);
         // k is prepped in place; q either in the attention prologue or, for halves the
         // prologue cannot turn, into `out` first (each attention block then reads its
         // q rows from out before it overwrites exactly those rows).
@@ -188,7 +190,7 @@ attn_status_t attn_prefill(const void *q, void *k, const void *v, void *out, int
         }
         pa.batch = batch; pa.seq = seq; pa.d = d; pa.pos0 = pos0;
         pa.qw = prep->qw; pa.kw = prep->kw; pa.cos = prep->cos; pa.sin = prep->sin;
-        pa.half = prep->half; pa.eps = (float)prep->eps; pa.bf16 = bf16;
+        pa.half = prep->half; pa.pairs = prep->pairs != 0; pa.eps = (float)prep->eps; pa.bf16 = bf16;
         if (pa.k_src || pa.q_src)
             if ((st = hip_status(attn::launch_prep(pa, s), "attn_prefill (prep)"))) return st;
         if (fused) {
@@ -255,7 +257,7 @@ attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v
         pk.k_src_bs = tq * crs; pk.k_dst_bs = cbs;
         pk.batch = batch; pk.seq = tq; pk.d = d; pk.pos0 = n_past;
         pk.qw = prep->qw; pk.kw = prep->kw; pk.cos = prep->cos; pk.sin = prep->sin;
-        pk.half = prep->half; pk.eps = (float)prep->eps; pk.bf16 = bf16;
+        pk.half = prep->half; pk.pairs = prep->pairs != 0; pk.eps = (float)prep->eps; pk.bf16 = bf16;
         if ((st = hip_status(attn::launch_prep(pk, s), "attn_prefill_chunk (k prep)"))) return st;
     } else {
         attn::CopyRowsLaunch ck = cv;
@@ -272,7 +274,7 @@ attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v
     a.batch = batch; a.seq = tq; a.tk = n_past + tq; a.hq = hq; a.hkv = hkv; a.d = d; a.pos0 = n_past;
     a.causal = causal != 0; a.scale = (float)scale; a.bf16 = bf16;
     if (prep) {
-        if (attn::prefill_fuses_half(d, prep->half, bf16)) {
+        if (!prep->pairs && attn::prefill_fuses_half(d, prep->half, bf16)) {
             a.prep_q = true;
             a.qw = prep->qw; a.cos = prep->cos; a.sin = prep->sin; a.half = prep->half; a.eps = (float)prep->eps;
         } else {
@@ -281,12 +283,108 @@ attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v
             pq.q_src = q; pq.q_dst = out; pq.q_src_rs = hq * d; pq.q_dst_rs = hq * d; pq.hq = hq;
             pq.batch = batch; pq.seq = tq; pq.d = d; pq.pos0 = n_past;
             pq.qw = prep->qw; pq.cos = prep->cos; pq.sin = prep->sin;
-            pq.half = prep->half; pq.eps = (float)prep->eps; pq.bf16 = bf16;
+            pq.half = prep->half; pq.pairs = prep->pairs != 0; pq.eps = (float)prep->eps; pq.bf16 = bf16;
             if ((st = hip_status(attn::launch_prep(pq, s), "attn_prefill_chunk (q prep)"))) return st;
             a.q = out;
         }
     }
     return hip_status(attn::launch_prefill(a, s), "attn_prefill_chunk");
+}
+
+attn_status_t attn_rows(void *qkv, int64_t n, int64_t heads, int64_t head, int64_t group, int64_t queries, void *out,
+                        const attn_headprep_t *prep, attn_dtype_t dtype, void *stream) {
+    g_last_error[0] = 0;
+    attn_status_t st = check_dtype_d(dtype, head);
+    if (st) return st;
+    if (n < 0) return fail(ATTN_ERR_ARG, "n < 0");
+    if (heads <= 0) return fail(ATTN_ERR_ARG, "heads <= 0");
+    const int64_t rs = 3 * heads * head, ors = heads * head;
+    if ((st = check_rows("qkv", qkv, 3 * heads, head, rs))) return st;
+    if ((st = check_rows("out", out, heads, head, ors))) return st;
+    if (group < 0) return fail(ATTN_ERR_ARG, "group < 0");
+    if (queries < 0 || queries > n) return fail(ATTN_ERR_ARG, "queries %lld outside [0, n = %lld]", (long long)queries, (long long)n);
+    if (prep && (st = check_prep(prep, head, true, true, 0, n))) return st;
+    if (n == 0) return ATTN_OK;
+    const int64_t nq = queries ? queries : n;
+    const int64_t G = (group == 0 || group > n) ? n : group;
+    if (n >= ((int64_t)1 << 31) || ((G + 127) / 128) * ((nq + G - 1) / G) * heads >= ((int64_t)1 << 31))
+        return fail(ATTN_ERR_ARG, "problem too large for one launch");
+    const size_t es = elem_size(dtype);
+    if (overlap(span(out, nq, ors, heads, head, es), span(qkv, n, rs, 3 * heads, head, es)))
+        return fail(ATTN_ERR_ARG, "out overlaps qkv");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf16 = dtype == ATTN_BF16;
+    uint8_t *base = static_cast<uint8_t *>(qkv);
+    void *qp = base, *kp = base + (size_t)(heads * head) * es, *vp = base + (size_t)(2 * heads * head) * es;
+
+    // HeadPrep in place first: q of the query rows, k of every row, row r at table row r.
+    if (prep) {
+        attn::PrepLaunch pa{};
+        pa.k_src = kp; pa.k_dst = kp; pa.k_src_rs = rs; pa.k_dst_rs = rs; pa.hkv = heads;
+        pa.batch = 1; pa.seq = n; pa.d = head; pa.pos0 = 0;
+        pa.qw = prep->qw; pa.kw = prep->kw; pa.cos = prep->cos; pa.sin = prep->sin;
+        pa.half = prep->half; pa.pairs = prep->pairs != 0; pa.eps = (float)prep->eps; pa.bf16 = bf16;
+        attn::PrepLaunch pq = pa;
+        pq.k_src = nullptr; pq.k_dst = nullptr;
+        pq.q_src = qp; pq.q_dst = qp; pq.q_src_rs = rs; pq.q_dst_rs = rs; pq.hq = heads; pq.seq = nq;
+        if (nq == n) {   // one launch for both
+            pa.q_src = qp; pa.q_dst = qp; pa.q_src_rs = rs; pa.q_dst_rs = rs; pa.hq = heads;
+        } else if ((st = hip_status(attn::launch_prep(pq, s), "attn_rows (q prep)"))) {
+            return st;
+        }
+        if ((st = hip_status(attn::launch_prep(pa, s), "attn_rows (prep)"))) return st;
+    }
+
+    // Full attention inside each group of G rows: the groups whose rows are all queries
+    // form one batched launch; the queries left over (the start of the next group) attend
+    // that group's keys in a second one.
+    attn::PrefillLaunch a{};
+    a.q_rs = rs; a.k_rs = rs; a.v_rs = rs; a.o_rs = ors;
+    a.hq = heads; a.hkv = heads; a.d = head; a.causal = false; a.bf16 = bf16;
+    a.scale = (float)(1.0 / std::sqrt((double)head));
+    const int64_t full = nq / G;
+    if (full > 0) {
+        attn::PrefillLaunch f = a;
+        f.q = qp; f.k = kp; f.v = vp; f.out = out;
+        f.q_bs = G * rs; f.k_bs = G * rs; f.v_bs = G * rs; f.o_bs = G * ors;
+        f.batch = full; f.seq = G; f.tk = G;
+        if ((st = hip_status(attn::launch_prefill(f, s), "attn_rows"))) return st;
+    }
+    const int64_t r0 = full * G, tq = nq - r0;
+    if (tq > 0) {
+        attn::PrefillLaunch t = a;
+        const size_t off = (size_t)(r0 * rs) * es;
+        t.q = base + off; t.k = static_cast<uint8_t *>(kp) + off; t.v = static_cast<uint8_t *>(vp) + off;
+        t.out = static_cast<uint8_t *>(out) + (size_t)(r0 * ors) * es;
+        t.batch = 1; t.seq = tq; t.tk = std::min(G, n - r0);
+        if ((st = hip_status(attn::launch_prefill(t, s), "attn_rows (tail)"))) return st;
+    }
+    return ATTN_OK;
+}
+
+attn_status_t attn_row_norm_rope(void *x, int64_t rows, int64_t width, int64_t head, int64_t row_stride,
+                                 const float *w, const float *cos, const float *sin, double eps, attn_dtype_t dtype,
+                                 void *stream) {
+    g_last_error[0] = 0;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    if (!x || !w) return fail(ATTN_ERR_ARG, "x or w is NULL");
+    if (!aligned16(x) || !aligned16(w)) return fail(ATTN_ERR_ARG, "x or w is not 16-byte aligned");
+    if (rows < 0) return fail(ATTN_ERR_ARG, "rows < 0");
+    if (width < 8 || width > 8192 || width % 8 != 0)
+        return fail(ATTN_ERR_ARG, "width %lld not a multiple of 8 in [8, 8192]", (long long)width);
+    if (head < 8 || head % 8 != 0 || width % head != 0)
+        return fail(ATTN_ERR_ARG, "head %lld not a multiple of 8 dividing width %lld", (long long)head, (long long)width);
+    if (row_stride < width || row_stride % 8 != 0 || row_stride >= ((int64_t)1 << 31))
+        return fail(ATTN_ERR_ARG, "row stride %lld not a multiple of 8 in [width, 2^31)", (long long)row_stride);
+    if ((cos == nullptr) != (sin == nullptr)) return fail(ATTN_ERR_ARG, "cos and sin must both be given or both NULL");
+    if (cos && (!aligned16(cos) || !aligned16(sin))) return fail(ATTN_ERR_ARG, "cos/sin not 16-byte aligned");
+    if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(ATTN_ERR_ARG, "eps must be finite and >= 0");
+    if (rows >= ((int64_t)1 << 24)) return fail(ATTN_ERR_ARG, "rows %lld >= 2^24", (long long)rows);
+    if (rows == 0) return ATTN_OK;
+    attn::RowNormRopeLaunch a{};
+    a.x = x; a.rows = rows; a.width = width; a.head = head; a.rs = row_stride;
+    a.w = w; a.cos = cos; a.sin = sin; a.eps = (float)eps; a.bf16 = dtype == ATTN_BF16;
+    return hip_status(attn::launch_row_norm_rope(a, static_cast<hipStream_t>(stream)), "attn_row_norm_rope");
 }
 
 int64_t attn_decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len) {
@@ -351,7 +449,7 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
     a.prep_q = prep != nullptr;
     if (prep) {
         a.qw = prep->qw; a.cos = prep->cos; a.sin = prep->sin; a.half = prep->half;
-        a.table_rows = prep->table_rows; a.eps = (float)prep->eps;
+        a.table_rows = prep->table_rows; a.pairs = prep->pairs != 0; a.eps = (float)prep->eps;
     }
     a.scale = (float)scale; a.splits = splits; a.work = static_cast<float *>(workspace);
     a.bf16 = dtype == ATTN_BF16;

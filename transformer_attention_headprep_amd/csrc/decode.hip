@@ -50,7 +50,7 @@ struct DecodeParams {
     const float *qw, *cos, *sin;
     int half, table_rows, group, ngroups;
     float eps, C;
-    bool prep_q;
+    bool prep_q, pairs;
 };
 
 // Block coordinates: the kv-head groups of one (sequence, split) are consecutive block
@@ -110,7 +110,13 @@ __device__ void q_prologue(const DecodeParams &p, int b, int h0, int nh, float (
         for (int idx = tid; idx < GB * D; idx += kThreads) {
             const int hh = idx / D, e = idx % D;
             float y = qs[hh][e];
-            if (e < p.half) {
+            if (p.pairs) {       // adjacent pairs (2j, 2j + 1), table entry j
+                const int j = e >> 1;
+                if (j < p.half) {
+                    const float c = p.cos[(int64_t)prow * p.half + j], s = p.sin[(int64_t)prow * p.half + j];
+                    y = (e & 1) ? qs[hh][e] * c + qs[hh][e - 1] * s : qs[hh][e] * c - qs[hh][e + 1] * s;
+                }
+            } else if (e < p.half) {
                 const float c = p.cos[(int64_t)prow * p.half + e], s = p.sin[(int64_t)prow * p.half + e];
                 y = qs[hh][e] * c - qs[hh][e + p.half] * s;
             } else if (e < 2 * p.half) {
@@ -636,6 +642,7 @@ hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream) {
     p.eps = a.eps;
     p.C = a.scale * kLog2e;
     p.prep_q = a.prep_q;
+    p.pairs = a.prep_q && a.pairs;
     if (a.d == 64) {
         if (a.bf16) launch_split_gb<true, 64>(p, gb, stream); else launch_split_gb<false, 64>(p, gb, stream);
     } else {

@@ -20,6 +20,7 @@ struct PrepLaunch {
     int64_t batch, seq, d, pos0;
     const float *qw, *kw, *cos, *sin;
     int64_t half;
+    bool pairs;                  // turn adjacent pairs (2i, 2i + 1) rather than split halves
     float eps;
     bool bf16;
 };
@@ -50,6 +51,19 @@ bool prefill_fuses_half(int64_t d, int64_t half, bool bf16);
 // Fill the zero batch strides and tk of a prefill launch with their defaults.
 void prefill_defaults(PrefillLaunch &a);
 
+// Whole-row RMS norm (eps) times w [width], then with cos/sin [rows, width / 2] each
+// head of `head` values turned by split halves at table entry h * head / 2 + d of its
+// row; in place on `rows` rows `rs` elements apart.  width % 8 == 0, width <= 8192,
+// head % 8 == 0 and divides width (checked by the caller).
+struct RowNormRopeLaunch {
+    void *x;
+    int64_t rows, width, head, rs;
+    const float *w, *cos, *sin;  // cos == NULL: norm only
+    float eps;
+    bool bf16;
+};
+hipError_t launch_row_norm_rope(const RowNormRopeLaunch &a, hipStream_t stream);
+
 // Copy `rows` rows of `row_elems` elements of `batch` sequences (16-byte multiples,
 // 16-byte aligned): row t of sequence b from src + b * src_bs + t * src_rs to
 // dst + b * dst_bs + t * dst_rs (strides in elements of `elem` bytes).
@@ -67,6 +81,7 @@ struct DecodeLaunch {
     bool prep_q;
     const float *qw, *cos, *sin;
     int64_t half, table_rows;
+    bool pairs;                  // turn adjacent pairs (2i, 2i + 1) rather than split halves
     float eps;
     float scale;
     int64_t splits;

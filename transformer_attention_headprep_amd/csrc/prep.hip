@@ -9,7 +9,8 @@
 // coalescing: d/8 consecutive lanes own one head, lane i holding the 4 values at
 // 4i.. and the 4 values at d/2 + 4i.., so each wave reads 2 x 64 contiguous 8-byte
 // (bf16) or 16-byte (f32) pieces and, when half = d/2, every turned pair sits in one
-// lane.  Other halves go through LDS.
+// lane.  Other halves go through LDS.  Adjacent pairs (2i, 2i + 1: FLUX.3's layout)
+// always sit in one lane, whatever half is.
 #include <algorithm>
 
 #include "common.h"
@@ -29,6 +30,21 @@ struct PrepParams {
     int half;
     float eps;
 };
+
+// Turn the adjacent pairs (e, e + 1), e even, of 4 values starting at e0 (a multiple of
+// 4) by table entries e / 2 < half of row `crow` / `srow`.
+__device__ __forceinline__ void turn_pairs4(float (&x)[4], int e0, int half, const float *crow,
+                                            const float *srow) {
+#pragma unroll
+    for (int i = 0; i < 4; i += 2) {
+        const int j = (e0 + i) / 2;
+        if (j < half) {
+            const float c = crow[j], s = srow[j], a = x[i], b = x[i + 1];
+            x[i] = a * c - b * s;
+            x[i + 1] = b * c + a * s;
+        }
+    }
+}
 
 template <bool BF16>
 __device__ __forceinline__ void load4(const void *base, int64_t off, float (&x)[4]) {
@@ -55,7 +71,8 @@ __device__ __forceinline__ void store4(void *base, int64_t off, const float (&x)
     }
 }
 
-// MODE 0: no turn (half = 0); MODE 1: half = d/2, pairs in-lane; MODE 2: any half, via LDS.
+// MODE 0: no turn (half = 0); MODE 1: half = d/2, pairs in-lane; MODE 2: any half, via LDS;
+// MODE 3: adjacent pairs, any half, in-lane.
 template <bool BF16, int D, int MODE>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepParams p) {
     constexpr int LPH = D / 8;                  // lanes per head
@@ -109,7 +126,13 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepParams p) 
     }
     const int64_t posrow = p.pos0 + row % p.seq;
 
-    if constexpr (MODE == 1) {
+    if constexpr (MODE == 3) {
+        if (valid) {
+            const float *crow = p.cos + posrow * p.half, *srow = p.sin + posrow * p.half;
+            turn_pairs4(lo, e_lo, p.half, crow, srow);
+            turn_pairs4(hi, e_hi, p.half, crow, srow);
+        }
+    } else if constexpr (MODE == 1) {
         if (valid) {
             const float4 c = *reinterpret_cast<const float4 *>(p.cos + posrow * (D / 2) + e_lo);
             const float4 s = *reinterpret_cast<const float4 *>(p.sin + posrow * (D / 2) + e_lo);
@@ -162,8 +185,10 @@ hipError_t launch_prep_d(const PrepParams &p, int mode, hipStream_t stream) {
         hipLaunchKernelGGL((prep_kernel<BF16, D, 0>), dim3(blocks), dim3(kPrepThreads), 0, stream, p);
     else if (mode == 1)
         hipLaunchKernelGGL((prep_kernel<BF16, D, 1>), dim3(blocks), dim3(kPrepThreads), 0, stream, p);
-    else
+    else if (mode == 2)
         hipLaunchKernelGGL((prep_kernel<BF16, D, 2>), dim3(blocks), dim3(kPrepThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((prep_kernel<BF16, D, 3>), dim3(blocks), dim3(kPrepThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -180,7 +205,97 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const uint8_t *src, uint
     }
 }
 
+// Whole-row norm and per-head rotary (gizml:netops, Functions > rowNormRopeInto): one
+// block per row.  A unit is 4 values at h * head + 4i and the 4 at h * head + head / 2 +
+// 4i (the same lane layout as the HeadPrep kernel, so the turned pairs sit in one lane);
+// thread t owns units t, t + 256, ...; the row's sum of squares is reduced over the block.
+struct RowNormParams {
+    void *x; int64_t rs;
+    int width, head;
+    const float *w, *cos, *sin;
+    float eps;
+};
+
+template <bool BF16, int NPT>
+__global__ __launch_bounds__(256) void row_norm_rope_kernel(const RowNormParams p) {
+    __shared__ float part[4];
+    const int64_t r = blockIdx.x;
+    const int units = p.width / 8, hu = p.head / 8, halfh = p.head / 2;
+    const int64_t base = r * p.rs;
+    float lo[NPT][4], hi[NPT][4];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+        const int u = threadIdx.x + 256 * k;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo[k][i] = hi[k][i] = 0.f;
+        if (u < units) {
+            const int e = (u / hu) * p.head + 4 * (u % hu);
+            load4<BF16>(p.x, base + e, lo[k]);
+            load4<BF16>(p.x, base + e + halfh, hi[k]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss += lo[k][i] * lo[k][i] + hi[k][i] * hi[k][i];
+    }
+    ss = sum_lanes<64>(ss);
+    if (threadIdx.x % 64 == 0) part[threadIdx.x / 64] = ss;
+    __syncthreads();
+    ss = (part[0] + part[1]) + (part[2] + part[3]);
+    const float inv = 1.0f / __builtin_sqrtf(ss / (float)p.width + p.eps);
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+        const int u = threadIdx.x + 256 * k;
+        if (u >= units) continue;
+        const int h = u / hu, li = u % hu;
+        const int e = h * p.head + 4 * li;
+        const float4 wl = *reinterpret_cast<const float4 *>(p.w + e);
+        const float4 wh = *reinterpret_cast<const float4 *>(p.w + e + halfh);
+        const float wlo[4] = {wl.x, wl.y, wl.z, wl.w}, whi[4] = {wh.x, wh.y, wh.z, wh.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            lo[k][i] = lo[k][i] * inv * wlo[i];
+            hi[k][i] = hi[k][i] * inv * whi[i];
+        }
+        if (p.cos) {
+            // pair h * head / 2 + d of the row's table entry, d = 4 li + i
+            const int64_t t = r * (p.width / 2) + h * halfh + 4 * li;
+            const float4 c = *reinterpret_cast<const float4 *>(p.cos + t);
+            const float4 sn = *reinterpret_cast<const float4 *>(p.sin + t);
+            const float cc[4] = {c.x, c.y, c.z, c.w}, sc[4] = {sn.x, sn.y, sn.z, sn.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float a = lo[k][i], b = hi[k][i];
+                lo[k][i] = a * cc[i] - b * sc[i];
+                hi[k][i] = b * cc[i] + a * sc[i];
+            }
+        }
+        store4<BF16>(p.x, base + e, lo[k]);
+        store4<BF16>(p.x, base + e + halfh, hi[k]);
+    }
+}
+
+template <bool BF16>
+void launch_row_norm_npt(const RowNormParams &p, int64_t rows, hipStream_t stream) {
+    const int units = p.width / 8;
+    const dim3 grid((unsigned)rows);
+    if (units <= 256)
+        hipLaunchKernelGGL((row_norm_rope_kernel<BF16, 1>), grid, dim3(256), 0, stream, p);
+    else if (units <= 512)
+        hipLaunchKernelGGL((row_norm_rope_kernel<BF16, 2>), grid, dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((row_norm_rope_kernel<BF16, 4>), grid, dim3(256), 0, stream, p);
+}
+
 }  // namespace
+
+hipError_t launch_row_norm_rope(const RowNormRopeLaunch &a, hipStream_t stream) {
+    if (a.rows == 0) return hipSuccess;
+    RowNormParams p;
+    p.x = a.x; p.rs = a.rs; p.width = (int)a.width; p.head = (int)a.head;
+    p.w = a.w; p.cos = a.cos; p.sin = a.sin; p.eps = a.eps;
+    if (a.bf16) launch_row_norm_npt<true>(p, a.rows, stream); else launch_row_norm_npt<false>(p, a.rows, stream);
+    return hipGetLastError();
+}
 
 hipError_t launch_copy_rows(const CopyRowsLaunch &a, hipStream_t stream) {
     const int64_t row_bytes = a.row_elems * a.elem;
@@ -210,7 +325,7 @@ hipError_t launch_prep(const PrepLaunch &a, hipStream_t stream) {
     p.qw = a.qw; p.kw = a.kw; p.cos = a.cos; p.sin = a.sin;
     p.half = (int)a.half;
     p.eps = a.eps;
-    const int mode = a.half == 0 ? 0 : (2 * a.half == a.d ? 1 : 2);
+    const int mode = a.half == 0 ? 0 : (a.pairs ? 3 : (2 * a.half == a.d ? 1 : 2));
     if (a.d == 64)
         return a.bf16 ? launch_prep_d<true, 64>(p, mode, stream) : launch_prep_d<false, 64>(p, mode, stream);
     return a.bf16 ? launch_prep_d<true, 128>(p, mode, stream) : launch_prep_d<false, 128>(p, mode, stream);

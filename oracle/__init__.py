@@ -15,6 +15,8 @@ chunked prefill against a KV cache, decode):
 * attention and its causal mask -- same page, "Functions > attention" and
   "Functions > causalMask"; packed rows with block-diagonal groups -- same page,
   "Functions > attentionRows" and "Functions > attendedRows".
+* the quantised KV cache's coding -- compute guide "Tensors, GPU kernels and AI models",
+  "Step 5: Run a language model" (8, 4 or 2 bits, least-squared-error range per head).
 * headPrepInPlace's position rule (the table row of a token is its sequence row,
   ``row0`` being the row of the first) -- same page, "Functions > headPrepInPlace".
 """
@@ -29,5 +31,10 @@ from .oracle import (  # noqa: F401
     prefill_chunk,
     attended_rows,
     decode,
+    decode_q,
+    kv_quantize,
+    kv_dequantize,
+    kv_pack,
+    kv_unpack,
     threads,
 )

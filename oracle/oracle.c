@@ -7,7 +7,8 @@
  * step can be read against the definition it follows; the only parallelism is an
  * OpenMP loop over independent (row, head) or (query row, head) items.
  *
- * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -lm  (no fast-math: IEEE f64).
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC oracle.c -lm  (no fast-math and
+ * no fused multiply-add: IEEE f64, and f32 where a quantised code is decided).
  */
 #include "oracle.h"
 
@@ -177,6 +178,87 @@ int oracle_row_norm_rope(double *x, int64_t rows, int64_t width, int64_t head, c
                 xr[ia] = a * c[t] - b * s[t];
                 xr[ib] = b * c[t] + a * s[t];
             }
+    }
+    return 0;
+}
+
+/*
+ * Coding of a quantised KV cache (compute guide "Tensors, GPU kernels and AI models",
+ * Step 5: Run a language model -- keys and values kept in 8, 4 or 2 bits, each head coded
+ * over the range that returns it with the least squared error).  One unit is one head of one token: d float values.  With L = 2^bits levels,
+ * a range [lo, lo + (L-1) step] gives value x the code rint((x - lo) / step) clamped to
+ * [0, L-1], and back the value lo + step code.  The candidate ranges are centred on
+ * (min + max)/2 with half-widths r (32 - k)/32, k = 0..23 (r = (max - min)/2); the
+ * candidate giving the least squared error wins, the widest on a tie.  Every step that
+ * decides a code runs in f32, in the order written (the division as a product with the
+ * f32 reciprocal of step); the squared error of a candidate is summed in f64.  A unit
+ * whose half-range r is 1e-30 or less is coded as lo = min, step = 0, codes 0.
+ */
+/* Candidate k of a unit with half-range r around centre: its lo, step and 1/step. */
+static void kv_candidate(float centre, float r, int32_t k, int32_t top, float *lo, float *st, float *inv)
+{
+    const float hw = r * ((float)(32 - k) / 32.0f);
+    *lo = centre - hw;
+    *st = (hw + hw) / (float)top;
+    *inv = 1.0f / *st;
+}
+
+/* The code of value x in the range (lo, 1/step): nearest level, clamped to [0, top]. */
+static int32_t kv_code(float x, float lo, float inv, int32_t top)
+{
+    float t = rintf((x - lo) * inv);
+    if (t < 0.0f) t = 0.0f;
+    if (t > (float)top) t = (float)top;
+    return (int32_t)t;
+}
+
+int oracle_kv_quantize(const float *x, int64_t units, int64_t d, int64_t bits, int32_t *codes,
+                       float *lo_out, float *step_out, int32_t *k_out)
+{
+    if (!x || !codes || !lo_out || !step_out || units < 0 || d <= 0 || (bits != 8 && bits != 4 && bits != 2))
+        return -1;
+    const int32_t top = (1 << bits) - 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t u = 0; u < units; ++u) {
+        const float *xu = x + u * d;
+        int32_t *cu = codes + u * d;
+        float mn = xu[0], mx = xu[0];
+        for (int64_t e = 1; e < d; ++e) {
+            if (xu[e] < mn) mn = xu[e];
+            if (xu[e] > mx) mx = xu[e];
+        }
+        const float centre = (mn + mx) * 0.5f;
+        const float r = (mx - mn) * 0.5f;
+        if (!(r > 1e-30f)) {
+            lo_out[u] = mn;
+            step_out[u] = 0.0f;
+            for (int64_t e = 0; e < d; ++e) cu[e] = 0;
+            if (k_out) k_out[u] = 0;
+            continue;
+        }
+        double best = INFINITY;
+        int32_t best_k = 0;
+        for (int32_t k = 0; k < 24; ++k) {
+            float lo, st, inv;
+            kv_candidate(centre, r, k, top, &lo, &st, &inv);
+            double sse = 0.0;
+            for (int64_t e = 0; e < d; ++e) {
+                const double back = (double)lo + (double)st * (double)kv_code(xu[e], lo, inv, top);
+                const double err = (double)xu[e] - back;
+                sse += err * err;
+            }
+            if (sse < best) {
+                best = sse;
+                best_k = k;
+            }
+        }
+        float lo, st, inv;
+        kv_candidate(centre, r, best_k, top, &lo, &st, &inv);
+        for (int64_t e = 0; e < d; ++e)
+            cu[e] = kv_code(xu[e], lo, inv, top);
+        lo_out[u] = lo;
+        step_out[u] = st;
+        if (k_out) k_out[u] = best_k;
     }
     return 0;
 }

@@ -12,6 +12,9 @@
  *   - the whole-row norm and rotary: same page, "Functions > rowNormRopeInto".
  *   - attention, causal mask: gizml:netops reference page, "Functions > attention"
  *     and "Functions > causalMask".
+ *   - the quantised KV cache's coding: compute guide "Tensors, GPU kernels and AI
+ *     models", Step 5: Run a language model (8, 4 or 2 bits over a least-squared-error
+ *     range; decisions in f32).
  * Layouts are row-major, token rows with heads contiguous inside a row.
  * Every function returns 0 on success and a negative value on a bad argument
  * (nothing is written in that case).
@@ -80,6 +83,17 @@ int oracle_attention_rows(const double *q, const double *k, const double *v, dou
                           int64_t batch, int64_t tq, int64_t tk, int64_t hq, int64_t hkv,
                           int64_t d, int64_t dv, double scale, int causal, const int64_t *lens,
                           const int64_t *sel, int64_t nsel);
+
+/*
+ * Quantised KV cache coding of `units` heads of d f32 values each (x [units, d]) in
+ * `bits` in {8, 4, 2}: codes [units, d] in [0, 2^bits - 1], and per unit lo, step (f32)
+ * with value lo + step * code.  Candidate ranges centred on (min + max)/2, half-widths
+ * (max - min)/2 * (32 - k)/32 for k = 0..23; the least squared error (summed in f64)
+ * wins, the widest on a tie; codes rint((x - lo) * (1/step)) clamped, in f32.
+ * k_out (may be NULL) receives the winning k.  Returns -1 on a bad argument.
+ */
+int oracle_kv_quantize(const float *x, int64_t units, int64_t d, int64_t bits, int32_t *codes,
+                       float *lo_out, float *step_out, int32_t *k_out);
 
 /* Number of OpenMP threads a parallel region of this library uses. */
 int oracle_threads(void);

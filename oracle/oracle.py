@@ -30,7 +30,7 @@ def build(force: bool = False) -> str:
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.run(
-            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+            ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared", "-std=c99",
              "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"],
             check=True)
         os.replace(tmp, _LIB)
@@ -58,6 +58,10 @@ def _load():
         lib.oracle_attention.restype = ctypes.c_int
         lib.oracle_attention_rows.argtypes = att + [_lp, ctypes.c_int64]
         lib.oracle_attention_rows.restype = ctypes.c_int
+        fp = ctypes.POINTER(ctypes.c_float)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        lib.oracle_kv_quantize.argtypes = [fp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ip, fp, fp, ip]
+        lib.oracle_kv_quantize.restype = ctypes.c_int
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
@@ -240,6 +244,58 @@ def attended_rows(qkv, heads: int, head: int, group: int = 0, queries: int = 0, 
     return out.reshape(nq, heads * head), q, k
 
 
+def kv_quantize(x, bits: int):
+    """Quantised-cache coding of every head of x [..., d] (f32 values) in `bits` (8, 4, 2):
+    returns (codes [..., d] int32, lo [...] f32, step [...] f32, k [...] int32 -- the chosen
+    candidate), as oracle_kv_quantize defines it."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    d = x.shape[-1]
+    units = int(np.prod(x.shape[:-1], dtype=np.int64))
+    codes = np.zeros(x.shape, dtype=np.int32)
+    lo = np.zeros(x.shape[:-1], dtype=np.float32)
+    step = np.zeros(x.shape[:-1], dtype=np.float32)
+    kk = np.zeros(x.shape[:-1], dtype=np.int32)
+    fp = ctypes.POINTER(ctypes.c_float)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    rc = _load().oracle_kv_quantize(x.ctypes.data_as(fp), units, d, int(bits), codes.ctypes.data_as(ip),
+                                    lo.ctypes.data_as(fp), step.ctypes.data_as(fp), kk.ctypes.data_as(ip))
+    if rc != 0:
+        raise ValueError("oracle_kv_quantize rejected its arguments (code %d)" % rc)
+    return codes, lo, step, kk
+
+
+def kv_dequantize(codes, lo, step) -> np.ndarray:
+    """The values a coded head gives back, lo + step * code, in f64."""
+    return (np.asarray(lo, np.float64)[..., None] +
+            np.asarray(step, np.float64)[..., None] * np.asarray(codes, np.float64))
+
+
+def kv_pack(codes, bits: int) -> np.ndarray:
+    """The stored bytes of codes [..., d]: each 32-bit little-endian word holds 32 / bits
+    consecutive codes, code j of the word at bit (j mod 2) * 16 + (j // 2) * bits (even
+    codes in the low half-word, odd ones in the high half-word).  -> uint8 [..., d bits / 8]."""
+    codes = np.asarray(codes, dtype=np.uint64)
+    per = 32 // bits
+    d = codes.shape[-1]
+    assert d % per == 0
+    g = codes.reshape(codes.shape[:-1] + (d // per, per))
+    j = np.arange(per, dtype=np.uint64)
+    shift = (j % 2) * 16 + (j // 2) * bits
+    words = (g << shift).sum(axis=-1).astype(np.uint32)
+    return words.view(np.uint8).reshape(codes.shape[:-1] + (d * bits // 8,))
+
+
+def kv_unpack(packed, bits: int, d: int) -> np.ndarray:
+    """Inverse of kv_pack -> int32 codes [..., d]."""
+    packed = np.ascontiguousarray(np.asarray(packed, dtype=np.uint8))
+    per = 32 // bits
+    words = packed.view(np.uint32).astype(np.uint64)
+    j = np.arange(per, dtype=np.uint64)
+    shift = (j % 2) * 16 + (j // 2) * bits
+    g = (words[..., None] >> shift) & np.uint64((1 << bits) - 1)
+    return g.reshape(packed.shape[:-1] + (d,)).astype(np.int32)
+
+
 def decode(q, k_cache, v_cache, lens, pos, qw, cos, sin, half: int, eps: float,
            scale: float) -> np.ndarray:
     """One new query row per sequence: q [B, hq, d] prepped at table row pos[b], then
@@ -249,3 +305,11 @@ def decode(q, k_cache, v_cache, lens, pos, qw, cos, sin, half: int, eps: float,
     qh = headprep(q[:, None], qw, cos, sin, half, np.asarray(pos, dtype=np.int64)[:, None], eps)
     out = attention(qh, k_cache, v_cache, scale, causal=False, lens=lens)
     return out[:, 0]
+
+
+def decode_q(q, k_codes, k_lo, k_step, v_codes, v_lo, v_step, lens, pos, qw, cos, sin, half: int,
+             eps: float, scale: float) -> np.ndarray:
+    """Decode against a quantised cache: the cache [B, capacity, hkv, d] gives back
+    lo + step * code per head (kv_dequantize), then the decode above.  Codes unpacked."""
+    return decode(q, kv_dequantize(k_codes, k_lo, k_step), kv_dequantize(v_codes, v_lo, v_step), lens, pos,
+                  qw, cos, sin, half, eps, scale)

@@ -41,6 +41,11 @@ MUTANTS = {
                                  "const double a = x[2 * i], b = x[i + half];"),
     "row norm over one head": ("acc /= (double)width;", "acc /= (double)head;"),
     "row rotary: same angles for every head": ("t = h * half + j;", "t = j;"),
+    "kv: codes truncated, not rounded": ("float t = rintf((x - lo) * inv);", "float t = truncf((x - lo) * inv);"),
+    "kv: codes not clamped at the top": ("if (t > (float)top) t = (float)top;", ";"),
+    "kv: step over 2^bits levels": ("*st = (hw + hw) / (float)top;", "*st = (hw + hw) / (float)(top + 1);"),
+    "kv: range starts at the minimum": ("*lo = centre - hw;", "*lo = centre - r;"),
+    "kv: the largest error wins": ("if (sse < best) {", "if (sse > best || best == INFINITY) {"),
     "value of wrong key": ("const double *vj = v + ((b * tk + j) * hkv + g) * dv;",
                            "const double *vj = v + ((b * tk + (j ? j - 1 : 0)) * hkv + g) * dv;"),
 }
@@ -54,7 +59,7 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     mutant = tmp_path / "oracle_mutant.c"
     mutant.write_text(src.replace(old, new))
     lib = tmp_path / "liboracle_mutant.so"
-    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared", "-std=c99",
                     "-I", os.path.join(ROOT, "oracle"), str(mutant), "-o", str(lib), "-lm"],
                    check=True)
     env = dict(os.environ, ATTN_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")

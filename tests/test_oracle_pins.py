@@ -477,6 +477,94 @@ def test_attended_rows_is_block_diagonal_sdpa(n, group, queries):
     np.testing.assert_allclose(out, ref[:nq], rtol=0, atol=1e-13)
 
 
+# ------------------------------------------------------------ quantised KV cache coding
+
+def test_kv_coding_worked_examples(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "kv_coding.json")))
+    for case in g["quantize"]:
+        codes, lo, step, k = oracle.kv_quantize(np.array([case["x"]], np.float32), case["bits"])
+        assert codes[0].tolist() == case["codes"], case["name"]
+        assert float(lo[0]) == case["lo"] and float(step[0]) == case["step"], case["name"]
+        assert int(k[0]) == case["k"], case["name"]
+    for case in g["pack"]:
+        got = oracle.kv_pack(np.array([case["codes"]]), case["bits"])[0]
+        assert got.tolist() == case["bytes"], case["name"]
+        assert oracle.kv_unpack(got[None], case["bits"], len(case["codes"]))[0].tolist() == case["codes"]
+
+
+def _np_quantize(x, bits):
+    """Brute force in numpy float32 over the 24 candidate ranges (vectorised, a separate
+    code path from the oracle's loops): the codes, lo, step and k of least error."""
+    x = np.asarray(x, np.float32)
+    top = np.float32(2 ** bits - 1)
+    mn, mx = x.min(), x.max()
+    centre = (mn + mx) * np.float32(0.5)
+    r = (mx - mn) * np.float32(0.5)
+    f = (np.float32(32) - np.arange(24, dtype=np.float32)) / np.float32(32)
+    hw = r * f
+    lo = centre - hw
+    st = (hw + hw) / top
+    inv = np.float32(1) / st
+    c = np.clip(np.rint((x[None, :] - lo[:, None]) * inv[:, None]), 0, top)
+    back = lo[:, None].astype(np.float64) + st[:, None].astype(np.float64) * c
+    err = ((x[None, :].astype(np.float64) - back) ** 2).sum(axis=1)
+    k = int(np.argmin(err))
+    return c[k].astype(np.int32), lo[k], st[k], k, err
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+def test_kv_quantize_is_the_least_error_candidate(bits):
+    rng = np.random.default_rng(bits)
+    x = np.concatenate([rng.standard_normal((20, 64)), rng.standard_t(3, (20, 64)) * 3.0]).astype(np.float32)
+    codes, lo, step, k = oracle.kv_quantize(x, bits)
+    for u in range(x.shape[0]):
+        c, l0, s0, k0, err = _np_quantize(x[u], bits)
+        assert k[u] == k0 and lo[u] == l0 and step[u] == s0
+        np.testing.assert_array_equal(codes[u], c)
+        back = oracle.kv_dequantize(codes[u], lo[u], step[u])
+        assert abs(((x[u] - back) ** 2).sum() - err.min()) <= 1e-12 * max(1.0, err.min())
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+def test_kv_quantize_invariants(bits):
+    rng = np.random.default_rng(10 + bits)
+    x = (rng.standard_normal((50, 128)) * rng.uniform(0.1, 10, (50, 1))).astype(np.float32)
+    codes, lo, step, k = oracle.kv_quantize(x, bits)
+    top = 2 ** bits - 1
+    assert codes.min() >= 0 and codes.max() <= top
+    back = oracle.kv_dequantize(codes, lo, step)
+    inside = (x >= lo[:, None]) & (x <= lo[:, None] + top * step[:, None].astype(np.float64))
+    # inside the range every value comes back within half a step (plus f32 rounding)
+    assert (np.abs(x - back)[inside] <= (0.5 + 1e-5) * np.broadcast_to(step[:, None], x.shape)[inside]).all()
+    # scaling by a power of two scales the range exactly and keeps the codes
+    c2, lo2, st2, k2 = oracle.kv_quantize(x * np.float32(8.0), bits)
+    np.testing.assert_array_equal(c2, codes)
+    np.testing.assert_array_equal(k2, k)
+    np.testing.assert_array_equal(lo2, lo * np.float32(8.0))
+    np.testing.assert_array_equal(st2, step * np.float32(8.0))
+    # the chosen range is never worse than min..max (candidate 0 up to its f32 rounding)
+    mn, mx = x.min(axis=1), x.max(axis=1)
+    st0 = (mx - mn) / np.float32(top)
+    c0 = np.clip(np.rint((x - mn[:, None]) * (np.float32(1) / st0)[:, None]), 0, top)
+    err0 = ((x - (mn[:, None].astype(np.float64) + st0[:, None] * c0)) ** 2).sum(axis=1)
+    assert (((x - back) ** 2).sum(axis=1) <= err0 * (1 + 1e-4)).all()
+
+
+def test_kv_quantize_constant_head_and_fewer_bits_more_error():
+    x = np.full((2, 32), 1.25, np.float32)
+    codes, lo, step, _ = oracle.kv_quantize(x, 4)
+    assert (codes == 0).all() and (lo == 1.25).all() and (step == 0).all()
+    np.testing.assert_array_equal(oracle.kv_dequantize(codes, lo, step), x)
+    y = np.random.default_rng(3).standard_normal((200, 128)).astype(np.float32)
+    errs = []
+    for bits in (8, 4, 2):
+        c, l0, s0, _ = oracle.kv_quantize(y, bits)
+        errs.append(((y - oracle.kv_dequantize(c, l0, s0)) ** 2).mean())
+    assert errs[0] < errs[1] < errs[2]
+    # a uniform quantiser's error on N(0, 1) is about step^2 / 12: 8 bits at ~5.5 sigma / 255
+    assert 0.5 < errs[0] / ((5.5 / 255) ** 2 / 12) < 2.0
+
+
 # ------------------------------------------------------------------- input generation
 
 def test_bf16_rounding_matches_torch():

@@ -14,7 +14,9 @@ not served from the 256 MB last-level cache.
 After the timed steps: the long prefill workload (batch 1 x 16384 tokens, 64 q / 8 kv
 heads, rotary base 1e6, 1 % outlier key rows), k HeadPrep + attention per call; the
 chunked prefill workload (batch 4: 512 new tokens appended to a 3584-row cache, 32 q / 8
-kv heads, attention over all 4096 rows) per attn_prefill_chunk call; packed rows of an
+kv heads, attention over all 4096 rows) per attn_prefill_chunk call; the decode workload
+against caches coded in 8/8, 4/4 and 4/2 bits (attn_decode_q; GB/s of the codes, their
+ranges, q and out); packed rows of an
 image model (attn_rows: 4608 rows of 24 heads of 128, HeadPrep with adjacent pairs in
 place -- repeated calls re-prep the same buffer, which changes values, not work -- then
 full attention); the whole-row norm + per-head rotary of 6240 rows of 4096
@@ -95,6 +97,14 @@ def cpu_baseline(w, inp) -> dict:
             "host_cpu": platform.processor() or platform.machine()}
 
 
+def decode_bytes_q(w, kbits: int, vbits: int) -> int:
+    """Bytes a quantised-cache decode must move: the codes of every cached key and value
+    of every kv head, their (lo, step) pairs, q and out (bf16), one table row and qw."""
+    rows = w.batch * w.seq * w.hkv
+    return (rows * w.d * (kbits + vbits) // 8 + rows * 2 * 8 + 2 * w.batch * w.hq * w.d * 2 +
+            (2 * w.half + w.d) * 4)
+
+
 def stats_ms(a) -> dict:
     import numpy as np
     a = np.asarray(a)
@@ -146,6 +156,8 @@ def main() -> int:
     ap.add_argument("--cache-copies", type=int, default=3)
     ap.add_argument("--long-calls", type=int, default=20, help="timed calls of the long prefill (0: skip)")
     ap.add_argument("--chunk-calls", type=int, default=20, help="timed calls of the chunked prefill (0: skip)")
+    ap.add_argument("--quant-calls", type=int, default=30,
+                    help="timed calls of the decode against 8/8, 4/4 and 4/2-bit caches (0: skip)")
     ap.add_argument("--rows-calls", type=int, default=20,
                     help="timed calls of the packed-rows attention and the row norm (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -210,6 +222,18 @@ def main() -> int:
     out4 = torch.empty_like(q4)
     stream = torch.cuda.current_stream()
 
+    def time_calls(fn, calls):
+        for _ in range(3):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
     def step(i, ev=None):
         if ev is not None:
             ev[0].record(stream)
@@ -243,6 +267,39 @@ def main() -> int:
     pre_tflops = flops / ((prep_ms + attn_ms).mean() * 1e-3) / 1e12
     attn_tflops = flops / (attn_ms.mean() * 1e-3) / 1e12
     dec_gbps = nbytes / (dec_ms.mean() * 1e-3) / 1e9
+    # ---- decode against quantised caches (coded on the GPU from the same prepped caches)
+    quant_lines = {}
+    if args.quant_calls > 0:
+        for kb, vb in ((8, 8), (4, 4), (4, 2)):
+            qk, qv = [], []
+            for c in range(len(kcs)):
+                kq = tah.QuantCache.empty(wd.batch, wd.hkv, wd.seq, wd.d, kb, device=dev)
+                vq = tah.QuantCache.empty(wd.batch, wd.hkv, wd.seq, wd.d, vb, device=dev)
+                tah.attn_kv_quantize(kcs[c], kq, row0=0)
+                tah.attn_kv_quantize(vcs[c], vq, row0=0)
+                qk.append(kq)
+                qv.append(vq)
+            turn = [0]
+            sq = tah.decode_q_default_splits(wd.batch, wd.hq, wd.hkv, wd.seq, kb)
+            nq = tah.decode_workspace_size(wd.batch, wd.hq, wd.hkv, wd.d, wd.seq, sq)
+            wsq = torch.empty(nq, dtype=torch.uint8, device=dev) if nq else None
+
+            def callq():
+                c = turn[0] % len(qk)
+                turn[0] += 1
+                tah.attn_decode_q(q4, qk[c], qv[c], lens, pos, wd.seq, prep=prep4, scale=wd.scale, splits=sq,
+                                  workspace=wsq, out=out4, stream=stream)
+
+            msq = time_calls(callq, args.quant_calls)
+            qbytes = decode_bytes_q(wd, kb, vb)
+            gbq = qbytes / (msq.mean() * 1e-3) / 1e9
+            quant_lines["k%d_v%d" % (kb, vb)] = {
+                "value": round(gbq, 2), "unit": "GB/s", "ms": stats_ms(msq), "bytes": qbytes,
+                "frac_of_hbm_peak": round(gbq / PEAK_HBM_GBPS, 4), "splits": sq,
+                "speedup_vs_bf16_cache": round(float(dec_ms.mean() / msq.mean()), 3)}
+            del qk, qv
+        torch.cuda.empty_cache()
+
     del q3, k3, v3, out3, kcs, vcs, k_raw, v_raw
 
     # ---- long prefill: k HeadPrep + attention per call
@@ -319,18 +376,6 @@ def main() -> int:
                       "frac_of_bf16_peak": round(tf6 / PEAK_BF16_TFLOPS, 4)}
         del q6, kn6, vn6, out6, kc6, vc6
         torch.cuda.empty_cache()
-
-    def time_calls(fn, calls):
-        for _ in range(3):
-            fn()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
-        torch.cuda.synchronize()
-        for a, b in evs:
-            a.record(stream)
-            fn()
-            b.record(stream)
-        torch.cuda.synchronize()
-        return np.array([a.elapsed_time(b) for a, b in evs])
 
     # ---- packed image-model rows: HeadPrep (adjacent pairs) in place + full attention
     rows_line = None
@@ -422,6 +467,10 @@ def main() -> int:
         line["long_prefill"] = long_line
     if chunk_line is not None:
         line["chunk_prefill"] = chunk_line
+    if quant_lines:
+        line["decode_quantized"] = dict(
+            workload="bf16 decode workload against quantised caches (keys and values in k / v bits, per-head "
+                     "least-squared-error ranges), 3 cache copies in turn", **quant_lines)
     if rows_line is not None:
         line["image_rows"] = rows_line
     if rownorm_line is not None:

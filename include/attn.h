@@ -191,6 +191,67 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
                           void *stream);
 
 /*
+ * Quantised KV cache (compute guide "Tensors, GPU kernels and AI models", Step 5: Run a
+ * language model: keys and values kept in 8, 4 or 2 bits, or keys in 4 and values in 2,
+ * each head coded over the range that returns it with the least squared error).
+ *
+ * Format of one cached tensor (K or V) with `bits` in {8, 4, 2}, head-major:
+ *   codes  uint8 [batch, heads, capacity, d * bits / 8]: the d codes c of one head of one
+ *          token; each 32-bit little-endian word holds 32 / bits consecutive codes, code
+ *          j of the word at bit (j mod 2) * 16 + (j / 2) * bits (even codes in the low
+ *          half-word, odd codes in the high half-word).
+ *   params f32 [batch, heads, capacity, 2]: (lo, step); the head's value e is
+ *          lo + step * c[e].
+ * Coding (attn_kv_quantize): with L = 2^bits levels, min and max of the head's d values,
+ * centre = (min + max) / 2, r = (max - min) / 2, candidate k = 0..23 has
+ *   lo = centre - r (32 - k) / 32,  step = 2 r (32 - k) / 32 / (L - 1),
+ *   c = clamp(rint((x - lo) * (1 / step)), 0, L - 1)       (f32, round to nearest even);
+ * the candidate whose values lo + step c have the least squared error wins (the widest
+ * on a tie; the error is summed in f64, so candidates within rounding of each other may
+ * be ranked either way).  A head with r <= 1e-30 is coded lo = min, step = 0, c = 0.
+ */
+
+/*
+ * attn_kv_quantize -- code rows of keys or values into a quantised cache.
+ *   x       [batch, seq, heads, d] (row stride x_row_stride elements, sequences
+ *           seq * x_row_stride apart), dtype ATTN_BF16 or ATTN_F32; read only.
+ *   bits    8, 4 or 2.
+ *   codes, params  the cache in the format above, with `capacity` rows per (sequence,
+ *           head); token t of sequence b is written at row row0 + t.  16-byte aligned.
+ *   0 <= row0, row0 + seq <= capacity.  d in {64, 128}.  batch or seq 0 is a no-op.
+ * Keys are coded after their HeadPrep (run attn_prep on them first).
+ */
+attn_status_t attn_kv_quantize(const void *x, int64_t batch, int64_t seq, int64_t heads, int64_t d,
+                               int64_t x_row_stride, int64_t bits, uint8_t *codes, float *params,
+                               int64_t capacity, int64_t row0, attn_dtype_t dtype, void *stream);
+
+/*
+ * attn_decode_q -- attn_decode against a quantised cache: one new query row per
+ * sequence attends the first lens[b] rows; the cache returns lo + step c per head.
+ *   q, out       bf16 [batch, hq, d] contiguous (dtype must be ATTN_BF16).
+ *   k_codes, k_params, v_codes, v_params   the caches (format above) with hkv heads and
+ *                `capacity` rows, coded in k_bits and v_bits: (8, 8), (4, 4), (4, 2) or
+ *                (2, 2).
+ *   lens, pos, max_len, prep, scale: as attn_decode.
+ *   splits       number of key splits per sequence; 0 = attn_decode_q_default_splits
+ *                (more splits than the bf16 decode takes: a coded chunk carries fewer
+ *                bytes, so more blocks keep the memory busy).
+ *   workspace    at least attn_decode_workspace_size(batch, hq, hkv, d, max_len, s) bytes
+ *                where s is the split count the call uses (the default resolved above
+ *                when splits = 0); NULL is allowed when that size is 0.
+ *   The products run on the matrix cores over the codes as bf16 operands, q carried as
+ *   a bf16 high part plus a remainder; the errors are those of attn_decode's bf16 path.
+ */
+int64_t attn_decode_q_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len,
+                                     int64_t k_bits);
+attn_status_t attn_decode_q(const void *q, const uint8_t *k_codes, const float *k_params,
+                            const uint8_t *v_codes, const float *v_params, void *out, int64_t batch,
+                            int64_t hq, int64_t hkv, int64_t d, int64_t capacity, int64_t k_bits,
+                            int64_t v_bits, const int32_t *lens, const int32_t *pos, int64_t max_len,
+                            const attn_headprep_t *prep, double scale, int64_t splits, void *workspace,
+                            size_t workspace_bytes, attn_dtype_t dtype, void *stream);
+
+/*
  * attn_rows -- full attention of packed rows, for image and video models (gizml:netops,
  * Functions > attentionRows, its BF16 path, and attendedRows for `queries`).
  *   qkv      [n, 3 * heads * head]: row r holds q, k and v of `heads` heads of `head`

@@ -256,3 +256,83 @@ def test_row_norm_rope_rejects(lib, kw, code):
 def test_row_norm_rope_empty_is_a_no_op(lib):
     assert _row_norm(lib, rows=0) == A.ATTN_OK
     assert _row_norm(lib, rows=0, cos=None, sin=None) == A.ATTN_OK
+
+
+def _quant(lib, **kw):
+    a = dict(x=FAKE, batch=2, seq=16, heads=8, d=128, rs=1024, bits=4, codes=FAKE + (1 << 32),
+             params=FAKE + (2 << 32), capacity=64, row0=8, dtype=A.ATTN_BF16)
+    a.update(kw)
+    return lib.attn_kv_quantize(a["x"], a["batch"], a["seq"], a["heads"], a["d"], a["rs"], a["bits"], a["codes"],
+                                a["params"], a["capacity"], a["row0"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96, rs=768), A.ATTN_ERR_UNSUPPORTED),
+    (dict(bits=3), A.ATTN_ERR_ARG),
+    (dict(bits=16), A.ATTN_ERR_ARG),
+    (dict(x=None), A.ATTN_ERR_ARG),
+    (dict(codes=None), A.ATTN_ERR_ARG),
+    (dict(params=FAKE + (2 << 32) + 8), A.ATTN_ERR_ARG),   # misaligned
+    (dict(row0=-1), A.ATTN_ERR_ARG),
+    (dict(row0=49), A.ATTN_ERR_ARG),                        # row0 + seq > capacity
+    (dict(capacity=0, row0=0), A.ATTN_ERR_ARG),
+    (dict(rs=1000), A.ATTN_ERR_ARG),
+    (dict(codes=FAKE + 4096), A.ATTN_ERR_ARG),              # codes overlap x
+])
+def test_kv_quantize_rejects(lib, kw, code):
+    assert _quant(lib, **kw) == code
+    assert lib.attn_last_error()
+
+
+def test_kv_quantize_empty_is_a_no_op(lib):
+    assert _quant(lib, seq=0) == A.ATTN_OK
+    assert _quant(lib, batch=0) == A.ATTN_OK
+
+
+def _decq(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE + (1 << 32), kp=FAKE + (2 << 32), vc=FAKE + (3 << 32), vp=FAKE + (4 << 32),
+             out=FAKE + (5 << 32), batch=4, hq=32, hkv=8, d=128, cap=4096, kb=8, vb=8, lens=FAKE + (6 << 32),
+             pos=FAKE + (7 << 32), max_len=4096, prep=_prep(), scale=0.088, splits=1, ws=None, wsb=0,
+             dtype=A.ATTN_BF16)
+    a.update(kw)
+    prep = ctypes.byref(a["prep"]) if a["prep"] is not None else None
+    return lib.attn_decode_q(a["q"], a["kc"], a["kp"], a["vc"], a["vp"], a["out"], a["batch"], a["hq"], a["hkv"],
+                             a["d"], a["cap"], a["kb"], a["vb"], a["lens"], a["pos"], a["max_len"], prep, a["scale"],
+                             a["splits"], a["ws"], a["wsb"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=A.ATTN_F32), A.ATTN_ERR_UNSUPPORTED),       # bf16 q and out only
+    (dict(d=96), A.ATTN_ERR_UNSUPPORTED),
+    (dict(kb=8, vb=4), A.ATTN_ERR_ARG),                     # not an offered pair
+    (dict(kb=2, vb=4), A.ATTN_ERR_ARG),
+    (dict(kb=16, vb=16), A.ATTN_ERR_ARG),
+    (dict(kc=None), A.ATTN_ERR_ARG),
+    (dict(vp=FAKE + (4 << 32) + 4), A.ATTN_ERR_ARG),        # misaligned
+    (dict(lens=None), A.ATTN_ERR_ARG),
+    (dict(max_len=0), A.ATTN_ERR_ARG),
+    (dict(max_len=4097), A.ATTN_ERR_ARG),
+    (dict(hq=30), A.ATTN_ERR_ARG),
+    (dict(scale=-1.0), A.ATTN_ERR_ARG),
+    (dict(pos=None), A.ATTN_ERR_ARG),                       # turning HeadPrep needs pos
+    (dict(splits=4), A.ATTN_ERR_WORKSPACE),                 # a workspace is needed and missing
+    (dict(out=FAKE + 256), A.ATTN_ERR_ARG),                 # out overlaps q
+    (dict(prep=_prep(pairs=3)), A.ATTN_ERR_ARG),
+])
+def test_decode_q_rejects(lib, kw, code):
+    assert _decq(lib, **kw) == code
+    assert lib.attn_last_error()
+
+
+def test_decode_q_default_splits(lib):
+    # the decode workload's 256 (sequence, kv head) units: 2 blocks per CU at 8 bits, 4 below
+    assert lib.attn_decode_q_default_splits(32, 32, 8, 4096, 8) == 2
+    assert lib.attn_decode_q_default_splits(32, 32, 8, 4096, 4) == 4
+    assert lib.attn_decode_q_default_splits(32, 32, 8, 4096, 2) == 4
+    assert lib.attn_decode_q_default_splits(32, 32, 8, 300, 4) == 2      # at least 256 keys a split
+    assert lib.attn_decode_q_default_splits(32, 32, 8, 4096, 3) == 0     # not a width
+    assert lib.attn_decode_q_default_splits(0, 32, 8, 4096, 8) == 0
+
+
+def test_decode_q_empty_is_a_no_op(lib):
+    assert _decq(lib, batch=0) == A.ATTN_OK

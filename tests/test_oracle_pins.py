@@ -17,6 +17,7 @@ import torch.nn.functional as F
 
 import oracle
 import synthetic
+from kv_util import np_quantize
 
 RNG = np.random.default_rng(1234)
 
@@ -492,33 +493,13 @@ def test_kv_coding_worked_examples(golden_dir):
         assert oracle.kv_unpack(got[None], case["bits"], len(case["codes"]))[0].tolist() == case["codes"]
 
 
-def _np_quantize(x, bits):
-    """Brute force in numpy float32 over the 24 candidate ranges (vectorised, a separate
-    code path from the oracle's loops): the codes, lo, step and k of least error."""
-    x = np.asarray(x, np.float32)
-    top = np.float32(2 ** bits - 1)
-    mn, mx = x.min(), x.max()
-    centre = (mn + mx) * np.float32(0.5)
-    r = (mx - mn) * np.float32(0.5)
-    f = (np.float32(32) - np.arange(24, dtype=np.float32)) / np.float32(32)
-    hw = r * f
-    lo = centre - hw
-    st = (hw + hw) / top
-    inv = np.float32(1) / st
-    c = np.clip(np.rint((x[None, :] - lo[:, None]) * inv[:, None]), 0, top)
-    back = lo[:, None].astype(np.float64) + st[:, None].astype(np.float64) * c
-    err = ((x[None, :].astype(np.float64) - back) ** 2).sum(axis=1)
-    k = int(np.argmin(err))
-    return c[k].astype(np.int32), lo[k], st[k], k, err
-
-
 @pytest.mark.parametrize("bits", [8, 4, 2])
 def test_kv_quantize_is_the_least_error_candidate(bits):
     rng = np.random.default_rng(bits)
     x = np.concatenate([rng.standard_normal((20, 64)), rng.standard_t(3, (20, 64)) * 3.0]).astype(np.float32)
     codes, lo, step, k = oracle.kv_quantize(x, bits)
     for u in range(x.shape[0]):
-        c, l0, s0, k0, err = _np_quantize(x[u], bits)
+        c, l0, s0, k0, err = np_quantize(x[u], bits)
         assert k[u] == k0 and lo[u] == l0 and step[u] == s0
         np.testing.assert_array_equal(codes[u], c)
         back = oracle.kv_dequantize(codes[u], lo[u], step[u])

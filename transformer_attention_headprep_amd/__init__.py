@@ -7,9 +7,12 @@ with ``python -m transformer_attention_headprep_amd.build``.
 from .attn import (  # noqa: F401
     AttnError,
     HeadPrep,
+    QuantCache,
     LIB_PATH,
     EXPORTS,
     attn_decode,
+    attn_decode_q,
+    attn_kv_quantize,
     attn_prefill,
     attn_prefill_chunk,
     attn_prep,
@@ -17,6 +20,7 @@ from .attn import (  # noqa: F401
     attn_rows,
     attn_supported,
     decode_default_splits,
+    decode_q_default_splits,
     decode_workspace_size,
     load_library,
 )

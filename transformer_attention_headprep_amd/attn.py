@@ -21,7 +21,7 @@ ATTN_OK, ATTN_ERR_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 
 
 # The entry points include/attn.h declares (checked by the CPU test suite).
 EXPORTS = ("attn_prep", "attn_prefill", "attn_prefill_chunk", "attn_decode", "attn_decode_workspace_size",
-           "attn_decode_default_splits", "attn_rows", "attn_row_norm_rope", "attn_supported", "attn_status_str",
+           "attn_decode_default_splits", "attn_kv_quantize", "attn_decode_q", "attn_decode_q_default_splits", "attn_rows", "attn_row_norm_rope", "attn_supported", "attn_status_str",
            "attn_last_error")
 
 
@@ -66,6 +66,13 @@ def load_library(path: str = LIB_PATH):
     lib.attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.attn_decode_default_splits.argtypes = [_i64] * 4
     lib.attn_decode_default_splits.restype = _i64
+    lib.attn_kv_quantize.argtypes = [_vp] + [_i64] * 6 + [_vp, _vp, _i64, _i64, ctypes.c_int, _vp]
+    lib.attn_kv_quantize.restype = ctypes.c_int
+    lib.attn_decode_q.argtypes = [_vp] * 6 + [_i64] * 7 + [_vp, _vp, _i64, hp, _dbl, _i64, _vp, ctypes.c_size_t,
+                                                         ctypes.c_int, _vp]
+    lib.attn_decode_q.restype = ctypes.c_int
+    lib.attn_decode_q_default_splits.argtypes = [_i64] * 5
+    lib.attn_decode_q_default_splits.restype = _i64
     lib.attn_rows.argtypes = [_vp] + [_i64] * 5 + [_vp, hp, ctypes.c_int, _vp]
     lib.attn_rows.restype = ctypes.c_int
     lib.attn_row_norm_rope.argtypes = [_vp] + [_i64] * 4 + [_vp, _vp, _vp, _dbl, ctypes.c_int, _vp]
@@ -212,6 +219,65 @@ def attn_prefill_chunk(q, k_new, v_new, k_cache, v_cache, n_past: int, out=None,
     return out
 
 
+@dataclass
+class QuantCache:
+    """A quantised KV cache of one tensor (K or V): codes uint8 [B, hkv, capacity, d bits / 8]
+    and params f32 [B, hkv, capacity, 2] (lo, step) on the device."""
+    codes: torch.Tensor
+    params: torch.Tensor
+    bits: int
+
+    @staticmethod
+    def empty(batch: int, heads: int, capacity: int, d: int, bits: int, device="cuda") -> "QuantCache":
+        return QuantCache(torch.zeros(batch, heads, capacity, d * bits // 8, dtype=torch.uint8, device=device),
+                          torch.zeros(batch, heads, capacity, 2, dtype=torch.float32, device=device), bits)
+
+    @property
+    def capacity(self) -> int:
+        return int(self.codes.shape[2])
+
+
+def attn_kv_quantize(x, cache: QuantCache, row0: int = 0, stream=None) -> None:
+    """Code x [B, S, H, D] (bf16 or f32) into cache rows row0 .. row0 + S - 1."""
+    lib = load_library()
+    B, S, H, D = x.shape
+    for t in (cache.codes, cache.params):
+        if not t.is_contiguous():
+            raise ValueError("the cache tensors must be contiguous")
+    if tuple(cache.codes.shape) != (B, H, cache.capacity, D * cache.bits // 8):
+        raise ValueError("cache codes must be [B, H, capacity, D * bits / 8]")
+    _check(lib.attn_kv_quantize(_ptr(x), B, S, H, D, _row_stride(x, "x"), cache.bits, _ptr(cache.codes),
+                                _ptr(cache.params), cache.capacity, row0, _dtype_code(x), _stream(stream)))
+
+
+def attn_decode_q(q, k: QuantCache, v: QuantCache, lens, pos, max_len: int, prep: HeadPrep | None = None,
+                  scale: float | None = None, splits: int = 0, workspace=None, out=None, stream=None) -> torch.Tensor:
+    """One bf16 query row per sequence (q [B, Hq, D]) against quantised caches."""
+    lib = load_library()
+    B, hq, D = q.shape
+    hkv, cap = k.codes.shape[1], k.capacity
+    if q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bfloat16 tensor")
+    if lens.dtype != torch.int32 or (pos is not None and pos.dtype != torch.int32):
+        raise TypeError("lens and pos must be int32 device tensors")
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if splits == 0:
+        splits = int(lib.attn_decode_q_default_splits(B, hq, hkv, max_len, k.bits))
+    need = decode_workspace_size(B, hq, hkv, D, max_len, splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = prep.struct() if prep is not None else None
+    _check(lib.attn_decode_q(_ptr(q), _ptr(k.codes), _ptr(k.params), _ptr(v.codes), _ptr(v.params), _ptr(out),
+                             B, hq, hkv, D, cap, k.bits, v.bits, _ptr(lens), _ptr(pos), max_len,
+                             ctypes.byref(st) if st is not None else None, float(scale), splits, _ptr(workspace),
+                             0 if workspace is None else workspace.numel() * workspace.element_size(),
+                             ATTN_BF16, _stream(stream)))
+    return out
+
+
 def attn_rows(qkv, heads: int, head: int, group: int = 0, queries: int = 0, out=None,
               prep: HeadPrep | None = None, stream=None) -> torch.Tensor:
     """Full attention of packed rows qkv [n, 3 * heads * head] (q, k, v of every head), each
@@ -255,6 +321,10 @@ def attn_row_norm_rope(x, w, eps: float, cos=None, sin=None, head: int | None = 
 
 def decode_workspace_size(batch: int, hq: int, hkv: int, d: int, max_len: int, splits: int = 0) -> int:
     return int(load_library().attn_decode_workspace_size(batch, hq, hkv, d, max_len, splits))
+
+
+def decode_q_default_splits(batch: int, hq: int, hkv: int, max_len: int, k_bits: int) -> int:
+    return int(load_library().attn_decode_q_default_splits(batch, hq, hkv, max_len, k_bits))
 
 
 def decode_default_splits(batch: int, hq: int, hkv: int, max_len: int) -> int:

@@ -392,6 +392,12 @@ int64_t attn_decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64
     return attn::decode_default_splits(batch, hq, hkv, max_len);
 }
 
+int64_t attn_decode_q_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len, int64_t k_bits) {
+    if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || max_len <= 0) return 0;
+    if (k_bits != 8 && k_bits != 4 && k_bits != 2) return 0;
+    return attn::decode_q_default_splits(batch, hq, hkv, max_len, k_bits);
+}
+
 size_t attn_decode_workspace_size(int64_t batch, int64_t hq, int64_t hkv, int64_t d, int64_t max_len,
                                   int64_t splits) {
     if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || d <= 0 || max_len <= 0 || splits < 0) return 0;
@@ -454,6 +460,105 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
     a.scale = (float)scale; a.splits = splits; a.work = static_cast<float *>(workspace);
     a.bf16 = dtype == ATTN_BF16;
     return hip_status(attn::launch_decode(a, static_cast<hipStream_t>(stream)), "attn_decode");
+}
+
+attn_status_t attn_kv_quantize(const void *x, int64_t batch, int64_t seq, int64_t heads, int64_t d,
+                               int64_t x_row_stride, int64_t bits, uint8_t *codes, float *params,
+                               int64_t capacity, int64_t row0, attn_dtype_t dtype, void *stream) {
+    g_last_error[0] = 0;
+    attn_status_t st = check_dtype_d(dtype, d);
+    if (st) return st;
+    if (batch < 0 || seq < 0) return fail(ATTN_ERR_ARG, "negative batch or seq");
+    if ((st = check_rows("x", x, heads, d, x_row_stride))) return st;
+    if (bits != 8 && bits != 4 && bits != 2) return fail(ATTN_ERR_ARG, "bits %lld not 8, 4 or 2", (long long)bits);
+    if (!codes || !params) return fail(ATTN_ERR_ARG, "codes or params is NULL");
+    if (!aligned16(codes) || !aligned16(params)) return fail(ATTN_ERR_ARG, "codes or params not 16-byte aligned");
+    if (capacity <= 0 || capacity >= ((int64_t)1 << 31)) return fail(ATTN_ERR_ARG, "capacity %lld outside [1, 2^31)", (long long)capacity);
+    if (row0 < 0 || row0 + seq > capacity)
+        return fail(ATTN_ERR_ARG, "rows [%lld, %lld) outside the %lld-row cache", (long long)row0, (long long)(row0 + seq),
+                    (long long)capacity);
+    if (batch == 0 || seq == 0) return ATTN_OK;
+    if (batch * seq * heads >= ((int64_t)1 << 36)) return fail(ATTN_ERR_ARG, "problem too large for one launch");
+    const size_t es = elem_size(dtype);
+    const Span sx = span(x, batch * seq, x_row_stride, heads, d, es);
+    const uintptr_t c0 = reinterpret_cast<uintptr_t>(codes), p0 = reinterpret_cast<uintptr_t>(params);
+    const Span sc{c0, c0 + (uintptr_t)(batch * heads * capacity * d * bits / 8)};
+    const Span sp{p0, p0 + (uintptr_t)(batch * heads * capacity * 2 * 4)};
+    if (overlap(sx, sc) || overlap(sx, sp) || overlap(sc, sp)) return fail(ATTN_ERR_ARG, "x, codes and params overlap");
+    attn::KvQuantLaunch a{};
+    a.x = x; a.rs = x_row_stride; a.batch = batch; a.seq = seq; a.heads = heads; a.d = d; a.bits = (int)bits;
+    a.codes = codes; a.params = params; a.capacity = capacity; a.row0 = row0; a.bf16 = dtype == ATTN_BF16;
+    return hip_status(attn::launch_kv_quantize(a, static_cast<hipStream_t>(stream)), "attn_kv_quantize");
+}
+
+attn_status_t attn_decode_q(const void *q, const uint8_t *k_codes, const float *k_params, const uint8_t *v_codes,
+                            const float *v_params, void *out, int64_t batch, int64_t hq, int64_t hkv, int64_t d,
+                            int64_t capacity, int64_t k_bits, int64_t v_bits, const int32_t *lens,
+                            const int32_t *pos, int64_t max_len, const attn_headprep_t *prep, double scale,
+                            int64_t splits, void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
+                            void *stream) {
+    g_last_error[0] = 0;
+    attn_status_t st = check_dtype_d(dtype, d);
+    if (st) return st;
+    if (dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "attn_decode_q takes bf16 q and out");
+    if (batch < 0) return fail(ATTN_ERR_ARG, "negative batch");
+    if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
+        return fail(ATTN_ERR_ARG, "hq = %lld must be a positive multiple of hkv = %lld", (long long)hq, (long long)hkv);
+    if (!((k_bits == 8 && v_bits == 8) || (k_bits == 4 && v_bits == 4) || (k_bits == 4 && v_bits == 2) ||
+          (k_bits == 2 && v_bits == 2)))
+        return fail(ATTN_ERR_ARG, "bits (%lld, %lld) not (8, 8), (4, 4), (4, 2) or (2, 2)", (long long)k_bits,
+                    (long long)v_bits);
+    if ((st = check_rows("q", q, hq, d, hq * d))) return st;
+    if ((st = check_rows("out", out, hq, d, hq * d))) return st;
+    if (!k_codes || !k_params || !v_codes || !v_params) return fail(ATTN_ERR_ARG, "a cache pointer is NULL");
+    if (!aligned16(k_codes) || !aligned16(k_params) || !aligned16(v_codes) || !aligned16(v_params))
+        return fail(ATTN_ERR_ARG, "cache pointers must be 16-byte aligned");
+    if (!lens) return fail(ATTN_ERR_ARG, "lens is NULL");
+    if (capacity <= 0 || capacity >= ((int64_t)1 << 31)) return fail(ATTN_ERR_ARG, "capacity %lld outside [1, 2^31)", (long long)capacity);
+    if (max_len < 1 || max_len > capacity) return fail(ATTN_ERR_ARG, "max_len %lld outside [1, capacity]", (long long)max_len);
+    if (splits < 0 || splits > max_len) return fail(ATTN_ERR_ARG, "splits %lld outside [0, max_len]", (long long)splits);
+    if (!std::isfinite(scale) || !(scale > 0.0)) return fail(ATTN_ERR_ARG, "scale must be finite and > 0");
+    if (prep) {
+        if ((st = check_prep(prep, d, true, false, 0, 0))) return st;
+        if (prep->half > 0 && !pos) return fail(ATTN_ERR_ARG, "pos is NULL with a turning HeadPrep");
+        if (prep->table_rows >= ((int64_t)1 << 31)) return fail(ATTN_ERR_ARG, "table too large");
+    }
+    if (batch == 0) return ATTN_OK;
+    if (splits == 0) splits = attn::decode_q_default_splits(batch, hq, hkv, max_len, k_bits);
+    if (splits * batch >= ((int64_t)1 << 31) || splits >= 65536 || batch >= 65536 || hkv * hq >= 65536 ||
+        batch * hkv * capacity * d >= ((int64_t)1 << 40))
+        return fail(ATTN_ERR_ARG, "problem too large for one launch");
+    const size_t need = attn::decode_workspace_bytes(batch, hq, d, splits);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+        if (!aligned16(workspace)) return fail(ATTN_ERR_ARG, "workspace is not 16-byte aligned");
+    }
+    const Span so = span(out, batch, hq * d, hq, d, 2);
+    const Span sw{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+    auto bytes_span = [](const void *ptr, int64_t n) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(ptr);
+        return Span{a, a + (uintptr_t)n};
+    };
+    const int64_t rows = batch * hkv * capacity;
+    if (overlap(so, span(q, batch, hq * d, hq, d, 2)) || overlap(so, sw) ||
+        overlap(so, bytes_span(k_codes, rows * d * k_bits / 8)) || overlap(so, bytes_span(v_codes, rows * d * v_bits / 8)) ||
+        overlap(so, bytes_span(k_params, rows * 8)) || overlap(so, bytes_span(v_params, rows * 8)))
+        return fail(ATTN_ERR_ARG, "out overlaps an input or the workspace");
+
+    attn::DecodeLaunch a{};
+    a.q = q; a.k = k_codes; a.v = v_codes; a.out = out;
+    a.batch = batch; a.hq = hq; a.hkv = hkv; a.d = d; a.capacity = capacity; a.max_len = max_len;
+    a.lens = lens; a.pos = pos;
+    a.prep_q = prep != nullptr;
+    if (prep) {
+        a.qw = prep->qw; a.cos = prep->cos; a.sin = prep->sin; a.half = prep->half;
+        a.table_rows = prep->table_rows; a.pairs = prep->pairs != 0; a.eps = (float)prep->eps;
+    }
+    a.scale = (float)scale; a.splits = splits; a.work = static_cast<float *>(workspace);
+    a.bf16 = true;
+    a.kpar = k_params; a.vpar = v_params; a.kbits = (int)k_bits; a.vbits = (int)v_bits;
+    return hip_status(attn::launch_decode(a, static_cast<hipStream_t>(stream)), "attn_decode_q");
 }
 
 }  // extern "C"

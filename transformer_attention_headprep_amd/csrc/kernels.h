@@ -87,12 +87,32 @@ struct DecodeLaunch {
     int64_t splits;
     float *work;                 // [splits][batch][hq] x (d + 2) f32 partials
     bool bf16;
+    // Quantised caches (kbits != 0): k and v hold codes [batch, hkv, capacity, d bits / 8]
+    // (kbits for k, vbits for v, in {8, 4, 2}), kpar / vpar the (lo, step) f32 pairs
+    // [batch, hkv, capacity, 2]; q and out are then bf16.
+    const float *kpar, *vpar;
+    int kbits, vbits;
 };
 hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream);
+hipError_t launch_decode_q(const DecodeLaunch &a, hipStream_t stream);
+
+// Quantised-cache coding of rows [0, seq) of `batch` sequences x [batch, seq, heads, d]
+// (row stride rs, batch stride seq * rs elements) into cache rows row0 .. row0 + seq - 1:
+// codes [batch, heads, capacity, d bits / 8], params [batch, heads, capacity, 2].
+struct KvQuantLaunch {
+    const void *x; int64_t rs;
+    int64_t batch, seq, heads, d;
+    int bits;
+    uint8_t *codes; float *params;
+    int64_t capacity, row0;
+    bool bf16;
+};
+hipError_t launch_kv_quantize(const KvQuantLaunch &a, hipStream_t stream);
 
 // Geometry of the decode split kernel, shared with the ABI layer's size queries.
 int64_t decode_heads_per_block(int64_t hq, int64_t hkv);
 int64_t decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len);
+int64_t decode_q_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len, int64_t kbits);
 size_t decode_workspace_bytes(int64_t batch, int64_t hq, int64_t d, int64_t splits);
 
 }  // namespace attn

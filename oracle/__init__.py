@@ -30,6 +30,11 @@ from .oracle import (  # noqa: F401
     prefill,
     prefill_chunk,
     attended_rows,
+    attended_rows8,
+    rows8_operands,
+    int8_code,
+    e4m3_code,
+    KEY_TILE,
     decode,
     decode_q,
     kv_quantize,

@@ -263,6 +263,72 @@ int oracle_kv_quantize(const float *x, int64_t units, int64_t d, int64_t bits, i
     return 0;
 }
 
+/*
+ * 8-bit operands of the quantised attention path (gizml:netops, Functions >
+ * attentionRows: with `quantized`, Q K^T on INT8 and P V on E4M3, SageAttention's split).
+ * Each unit of n f32 values shares one scale; every decision runs in f32 as written.
+ *   int8: s = amax / 127, code = clamp(rint(x * (1 / s)), -127, 127); amax = 0 gives s = 1,
+ *         codes 0.  The unit gives back code * s.
+ *   e4m3: s = amax / 448, value = the E4M3 number nearest to x * (1 / s) (ties to the even
+ *         code; 3 fraction bits, exponent bias 7, subnormal step 2^-9, largest 448), given
+ *         back times s.  amax = 0 gives s = 1, values 0.
+ */
+int oracle_int8_code(const float *x, int64_t units, int64_t n, int8_t *codes, float *scale)
+{
+    if (!x || !codes || !scale || units < 0 || n <= 0)
+        return -1;
+    for (int64_t u = 0; u < units; ++u) {
+        const float *xu = x + u * n;
+        float amax = 0.0f;
+        for (int64_t i = 0; i < n; ++i)
+            if (fabsf(xu[i]) > amax) amax = fabsf(xu[i]);
+        const float s = amax > 0.0f ? amax / 127.0f : 1.0f;
+        const float inv = 1.0f / s;
+        for (int64_t i = 0; i < n; ++i) {
+            float t = rintf(xu[i] * inv);
+            if (t < -127.0f) t = -127.0f;
+            if (t > 127.0f) t = 127.0f;
+            codes[u * n + i] = (int8_t)t;
+        }
+        scale[u] = s;
+    }
+    return 0;
+}
+
+/* The E4M3 number nearest to a (ties to even), a finite f32 with |a| <= 464. */
+static float e4m3_round(float a)
+{
+    const float m = fabsf(a);
+    float step;
+    if (m < 0.015625f) {                      /* below 2^-6: subnormal spacing 2^-9 */
+        step = 0.001953125f;
+    } else {
+        int e;
+        frexpf(m, &e);                        /* m = f 2^e, f in [0.5, 1) */
+        step = ldexpf(1.0f, e - 1 - 3);       /* 3 fraction bits below the leading one */
+    }
+    const float q = rintf(m / step) * step;   /* m / step and the product are exact */
+    return a < 0.0f ? -q : q;
+}
+
+int oracle_e4m3_code(const float *x, int64_t units, int64_t n, float *values, float *scale)
+{
+    if (!x || !values || !scale || units < 0 || n <= 0)
+        return -1;
+    for (int64_t u = 0; u < units; ++u) {
+        const float *xu = x + u * n;
+        float amax = 0.0f;
+        for (int64_t i = 0; i < n; ++i)
+            if (fabsf(xu[i]) > amax) amax = fabsf(xu[i]);
+        const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+        const float inv = 1.0f / s;
+        for (int64_t i = 0; i < n; ++i)
+            values[u * n + i] = e4m3_round(xu[i] * inv);
+        scale[u] = s;
+    }
+    return 0;
+}
+
 static void attend_one(const double *q, const double *k, const double *v, double *out,
                        int64_t b, int64_t i, int64_t h,
                        int64_t tq, int64_t tk, int64_t hq, int64_t hkv,

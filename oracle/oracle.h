@@ -95,6 +95,17 @@ int oracle_attention_rows(const double *q, const double *k, const double *v, dou
 int oracle_kv_quantize(const float *x, int64_t units, int64_t d, int64_t bits, int32_t *codes,
                        float *lo_out, float *step_out, int32_t *k_out);
 
+/*
+ * 8-bit operands of the quantised attention path (netops attentionRows with
+ * `quantized`): `units` groups of n f32 values (x [units, n]), one scale per group.
+ *   oracle_int8_code: s = amax / 127 (1 if amax = 0), code = clamp(rint(x (1/s)), -127, 127).
+ *   oracle_e4m3_code: s = amax / 448 (1 if amax = 0), values = E4M3 rounding (nearest,
+ *                     ties to even) of x (1/s), returned as floats (times s gives back x).
+ * Returns -1 on a bad argument.
+ */
+int oracle_int8_code(const float *x, int64_t units, int64_t n, int8_t *codes, float *scale);
+int oracle_e4m3_code(const float *x, int64_t units, int64_t n, float *values, float *scale);
+
 /* Number of OpenMP threads a parallel region of this library uses. */
 int oracle_threads(void);
 

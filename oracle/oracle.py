@@ -62,6 +62,11 @@ def _load():
         ip = ctypes.POINTER(ctypes.c_int32)
         lib.oracle_kv_quantize.argtypes = [fp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ip, fp, fp, ip]
         lib.oracle_kv_quantize.restype = ctypes.c_int
+        i8p = ctypes.POINTER(ctypes.c_int8)
+        lib.oracle_int8_code.argtypes = [fp, ctypes.c_int64, ctypes.c_int64, i8p, fp]
+        lib.oracle_int8_code.restype = ctypes.c_int
+        lib.oracle_e4m3_code.argtypes = [fp, ctypes.c_int64, ctypes.c_int64, fp, fp]
+        lib.oracle_e4m3_code.restype = ctypes.c_int
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
@@ -313,3 +318,94 @@ def decode_q(q, k_codes, k_lo, k_step, v_codes, v_lo, v_step, lens, pos, qw, cos
     lo + step * code per head (kv_dequantize), then the decode above.  Codes unpacked."""
     return decode(q, kv_dequantize(k_codes, k_lo, k_step), kv_dequantize(v_codes, v_lo, v_step), lens, pos,
                   qw, cos, sin, half, eps, scale)
+
+
+def int8_code(x):
+    """Symmetric int8 coding of each unit x[..., :] (f32 values): (codes int8 [...], scale
+    f32 [...[:-1]]) with scale amax / 127 and codes rint(x (1/scale)) clamped to +-127."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    n = x.shape[-1]
+    units = int(np.prod(x.shape[:-1], dtype=np.int64))
+    codes = np.zeros(x.shape, dtype=np.int8)
+    scale = np.zeros(x.shape[:-1], dtype=np.float32)
+    fp = ctypes.POINTER(ctypes.c_float)
+    rc = _load().oracle_int8_code(x.ctypes.data_as(fp), units, n, codes.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)),
+                                  scale.ctypes.data_as(fp))
+    if rc != 0:
+        raise ValueError("oracle_int8_code rejected its arguments (code %d)" % rc)
+    return codes, scale
+
+
+def e4m3_code(x):
+    """E4M3 coding of each unit x[..., :] (f32 values): (values f32 [...] -- the E4M3 numbers,
+    nearest with ties to even, of x (1/scale)), scale f32 [...[:-1]] = amax / 448)."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    n = x.shape[-1]
+    units = int(np.prod(x.shape[:-1], dtype=np.int64))
+    vals = np.zeros(x.shape, dtype=np.float32)
+    scale = np.zeros(x.shape[:-1], dtype=np.float32)
+    fp = ctypes.POINTER(ctypes.c_float)
+    rc = _load().oracle_e4m3_code(x.ctypes.data_as(fp), units, n, vals.ctypes.data_as(fp), scale.ctypes.data_as(fp))
+    if rc != 0:
+        raise ValueError("oracle_e4m3_code rejected its arguments (code %d)" % rc)
+    return vals, scale
+
+
+KEY_TILE = 64     # keys that share one int8 key scale (a tile of consecutive keys of a group)
+
+
+def rows8_operands(qkv, heads: int, head: int, group: int = 0, queries: int = 0, prep=None):
+    """The operands of attentionRows' quantized path (gizml:netops, Functions > attentionRows:
+    Q K^T on INT8, P V on E4M3): HeadPrep of q and k (row r at table row r) in f64, rounded to
+    f32; q coded in int8 per (row, head); k in int8 per (tile of 64 consecutive keys of a
+    group, head); v in E4M3 per (group, head).  Returns a dict of the codes and, per row and
+    head, the scales (q8, sq, k8, sk, v8 (E4M3 values as f32), sv) and the values they give
+    back (q_back, k_back, v_back, f64 [rows, heads, head])."""
+    x = np.asarray(qkv, dtype=np.float64)
+    n = x.shape[0]
+    x = x.reshape(n, 3, heads, head)
+    q, k, v = x[:, 0], x[:, 1], x[:, 2]
+    if prep is not None:
+        pos = np.arange(n, dtype=np.int64)
+        args = (prep["cos"], prep["sin"], prep["half"], pos, prep["eps"])
+        q = headprep(q, prep["qw"], *args, pairs=prep.get("pairs", False))
+        k = headprep(k, prep["kw"], *args, pairs=prep.get("pairs", False))
+    nq = queries if queries else n
+    g = group if 0 < group < n else n
+    q32, k32, v32 = q[:nq].astype(np.float32), k.astype(np.float32), v.astype(np.float32)
+    q8, sq = int8_code(q32)
+    k8 = np.zeros((n, heads, head), np.int8)
+    sk = np.zeros((n, heads), np.float32)
+    v8 = np.zeros((n, heads, head), np.float32)
+    sv = np.zeros((n, heads), np.float32)
+    for lo in range(0, n, g):
+        hi = min(lo + g, n)
+        vals, s = e4m3_code(np.ascontiguousarray(v32[lo:hi].transpose(1, 0, 2)).reshape(heads, -1))
+        v8[lo:hi] = vals.reshape(heads, hi - lo, head).transpose(1, 0, 2)
+        sv[lo:hi] = s[None, :]
+        for t0 in range(lo, hi, KEY_TILE):
+            t1 = min(t0 + KEY_TILE, hi)
+            c, s = int8_code(np.ascontiguousarray(k32[t0:t1].transpose(1, 0, 2)).reshape(heads, -1))
+            k8[t0:t1] = c.reshape(heads, t1 - t0, head).transpose(1, 0, 2)
+            sk[t0:t1] = s[None, :]
+    return dict(q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, q32=q32, k32=k32,
+                q_back=q8.astype(np.float64) * sq[..., None], k_back=k8.astype(np.float64) * sk[..., None],
+                v_back=v8.astype(np.float64) * sv[..., None])
+
+
+def attended_rows8(ops, heads: int, head: int, group: int = 0, queries: int = 0):
+    """attentionRows over the values 8-bit operands give back (rows8_operands), in f64 with
+    an exact softmax: out [nq, heads head]; and the per-element sum_j p_j |v_j| (same
+    shape), which bounds what rounding the weights p changes in out."""
+    n = ops["k_back"].shape[0]
+    nq = queries if queries else n
+    g = group if 0 < group < n else n
+    out = np.zeros((nq, heads, head))
+    bound = np.zeros((nq, heads, head))
+    qb, kb, vb = ops["q_back"], ops["k_back"], ops["v_back"]
+    for lo in range(0, nq, g):
+        hi, qhi = min(lo + g, n), min(lo + g, nq)
+        args = (1.0 / np.sqrt(head), False)
+        out[lo:qhi] = attention(qb[None, lo:qhi], kb[None, lo:hi], vb[None, lo:hi], *args)[0]
+        bound[lo:qhi] = attention(qb[None, lo:qhi], kb[None, lo:hi], np.abs(vb[None, lo:hi]), *args)[0]
+    return out.reshape(nq, heads * head), bound.reshape(nq, heads * head)

@@ -46,6 +46,11 @@ MUTANTS = {
     "kv: step over 2^bits levels": ("*st = (hw + hw) / (float)top;", "*st = (hw + hw) / (float)(top + 1);"),
     "kv: range starts at the minimum": ("*lo = centre - hw;", "*lo = centre - r;"),
     "kv: the largest error wins": ("if (sse < best) {", "if (sse > best || best == INFINITY) {"),
+    "int8: scale over 128": ("const float s = amax > 0.0f ? amax / 127.0f : 1.0f;",
+                             "const float s = amax > 0.0f ? amax / 128.0f : 1.0f;"),
+    "int8: codes truncated": ("float t = rintf(xu[i] * inv);", "float t = truncf(xu[i] * inv);"),
+    "e4m3: two fraction bits": ("step = ldexpf(1.0f, e - 1 - 3);", "step = ldexpf(1.0f, e - 1 - 2);"),
+    "e4m3: ties away from zero": ("const float q = rintf(m / step) * step;", "const float q = roundf(m / step) * step;"),
     "value of wrong key": ("const double *vj = v + ((b * tk + j) * hkv + g) * dv;",
                            "const double *vj = v + ((b * tk + (j ? j - 1 : 0)) * hkv + g) * dv;"),
 }

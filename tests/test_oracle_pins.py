@@ -546,6 +546,87 @@ def test_kv_quantize_constant_head_and_fewer_bits_more_error():
     assert 0.5 < errs[0] / ((5.5 / 255) ** 2 / 12) < 2.0
 
 
+# ------------------------------------------------------------ 8-bit attention operands
+
+def test_e4m3_rounding_is_torch_float8_e4m3fn():
+    """E4M3 coding = torch's float8_e4m3fn conversion (nearest, ties to even) of x (1/s), on
+    every E4M3 number, every midpoint and its neighbours, and random values, with s = 1
+    (units whose largest magnitude is 448)."""
+    codes = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    mids = (codes[:-1] + codes[1:]) / 2
+    xs = np.concatenate([codes, mids, np.nextafter(mids, 1e9, dtype=np.float32),
+                         np.nextafter(mids, -1e9, dtype=np.float32),
+                         RNG.uniform(-448, 448, 4000).astype(np.float32)]).astype(np.float32)
+    xs = np.concatenate([xs, -xs])
+    n = 448
+    units = []
+    for i in range(0, len(xs), n - 1):
+        u = np.zeros(n, np.float32)
+        chunk = xs[i:i + n - 1]
+        u[:len(chunk)] = chunk
+        u[-1] = 448.0                       # every unit's largest magnitude: scale 1
+        units.append(u)
+    units = np.stack(units)
+    vals, scale = oracle.e4m3_code(units)
+    assert (scale == 1.0).all()
+    ref = torch.from_numpy(units).to(torch.float8_e4m3fn).float().numpy()
+    np.testing.assert_array_equal(vals, ref)
+
+
+def test_int8_coding():
+    x = (RNG.standard_normal((40, 128)) * RNG.uniform(0.01, 100, (40, 1))).astype(np.float32)
+    codes, scale = oracle.int8_code(x)
+    amax = np.abs(x).max(axis=1)
+    np.testing.assert_array_equal(scale, (amax / np.float32(127)).astype(np.float32))
+    inv = (np.float32(1) / scale).astype(np.float32)
+    np.testing.assert_array_equal(codes, np.clip(np.rint(x * inv[:, None]), -127, 127).astype(np.int8))
+    assert np.abs(codes).max() == 127
+    back = codes.astype(np.float64) * scale[:, None]
+    assert (np.abs(back - x) <= 0.5 * scale[:, None] * (1 + 1e-6)).all()
+    c0, s0 = oracle.int8_code(np.zeros((1, 8), np.float32))
+    assert (c0 == 0).all() and s0[0] == 1.0
+
+
+def test_rows8_operands_are_exact_on_exact_inputs():
+    """Rows whose q and k are multiples of their unit's scale (largest magnitude 127 of them)
+    and whose v lie on the E4M3 grid of their group's scale come back unchanged, so the
+    8-bit attention equals the exact one; this pins the units (q per row, k per 64-key
+    tile restarting at every group, v per group) and the composition."""
+    n, heads, head, group = 150, 2, 16, 100
+    rng = np.random.default_rng(8)
+    x = np.zeros((n, 3, heads, head), np.float32)
+    x[:, 0] = rng.integers(-126, 127, (n, heads, head)) * np.float32(2.0 ** -6)
+    x[:, 0, :, 0] = 127 * np.float32(2.0 ** -6)                    # q: every row's max 127 s
+    x[:, 1] = rng.integers(-126, 127, (n, heads, head)) * np.float32(2.0 ** -5)
+    for t0 in (0, 64, 100):                                          # tiles 0-63, 64-99, 100-149
+        x[t0, 1, :, 1] = 127 * np.float32(2.0 ** -5)
+    grid = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    x[:, 2] = rng.choice(np.concatenate([grid, -grid]), (n, heads, head)) * np.float32(2.0 ** -4)
+    x[0, 2, :, 0] = x[100, 2, :, 0] = 448 * np.float32(2.0 ** -4)    # each group's v max
+    ops = oracle.rows8_operands(x.reshape(n, -1), heads, head, group)
+    np.testing.assert_array_equal(ops["q_back"], x[:, 0])
+    np.testing.assert_array_equal(ops["k_back"], x[:, 1])
+    np.testing.assert_array_equal(ops["v_back"], x[:, 2])
+    assert len(np.unique(ops["sk"][:, 0])) == 1                      # one k scale (same max)
+    out8, _ = oracle.attended_rows8(ops, heads, head, group)
+    ref, _, _ = oracle.attended_rows(x.reshape(n, -1), heads, head, group)
+    np.testing.assert_allclose(out8, ref, rtol=0, atol=1e-13)
+
+
+def test_rows8_key_tiles_restart_at_groups():
+    n, heads, head, group = 150, 1, 8, 100
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((n, 3 * heads * head)).astype(np.float32)
+    x[70, heads * head:2 * heads * head] *= 50        # a large key in tile 64..99 only
+    ops = oracle.rows8_operands(x, heads, head, group)
+    sk = ops["sk"][:, 0]
+    assert (sk[64:100] == sk[70]).all()
+    assert sk[70] > 10 * sk[0] and sk[70] > 10 * sk[100]
+    assert (sk[:64] == sk[0]).all() and (sk[100:150] == sk[100]).all()
+    sv = ops["sv"][:, 0]
+    assert (sv[:100] == sv[0]).all() and (sv[100:] == sv[100]).all()
+
+
 # ------------------------------------------------------------------- input generation
 
 def test_bf16_rounding_matches_torch():

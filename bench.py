@@ -19,7 +19,8 @@ against caches coded in 8/8, 4/4 and 4/2 bits (attn_decode_q; GB/s of the codes,
 ranges, q and out); packed rows of an
 image model (attn_rows: 4608 rows of 24 heads of 128, HeadPrep with adjacent pairs in
 place -- repeated calls re-prep the same buffer, which changes values, not work -- then
-full attention); the whole-row norm + per-head rotary of 6240 rows of 4096
+full attention), and the same rows through the quantised path (attn_rows8: 8-bit coding
+pass + Q K^T on INT8, P V on E4M3); the whole-row norm + per-head rotary of 6240 rows of 4096
 (attn_row_norm_rope, in place, GB/s of one read and one write plus the tables); then two
 calibration kernels (libpeak.so: a bf16 MFMA loop and a streaming read) give measured
 ceilings next to the published ones.
@@ -48,6 +49,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E (published)
+PEAK_8BIT_TFLOPS = 5000.0      # MI355X dense int8 / fp8 MFMA (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -395,6 +397,22 @@ def main() -> int:
                                  "of 128, full attention, HeadPrep with adjacent pairs in place)",
                      "value": round(tf7, 3), "unit": "TFLOP/s", "calls": args.rows_calls,
                      "ms": stats_ms(ms7), "flops": flops7, "frac_of_bf16_peak": round(tf7 / PEAK_BF16_TFLOPS, 4)}
+        # the same rows through the quantised path: HeadPrep + 8-bit coding pass, then
+        # Q K^T on INT8 and P V on E4M3 (qkv is not written)
+        total8, _ = tah.rows8_layout(n7, heads7, head7)
+        ws8 = torch.empty(total8, dtype=torch.uint8, device=dev)
+        ms8a = time_calls(lambda: tah.attn_rows8(qkv7, heads7, head7, out=out7, prep=prep7, workspace=ws8,
+                                                 stream=stream), args.rows_calls)
+        ms8b = time_calls(lambda: tah.attn_rows8_attend(ws8, n7, heads7, head7, out=out7, stream=stream),
+                          args.rows_calls)
+        tf8a = flops7 / (ms8a.mean() * 1e-3) / 1e12
+        tf8b = flops7 / (ms8b.mean() * 1e-3) / 1e12
+        rows_line["quantized"] = {
+            "value": round(tf8a, 3), "unit": "TFLOP/s", "ms": stats_ms(ms8a),
+            "attention_only": {"value": round(tf8b, 3), "ms": stats_ms(ms8b),
+                               "frac_of_int8_fp8_peak": round(tf8b / PEAK_8BIT_TFLOPS, 4)},
+            "speedup_vs_bf16": round(float(ms7.mean() / ms8a.mean()), 3)}
+        del ws8
         del qkv7, out7
         torch.cuda.empty_cache()
 

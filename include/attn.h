@@ -276,6 +276,45 @@ attn_status_t attn_rows(void *qkv, int64_t n, int64_t heads, int64_t head, int64
                         attn_dtype_t dtype, void *stream);
 
 /*
+ * attn_rows8 -- attn_rows' quantised path (gizml:netops, Functions > attentionRows with
+ * `quantized`: Q K^T on INT8, P V on E4M3 -- SageAttention's split -- with the head norm and
+ * rotary applied in the quantizing pass; qkv is not written).  Same qkv, n, heads, head,
+ * group, queries, out and prep as attn_rows (bf16 only, head in {64, 128}; prep: split
+ * halves with half = head / 2 or 0, or adjacent pairs with any half); then:
+ *   1. the quantizing pass writes the 8-bit operands into `workspace`:
+ *        q8   int8 [nq, heads, head]   q after HeadPrep, one scale per (row, head):
+ *        sq   f32  [nq, heads]         s = amax / 127, code = rint(x * (1 / s)) in [-127, 127]
+ *        k8   int8 [n, heads, head]    k after HeadPrep, one scale per (tile, head), a tile
+ *        sk   f32  [G, T, heads]       being 64 consecutive keys of a group (T tiles a group)
+ *        v8t  E4M3 [G, T, heads, head, 64]  v over one scale per (group, head), s = amax /
+ *        sv   f32  [G, heads]          448, nearest E4M3 of x * (1 / s), ties to even; row e
+ *                                      of a tile's block holds value e of the tile's keys,
+ *                                      position 32 g + b holding key
+ *                                      32 (b / 16) + 8 ((b % 16) / 4) + 4 g + b % 4 (g < 2,
+ *                                      b < 32); keys past the group's end are 0
+ *        vmax u32  [G, heads]          scratch
+ *      (G groups, nq = queries or n; an amax of 0 gives s = 1);
+ *   2. out = softmax(q k^T / sqrt(head)) v over the values these give back, the weights
+ *      carried as E4M3 numbers 2^(s - m) 448 with the running max m.
+ * attn_rows8_layout fills offsets[0..6] with the byte offsets of q8, sq, k8, sk, v8t, sv,
+ * vmax (256-byte aligned) and returns the workspace size (0 for bad sizes).
+ * attn_rows8_quantize runs step 1 only, attn_rows8_attend step 2 only (on operands already
+ * in the workspace), attn_rows8 both.  workspace: device memory of at least the layout's
+ * size, 16-byte aligned, not overlapping qkv or out; calls sharing it must not overlap.
+ */
+size_t attn_rows8_layout(int64_t n, int64_t heads, int64_t head, int64_t group, int64_t queries,
+                         int64_t *offsets);
+attn_status_t attn_rows8_quantize(const void *qkv, int64_t n, int64_t heads, int64_t head,
+                                  int64_t group, int64_t queries, const attn_headprep_t *prep,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+attn_status_t attn_rows8_attend(const void *workspace, size_t workspace_bytes, int64_t n,
+                                int64_t heads, int64_t head, int64_t group, int64_t queries,
+                                void *out, void *stream);
+attn_status_t attn_rows8(const void *qkv, int64_t n, int64_t heads, int64_t head, int64_t group,
+                         int64_t queries, void *out, const attn_headprep_t *prep, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/*
  * attn_row_norm_rope -- a norm over the whole row followed by a per-head rotary, in
  * place (gizml:netops, Functions > rowNormRopeInto: LTX's QK norm, which spans every
  * head of a row, then its rotary).  For each row r of x:

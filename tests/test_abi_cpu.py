@@ -22,7 +22,7 @@ def lib():
 def _declared_functions():
     src = open(os.path.join(ROOT, "include", "attn.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -336,3 +336,48 @@ def test_decode_q_default_splits(lib):
 
 def test_decode_q_empty_is_a_no_op(lib):
     assert _decq(lib, batch=0) == A.ATTN_OK
+
+
+def test_rows8_layout(lib):
+    total, off = A.rows8_layout(300, 4, 128, group=128, queries=200)
+    # 3 groups of 128 rows (the last 44), 2 key tiles and 1 query tile a group
+    sizes = dict(q8=200 * 4 * 128, sq=200 * 4 * 4, k8=300 * 4 * 128, sk=3 * 2 * 4 * 4, v8t=3 * 2 * 4 * 128 * 64,
+                 sv=3 * 4 * 4, vmax=3 * 4 * 4)
+    at = 0
+    for part in A.ROWS8_PARTS:
+        assert off[part] == at and at % 256 == 0
+        at += (sizes[part] + 255) // 256 * 256
+    assert total == at
+    assert lib.attn_rows8_layout(300, 4, 96, 0, 0, None) == 0          # head not 64 or 128
+    assert lib.attn_rows8_layout(300, 4, 128, 0, 301, None) == 0       # queries > n
+
+
+def _rows8(lib, **kw):
+    a = dict(qkv=FAKE, n=300, heads=4, head=128, group=0, queries=0, out=FAKE + (1 << 32), prep=_prep(),
+             ws=FAKE + (2 << 32), wsb=1 << 30)
+    a.update(kw)
+    prep = ctypes.byref(a["prep"]) if a["prep"] is not None else None
+    return lib.attn_rows8(a["qkv"], a["n"], a["heads"], a["head"], a["group"], a["queries"], a["out"], prep, a["ws"],
+                          a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head=96), A.ATTN_ERR_UNSUPPORTED),
+    (dict(prep=_prep(half=32)), A.ATTN_ERR_UNSUPPORTED),      # split halves other than head / 2
+    (dict(qkv=None), A.ATTN_ERR_ARG),
+    (dict(out=None), A.ATTN_ERR_ARG),
+    (dict(ws=None), A.ATTN_ERR_WORKSPACE),
+    (dict(wsb=1000), A.ATTN_ERR_WORKSPACE),
+    (dict(ws=FAKE + (2 << 32) + 8), A.ATTN_ERR_ARG),         # misaligned
+    (dict(queries=301), A.ATTN_ERR_ARG),
+    (dict(group=-1), A.ATTN_ERR_ARG),
+    (dict(ws=FAKE + 4096), A.ATTN_ERR_ARG),                  # workspace overlaps qkv
+    (dict(prep=_prep(rows=100)), A.ATTN_ERR_ARG),             # table shorter than n
+])
+def test_rows8_rejects(lib, kw, code):
+    assert _rows8(lib, **kw) == code
+    assert lib.attn_last_error()
+
+
+def test_rows8_empty_is_a_no_op(lib):
+    assert _rows8(lib, n=0) == A.ATTN_OK

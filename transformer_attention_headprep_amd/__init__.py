@@ -18,6 +18,10 @@ from .attn import (  # noqa: F401
     attn_prep,
     attn_row_norm_rope,
     attn_rows,
+    attn_rows8,
+    attn_rows8_attend,
+    attn_rows8_quantize,
+    rows8_layout,
     attn_supported,
     decode_default_splits,
     decode_q_default_splits,

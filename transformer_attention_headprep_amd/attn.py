@@ -21,7 +21,8 @@ ATTN_OK, ATTN_ERR_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 
 
 # The entry points include/attn.h declares (checked by the CPU test suite).
 EXPORTS = ("attn_prep", "attn_prefill", "attn_prefill_chunk", "attn_decode", "attn_decode_workspace_size",
-           "attn_decode_default_splits", "attn_kv_quantize", "attn_decode_q", "attn_decode_q_default_splits", "attn_rows", "attn_row_norm_rope", "attn_supported", "attn_status_str",
+           "attn_decode_default_splits", "attn_kv_quantize", "attn_decode_q", "attn_decode_q_default_splits", "attn_rows", "attn_rows8_layout", "attn_rows8_quantize",
+           "attn_rows8_attend", "attn_rows8", "attn_row_norm_rope", "attn_supported", "attn_status_str",
            "attn_last_error")
 
 
@@ -73,6 +74,14 @@ def load_library(path: str = LIB_PATH):
     lib.attn_decode_q.restype = ctypes.c_int
     lib.attn_decode_q_default_splits.argtypes = [_i64] * 5
     lib.attn_decode_q_default_splits.restype = _i64
+    lib.attn_rows8_layout.argtypes = [_i64] * 5 + [_vp]
+    lib.attn_rows8_layout.restype = ctypes.c_size_t
+    lib.attn_rows8_quantize.argtypes = [_vp] + [_i64] * 5 + [hp, _vp, ctypes.c_size_t, _vp]
+    lib.attn_rows8_quantize.restype = ctypes.c_int
+    lib.attn_rows8_attend.argtypes = [_vp, ctypes.c_size_t] + [_i64] * 5 + [_vp, _vp]
+    lib.attn_rows8_attend.restype = ctypes.c_int
+    lib.attn_rows8.argtypes = [_vp] + [_i64] * 5 + [_vp, hp, _vp, ctypes.c_size_t, _vp]
+    lib.attn_rows8.restype = ctypes.c_int
     lib.attn_rows.argtypes = [_vp] + [_i64] * 5 + [_vp, hp, ctypes.c_int, _vp]
     lib.attn_rows.restype = ctypes.c_int
     lib.attn_row_norm_rope.argtypes = [_vp] + [_i64] * 4 + [_vp, _vp, _vp, _dbl, ctypes.c_int, _vp]
@@ -295,6 +304,59 @@ def attn_rows(qkv, heads: int, head: int, group: int = 0, queries: int = 0, out=
     st = prep.struct() if prep is not None else None
     _check(lib.attn_rows(_ptr(qkv), n, heads, head, group, queries, _ptr(out),
                          ctypes.byref(st) if st is not None else None, _dtype_code(qkv), _stream(stream)))
+    return out
+
+
+ROWS8_PARTS = ("q8", "sq", "k8", "sk", "v8t", "sv", "vmax")
+
+
+def rows8_layout(n: int, heads: int, head: int, group: int = 0, queries: int = 0):
+    """(workspace bytes, {part: byte offset}) of the quantised rows path's workspace."""
+    offs = (ctypes.c_int64 * 7)()
+    total = int(load_library().attn_rows8_layout(n, heads, head, group, queries, offs))
+    if total == 0:
+        raise ValueError("bad sizes for the quantised rows path")
+    return total, dict(zip(ROWS8_PARTS, list(offs)))
+
+
+def attn_rows8(qkv, heads: int, head: int, group: int = 0, queries: int = 0, out=None, prep: HeadPrep | None = None,
+               workspace=None, stream=None) -> torch.Tensor:
+    """attn_rows' quantised path: 8-bit operands (coded with HeadPrep in the quantizing pass,
+    qkv untouched), Q K^T on INT8 and P V on E4M3; out [queries or n, heads * head] bf16."""
+    lib = load_library()
+    if qkv.dtype != torch.bfloat16 or qkv.dim() != 2 or not qkv.is_contiguous() or qkv.shape[1] != 3 * heads * head:
+        raise ValueError("qkv must be a contiguous bf16 [n, 3 * heads * head] tensor")
+    n = qkv.shape[0]
+    nq = queries if queries else n
+    if out is None:
+        out = torch.empty(nq, heads * head, dtype=torch.bfloat16, device=qkv.device)
+    total, _ = rows8_layout(n, heads, head, group, queries)
+    if workspace is None:
+        workspace = torch.empty(total, dtype=torch.uint8, device=qkv.device)
+    st = prep.struct() if prep is not None else None
+    _check(lib.attn_rows8(_ptr(qkv), n, heads, head, group, queries, _ptr(out),
+                          ctypes.byref(st) if st is not None else None, _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def attn_rows8_quantize(qkv, heads: int, head: int, workspace, group: int = 0, queries: int = 0,
+                        prep: HeadPrep | None = None, stream=None) -> None:
+    lib = load_library()
+    st = prep.struct() if prep is not None else None
+    _check(lib.attn_rows8_quantize(_ptr(qkv), qkv.shape[0], heads, head, group, queries,
+                                   ctypes.byref(st) if st is not None else None, _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attn_rows8_attend(workspace, n: int, heads: int, head: int, group: int = 0, queries: int = 0, out=None,
+                      stream=None) -> torch.Tensor:
+    lib = load_library()
+    nq = queries if queries else n
+    if out is None:
+        out = torch.empty(nq, heads * head, dtype=torch.bfloat16, device=workspace.device)
+    _check(lib.attn_rows8_attend(_ptr(workspace), workspace.numel() * workspace.element_size(), n, heads, head, group,
+                                 queries, _ptr(out), _stream(stream)))
     return out
 
 

@@ -22,13 +22,14 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libattn.so")
 PEAK_OUT = os.path.join(PKG, "libpeak.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["attn_api.cpp", "prep.hip", "prefill_f32.hip", "prefill_bf16.hip", "decode.hip", "kvq.hip"]
+SOURCES = ["attn_api.cpp", "prep.hip", "prefill_f32.hip", "prefill_bf16.hip", "decode.hip", "kvq.hip", "rows8.hip"]
 PEAK_SOURCES = ["peak.hip"]
 # Per-source flags.  The bf16 prefill kernel never sees NaN operands in valid use, so it
 # drops NaN quieting: row maxima become single v_max3 instructions.
 # The quantised-cache coding decides integer codes in f32 in the order it is written (the
 # same order the checker uses), so that file forbids fusing a multiply into an add.
-EXTRA = {"prefill_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"], "kvq.hip": ["-ffp-contract=off"]}
+EXTRA = {"prefill_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"], "kvq.hip": ["-ffp-contract=off"],
+         "rows8.hip": ["-ffp-contract=off"]}
 ARCH = "gfx950"
 
 

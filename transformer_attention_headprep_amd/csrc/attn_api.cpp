@@ -85,9 +85,120 @@ attn_status_t check_prep(const attn_headprep_t *p, int64_t d, bool need_qw, bool
     return ATTN_OK;
 }
 
+// Geometry and workspace layout of the quantised rows path (see attn_rows8 in attn.h).
+struct Rows8Geo {
+    int64_t nq, G, groups, tiles, qtiles;
+    int64_t off[7];
+    size_t total;
+};
+
+bool rows8_geo(int64_t n, int64_t heads, int64_t head, int64_t group, int64_t queries, Rows8Geo &g) {
+    if (n <= 0 || heads <= 0 || (head != 64 && head != 128) || group < 0 || queries < 0 || queries > n) return false;
+    g.nq = queries ? queries : n;
+    g.G = (group == 0 || group > n) ? n : group;
+    g.groups = (n + g.G - 1) / g.G;
+    g.tiles = (g.G + 63) / 64;
+    g.qtiles = (g.G + 127) / 128;
+    const int64_t sizes[7] = {g.nq * heads * head, g.nq * heads * 4, n * heads * head, g.groups * g.tiles * heads * 4,
+                              g.groups * g.tiles * heads * head * 64, g.groups * heads * 4, g.groups * heads * 4};
+    int64_t at = 0;
+    for (int i = 0; i < 7; ++i) {
+        g.off[i] = at;
+        at += (sizes[i] + 255) / 256 * 256;
+    }
+    g.total = (size_t)at;
+    return true;
+}
+
+attn_status_t rows8_launch(const void *qkv, int64_t n, int64_t heads, int64_t head, int64_t group, int64_t queries,
+                           void *out, const attn_headprep_t *prep, const void *workspace, size_t workspace_bytes,
+                           bool quantize, bool attend, void *stream) {
+    attn_status_t st;
+    if (n < 0) return fail(ATTN_ERR_ARG, "n < 0");
+    if (head != 64 && head != 128) return fail(ATTN_ERR_UNSUPPORTED, "head %lld not in {64, 128}", (long long)head);
+    if (heads <= 0) return fail(ATTN_ERR_ARG, "heads <= 0");
+    if (group < 0) return fail(ATTN_ERR_ARG, "group < 0");
+    if (queries < 0 || queries > n) return fail(ATTN_ERR_ARG, "queries %lld outside [0, n = %lld]", (long long)queries, (long long)n);
+    const int64_t rs = 3 * heads * head;
+    if (quantize && (st = check_rows("qkv", qkv, 3 * heads, head, rs))) return st;
+    if (attend && (st = check_rows("out", out, heads, head, heads * head))) return st;
+    int mode = 0;
+    if (quantize && prep) {
+        if ((st = check_prep(prep, head, true, true, 0, n))) return st;
+        if (prep->half > 0) {
+            if (prep->pairs) mode = 2;
+            else if (2 * prep->half == head) mode = 1;
+            else return fail(ATTN_ERR_UNSUPPORTED, "the quantised path turns split halves only with half = head / 2");
+        } else {
+            mode = 1;   // norm and weight only
+        }
+    }
+    if (n == 0) return ATTN_OK;
+    Rows8Geo geo;
+    rows8_geo(n, heads, head, group, queries, geo);
+    if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is NULL");
+    if (workspace_bytes < geo.total)
+        return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, geo.total);
+    if (!aligned16(workspace)) return fail(ATTN_ERR_ARG, "workspace is not 16-byte aligned");
+    if (geo.groups * geo.tiles >= ((int64_t)1 << 31) || heads >= 65536 || n >= ((int64_t)1 << 31))
+        return fail(ATTN_ERR_ARG, "problem too large for one launch");
+    const Span sw{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + geo.total};
+    if (quantize && overlap(sw, span(qkv, n, rs, 3 * heads, head, 2))) return fail(ATTN_ERR_ARG, "workspace overlaps qkv");
+    if (attend && overlap(sw, span(out, geo.nq, heads * head, heads, head, 2))) return fail(ATTN_ERR_ARG, "workspace overlaps out");
+    if (quantize && attend && overlap(span(out, geo.nq, heads * head, heads, head, 2), span(qkv, n, rs, 3 * heads, head, 2)))
+        return fail(ATTN_ERR_ARG, "out overlaps qkv");
+    uint8_t *ws = static_cast<uint8_t *>(const_cast<void *>(workspace));
+    attn::Rows8Launch a{};
+    a.qkv = qkv; a.n = n; a.nq = geo.nq; a.heads = heads; a.d = head; a.group = geo.G; a.groups = geo.groups;
+    a.tiles = geo.tiles; a.qtiles = geo.qtiles;
+    a.prep_mode = mode;
+    if (quantize && prep) {
+        a.qw = prep->qw; a.kw = prep->kw; a.cos = prep->cos; a.sin = prep->sin;
+        a.half = (int)prep->half; a.eps = (float)prep->eps;
+    }
+    a.q8 = reinterpret_cast<int8_t *>(ws + geo.off[0]); a.sq = reinterpret_cast<float *>(ws + geo.off[1]);
+    a.k8 = reinterpret_cast<int8_t *>(ws + geo.off[2]); a.sk = reinterpret_cast<float *>(ws + geo.off[3]);
+    a.v8t = ws + geo.off[4]; a.sv = reinterpret_cast<float *>(ws + geo.off[5]);
+    a.vmax = reinterpret_cast<uint32_t *>(ws + geo.off[6]);
+    a.out = out; a.scale = (float)(1.0 / std::sqrt((double)head));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (quantize && (st = hip_status(attn::launch_rows8_quantize(a, s), "attn_rows8 (quantize)"))) return st;
+    if (attend && (st = hip_status(attn::launch_rows8_attend(a, s), "attn_rows8 (attend)"))) return st;
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t attn_rows8_layout(int64_t n, int64_t heads, int64_t head, int64_t group, int64_t queries, int64_t *offsets) {
+    Rows8Geo geo;
+    if (!rows8_geo(n, heads, head, group, queries, geo)) return 0;
+    if (offsets)
+        for (int i = 0; i < 7; ++i) offsets[i] = geo.off[i];
+    return geo.total;
+}
+
+attn_status_t attn_rows8_quantize(const void *qkv, int64_t n, int64_t heads, int64_t head, int64_t group,
+                                  int64_t queries, const attn_headprep_t *prep, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+    g_last_error[0] = 0;
+    return rows8_launch(qkv, n, heads, head, group, queries, nullptr, prep, workspace, workspace_bytes, true, false,
+                        stream);
+}
+
+attn_status_t attn_rows8_attend(const void *workspace, size_t workspace_bytes, int64_t n, int64_t heads, int64_t head,
+                                int64_t group, int64_t queries, void *out, void *stream) {
+    g_last_error[0] = 0;
+    return rows8_launch(nullptr, n, heads, head, group, queries, out, nullptr, workspace, workspace_bytes, false, true,
+                        stream);
+}
+
+attn_status_t attn_rows8(const void *qkv, int64_t n, int64_t heads, int64_t head, int64_t group, int64_t queries,
+                         void *out, const attn_headprep_t *prep, void *workspace, size_t workspace_bytes, void *stream) {
+    g_last_error[0] = 0;
+    return rows8_launch(qkv, n, heads, head, group, queries, out, prep, workspace, workspace_bytes, true, true, stream);
+}
 
 const char *attn_last_error(void) { return g_last_error; }
 

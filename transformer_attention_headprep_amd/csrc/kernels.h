@@ -96,6 +96,26 @@ struct DecodeLaunch {
 hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream);
 hipError_t launch_decode_q(const DecodeLaunch &a, hipStream_t stream);
 
+// attentionRows' quantised path over packed rows qkv [n, 3 heads d] (bf16): groups of
+// `group` rows (the last may be shorter), `tiles` 64-key tiles and `qtiles` 128-row query
+// tiles per group; the first nq rows are queries.  The quantizing pass writes q8 [nq, heads,
+// d] + sq [nq, heads], k8 [n, heads, d] + sk [groups, tiles, heads], v8t [groups, tiles,
+// heads, d, 64] (E4M3, keys of a tile in the order the P V product takes them) + sv [groups,
+// heads], using vmax [groups, heads] as scratch; the attention reads them and writes out
+// [nq, heads d] (bf16).  prep_mode: 0 none, 1 split halves with half = d / 2, 2 pairs.
+struct Rows8Launch {
+    const void *qkv;
+    int64_t n, nq, heads, d, group, groups, tiles, qtiles;
+    const float *qw, *kw, *cos, *sin;
+    int half, prep_mode;
+    float eps;
+    int8_t *q8; float *sq; int8_t *k8; float *sk; uint8_t *v8t; float *sv; uint32_t *vmax;
+    void *out;
+    float scale;
+};
+hipError_t launch_rows8_quantize(const Rows8Launch &a, hipStream_t stream);
+hipError_t launch_rows8_attend(const Rows8Launch &a, hipStream_t stream);
+
 // Quantised-cache coding of rows [0, seq) of `batch` sequences x [batch, seq, heads, d]
 // (row stride rs, batch stride seq * rs elements) into cache rows row0 .. row0 + seq - 1:
 // codes [batch, heads, capacity, d bits / 8], params [batch, heads, capacity, 2].

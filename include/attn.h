@@ -292,7 +292,7 @@ attn_status_t attn_rows(void *qkv, int64_t n, int64_t heads, int64_t head, int64
  *                                      position 32 g + b holding key
  *                                      32 (b / 16) + 8 ((b % 16) / 4) + 4 g + b % 4 (g < 2,
  *                                      b < 32); keys past the group's end are 0
- *        vmax u32  [G, heads]          scratch
+ *        vmax f32  [G, T, heads]       scratch (each tile's amax of v)
  *      (G groups, nq = queries or n; an amax of 0 gives s = 1);
  *   2. out = softmax(q k^T / sqrt(head)) v over the values these give back, the weights
  *      carried as E4M3 numbers 2^(s - m) 448 with the running max m.

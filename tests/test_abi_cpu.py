@@ -342,7 +342,7 @@ def test_rows8_layout(lib):
     total, off = A.rows8_layout(300, 4, 128, group=128, queries=200)
     # 3 groups of 128 rows (the last 44), 2 key tiles and 1 query tile a group
     sizes = dict(q8=200 * 4 * 128, sq=200 * 4 * 4, k8=300 * 4 * 128, sk=3 * 2 * 4 * 4, v8t=3 * 2 * 4 * 128 * 64,
-                 sv=3 * 4 * 4, vmax=3 * 4 * 4)
+                 sv=3 * 4 * 4, vmax=3 * 2 * 4 * 4)
     at = 0
     for part in A.ROWS8_PARTS:
         assert off[part] == at and at % 256 == 0

@@ -100,7 +100,7 @@ bool rows8_geo(int64_t n, int64_t heads, int64_t head, int64_t group, int64_t qu
     g.tiles = (g.G + 63) / 64;
     g.qtiles = (g.G + 127) / 128;
     const int64_t sizes[7] = {g.nq * heads * head, g.nq * heads * 4, n * heads * head, g.groups * g.tiles * heads * 4,
-                              g.groups * g.tiles * heads * head * 64, g.groups * heads * 4, g.groups * heads * 4};
+                              g.groups * g.tiles * heads * head * 64, g.groups * heads * 4, g.groups * g.tiles * heads * 4};
     int64_t at = 0;
     for (int i = 0; i < 7; ++i) {
         g.off[i] = at;
@@ -140,7 +140,8 @@ attn_status_t rows8_launch(const void *qkv, int64_t n, int64_t heads, int64_t he
     if (workspace_bytes < geo.total)
         return fail(ATTN_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, geo.total);
     if (!aligned16(workspace)) return fail(ATTN_ERR_ARG, "workspace is not 16-byte aligned");
-    if (geo.groups * geo.tiles >= ((int64_t)1 << 31) || heads >= 65536 || n >= ((int64_t)1 << 31))
+    if (geo.groups * geo.tiles >= ((int64_t)1 << 31) || heads >= 65536 || n >= ((int64_t)1 << 31) ||
+        (quantize && prep && n * prep->half * 4 >= ((int64_t)1 << 31)) || 64 * rs * 2 >= ((int64_t)1 << 31))
         return fail(ATTN_ERR_ARG, "problem too large for one launch");
     const Span sw{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + geo.total};
     if (quantize && overlap(sw, span(qkv, n, rs, 3 * heads, head, 2))) return fail(ATTN_ERR_ARG, "workspace overlaps qkv");
@@ -159,7 +160,7 @@ attn_status_t rows8_launch(const void *qkv, int64_t n, int64_t heads, int64_t he
     a.q8 = reinterpret_cast<int8_t *>(ws + geo.off[0]); a.sq = reinterpret_cast<float *>(ws + geo.off[1]);
     a.k8 = reinterpret_cast<int8_t *>(ws + geo.off[2]); a.sk = reinterpret_cast<float *>(ws + geo.off[3]);
     a.v8t = ws + geo.off[4]; a.sv = reinterpret_cast<float *>(ws + geo.off[5]);
-    a.vmax = reinterpret_cast<uint32_t *>(ws + geo.off[6]);
+    a.vmax = reinterpret_cast<float *>(ws + geo.off[6]);
     a.out = out; a.scale = (float)(1.0 / std::sqrt((double)head));
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (quantize && (st = hip_status(attn::launch_rows8_quantize(a, s), "attn_rows8 (quantize)"))) return st;

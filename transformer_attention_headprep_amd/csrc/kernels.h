@@ -101,7 +101,7 @@ hipError_t launch_decode_q(const DecodeLaunch &a, hipStream_t stream);
 // tiles per group; the first nq rows are queries.  The quantizing pass writes q8 [nq, heads,
 // d] + sq [nq, heads], k8 [n, heads, d] + sk [groups, tiles, heads], v8t [groups, tiles,
 // heads, d, 64] (E4M3, keys of a tile in the order the P V product takes them) + sv [groups,
-// heads], using vmax [groups, heads] as scratch; the attention reads them and writes out
+// heads], using vmax [groups, tiles, heads] (each tile's amax of v) as scratch; the attention reads them and writes out
 // [nq, heads d] (bf16).  prep_mode: 0 none, 1 split halves with half = d / 2, 2 pairs.
 struct Rows8Launch {
     const void *qkv;
@@ -109,7 +109,7 @@ struct Rows8Launch {
     const float *qw, *kw, *cos, *sin;
     int half, prep_mode;
     float eps;
-    int8_t *q8; float *sq; int8_t *k8; float *sk; uint8_t *v8t; float *sv; uint32_t *vmax;
+    int8_t *q8; float *sq; int8_t *k8; float *sk; uint8_t *v8t; float *sv; float *vmax;
     void *out;
     float scale;
 };

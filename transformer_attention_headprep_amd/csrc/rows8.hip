@@ -5,8 +5,8 @@
 // Quantizing pass (rows8_quant_kernel, rows8_vt_kernel), per (64-row tile of a group, head):
 //   q: HeadPrep in f32, then int8 per (row, head): s = amax / 127, c = rint(x (1/s)).
 //   k: HeadPrep in f32, then int8 per (tile, head): one scale for the tile's 64 keys.
-//   v: E4M3 per (group, head): s = amax / 448 over the group (a first pass takes the
-//      amax with an atomic max), values rounded to nearest (ties even) by
+//   v: E4M3 per (group, head): s = amax / 448 over the group (the first kernel leaves each
+//      tile's amax, the second takes their largest), values rounded to nearest (ties even) by
 //      v_cvt_pk_fp8_f32, stored transposed ([d][64 keys]) with the keys of a tile in the
 //      order the P V product consumes them.
 // Every decision runs in f32 in the order written (correctly rounded division, no
@@ -48,15 +48,14 @@ __device__ __forceinline__ float lane_pair8(float x, int g) {
 
 // ------------------------------------------------------------------ quantizing pass
 
-__global__ void rows8_zero_kernel(uint32_t *p, int64_t n) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0u;
-}
-
 // HeadPrep of one row held as lo[4] (values 4 li ..) and hi[4] (values D/2 + 4 li ..) by the
-// LPR lanes of the row.  MODE 0: none; 1: split halves with half = D/2; 2: adjacent pairs.
+// LPR lanes of the row.  MODE 0: none; 1: split halves (half = D/2, or 0: norm and weight
+// only); 2: adjacent pairs.  tc / ts: the row's table entries this lane needs, loaded
+// beforehand -- MODE 1: entries 4 li .. 4 li + 3; MODE 2: entries 2 li, 2 li + 1 (pairs
+// of lo) and D/4 + 2 li, D/4 + 2 li + 1 (pairs of hi), used only below `half`.
 template <int D, int MODE>
-__device__ __forceinline__ void prep_row(float (&lo)[4], float (&hi)[4], int li, const float *w, const float *cs,
-                                         const float *sn, int half, int64_t trow, float eps) {
+__device__ __forceinline__ void prep_row(float (&lo)[4], float (&hi)[4], int li, const float *w, const f32x4 &tc,
+                                         const f32x4 &ts, int half, float eps) {
     constexpr int LPR = D / 8;
     if constexpr (MODE == 0) return;
     float ss = 0.f;
@@ -71,11 +70,10 @@ __device__ __forceinline__ void prep_row(float (&lo)[4], float (&hi)[4], int li,
         hi[i] = hi[i] * inv * w[eh + i];
     }
     if (half == 0) return;
-    const float *cr = cs + trow * half, *sr = sn + trow * half;
     if constexpr (MODE == 1) {          // half = D / 2: value e with e + D / 2, entry e
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float c = cr[el + i], s = sr[el + i], a = lo[i], b = hi[i];
+            const float c = tc[i], s = ts[i], a = lo[i], b = hi[i];
             lo[i] = a * c - b * s;
             hi[i] = b * c + a * s;
         }
@@ -84,12 +82,12 @@ __device__ __forceinline__ void prep_row(float (&lo)[4], float (&hi)[4], int li,
         for (int i = 0; i < 4; i += 2) {
             const int jl = (el + i) / 2, jh = (eh + i) / 2;
             if (jl < half) {
-                const float c = cr[jl], s = sr[jl], a = lo[i], b = lo[i + 1];
+                const float c = tc[i / 2], s = ts[i / 2], a = lo[i], b = lo[i + 1];
                 lo[i] = a * c - b * s;
                 lo[i + 1] = b * c + a * s;
             }
             if (jh < half) {
-                const float c = cr[jh], s = sr[jh], a = hi[i], b = hi[i + 1];
+                const float c = tc[2 + i / 2], s = ts[2 + i / 2], a = hi[i], b = hi[i + 1];
                 hi[i] = a * c - b * s;
                 hi[i + 1] = b * c + a * s;
             }
@@ -122,33 +120,54 @@ __global__ __launch_bounds__(256) void rows8_quant_kernel(const Rows8Launch a) {
     const int64_t rs = 3 * a.heads * D;
     const int el = 4 * li, eh = D / 2 + 4 * li;
 
+    // Every load of the tile first (q, k, v of all its rows, and their table entries):
+    // descriptors end with the group and the table, so rows past them read as zeros.
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const __amdgpu_buffer_rsrc_t rr = seq_rsrc(qkv + row0 * rs, gend > row0 ? (gend - row0) * rs * 2 : 0);
+    const int64_t tbytes = MODE ? a.n * (int64_t)a.half * 4 : 0;
+    const __amdgpu_buffer_rsrc_t cr = seq_rsrc(a.cos, tbytes), sr = seq_rsrc(a.sin, tbytes);
+    u32x2 raw[NP][6];
+    f32x4 tcv[NP], tsv[NP];
+#pragma unroll
+    for (int ps = 0; ps < NP; ++ps) {
+        const int ro = (ps * RPP + lr) * (int)rs * 2;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            raw[ps][2 * j] = __builtin_amdgcn_raw_buffer_load_b64(rr, ro + (int)((j * a.heads + h) * D + el) * 2, 0, 0);
+            raw[ps][2 * j + 1] = __builtin_amdgcn_raw_buffer_load_b64(rr, ro + (int)((j * a.heads + h) * D + eh) * 2, 0, 0);
+        }
+        const int trow = (int)(row0 + ps * RPP + lr);
+        if constexpr (MODE == 1) {
+            tcv[ps] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cr, (trow * a.half + el) * 4, 0, 0));
+            tsv[ps] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(sr, (trow * a.half + el) * 4, 0, 0));
+        } else if constexpr (MODE == 2) {
+            const u32x2 c0 = __builtin_amdgcn_raw_buffer_load_b64(cr, (trow * a.half + 2 * li) * 4, 0, 0);
+            const u32x2 c1 = __builtin_amdgcn_raw_buffer_load_b64(cr, (trow * a.half + D / 4 + 2 * li) * 4, 0, 0);
+            const u32x2 s0 = __builtin_amdgcn_raw_buffer_load_b64(sr, (trow * a.half + 2 * li) * 4, 0, 0);
+            const u32x2 s1 = __builtin_amdgcn_raw_buffer_load_b64(sr, (trow * a.half + D / 4 + 2 * li) * 4, 0, 0);
+            tcv[ps] = (f32x4){__uint_as_float(c0[0]), __uint_as_float(c0[1]), __uint_as_float(c1[0]), __uint_as_float(c1[1])};
+            tsv[ps] = (f32x4){__uint_as_float(s0[0]), __uint_as_float(s0[1]), __uint_as_float(s1[0]), __uint_as_float(s1[1])};
+        } else {
+            tcv[ps] = tsv[ps] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
     float kk[NP][8];
     float kmax = 0.f, vmax = 0.f;
 #pragma unroll
     for (int ps = 0; ps < NP; ++ps) {
         const int64_t r = row0 + ps * RPP + lr;
         const bool ok = r < gend;
-        float ql[4] = {0.f, 0.f, 0.f, 0.f}, qh[4] = {0.f, 0.f, 0.f, 0.f};
-        float kl[4] = {0.f, 0.f, 0.f, 0.f}, kh[4] = {0.f, 0.f, 0.f, 0.f};
-        float vl[4] = {0.f, 0.f, 0.f, 0.f}, vh[4] = {0.f, 0.f, 0.f, 0.f};
-        if (ok) {
-            const uint16_t *row = qkv + r * rs + (int64_t)h * D;
-            const uint2 q0 = *reinterpret_cast<const uint2 *>(row + el), q1 = *reinterpret_cast<const uint2 *>(row + eh);
-            const uint2 k0 = *reinterpret_cast<const uint2 *>(row + a.heads * D + el);
-            const uint2 k1 = *reinterpret_cast<const uint2 *>(row + a.heads * D + eh);
-            const uint2 v0 = *reinterpret_cast<const uint2 *>(row + 2 * a.heads * D + el);
-            const uint2 v1 = *reinterpret_cast<const uint2 *>(row + 2 * a.heads * D + eh);
-            unpack_bf16x2(q0.x, ql[0], ql[1]); unpack_bf16x2(q0.y, ql[2], ql[3]);
-            unpack_bf16x2(q1.x, qh[0], qh[1]); unpack_bf16x2(q1.y, qh[2], qh[3]);
-            unpack_bf16x2(k0.x, kl[0], kl[1]); unpack_bf16x2(k0.y, kl[2], kl[3]);
-            unpack_bf16x2(k1.x, kh[0], kh[1]); unpack_bf16x2(k1.y, kh[2], kh[3]);
-            unpack_bf16x2(v0.x, vl[0], vl[1]); unpack_bf16x2(v0.y, vl[2], vl[3]);
-            unpack_bf16x2(v1.x, vh[0], vh[1]); unpack_bf16x2(v1.y, vh[2], vh[3]);
-        }
-        const int64_t trow = ok ? r : gstart;
-        prep_row<D, MODE>(kl, kh, li, a.kw, a.cos, a.sin, a.half, trow, a.eps);
+        float ql[4], qh[4], kl[4], kh[4], vl[4], vh[4];
+        unpack_bf16x2(raw[ps][0][0], ql[0], ql[1]); unpack_bf16x2(raw[ps][0][1], ql[2], ql[3]);
+        unpack_bf16x2(raw[ps][1][0], qh[0], qh[1]); unpack_bf16x2(raw[ps][1][1], qh[2], qh[3]);
+        unpack_bf16x2(raw[ps][2][0], kl[0], kl[1]); unpack_bf16x2(raw[ps][2][1], kl[2], kl[3]);
+        unpack_bf16x2(raw[ps][3][0], kh[0], kh[1]); unpack_bf16x2(raw[ps][3][1], kh[2], kh[3]);
+        unpack_bf16x2(raw[ps][4][0], vl[0], vl[1]); unpack_bf16x2(raw[ps][4][1], vl[2], vl[3]);
+        unpack_bf16x2(raw[ps][5][0], vh[0], vh[1]); unpack_bf16x2(raw[ps][5][1], vh[2], vh[3]);
+        prep_row<D, MODE>(kl, kh, li, a.kw, tcv[ps], tsv[ps], a.half, a.eps);
         if (r < a.nq) {   // the row is a query: its own int8 scale (uniform over the LPR lanes)
-            prep_row<D, MODE>(ql, qh, li, a.qw, a.cos, a.sin, a.half, trow, a.eps);
+            prep_row<D, MODE>(ql, qh, li, a.qw, tcv[ps], tsv[ps], a.half, a.eps);
             float qm = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) qm = fmaxf(qm, fmaxf(fabsf(ql[i]), fabsf(qh[i])));
@@ -194,7 +213,7 @@ __global__ __launch_bounds__(256) void rows8_quant_kernel(const Rows8Launch a) {
     }
     if (tid == 0) {
         a.sk[((int64_t)g * a.tiles + t) * a.heads + h] = sk;
-        atomicMax(a.vmax + (int64_t)g * a.heads + h, __float_as_uint(vmax));   // non-negative: bits order as values
+        a.vmax[((int64_t)g * a.tiles + t) * a.heads + h] = vmax;    // the tile's amax of v
     }
 }
 
@@ -214,13 +233,24 @@ __global__ __launch_bounds__(256) void rows8_vt_kernel(const Rows8Launch a) {
     const int64_t row0 = gstart + (int64_t)t * kTile;
     const uint16_t *qkv = static_cast<const uint16_t *>(a.qkv);
     const int64_t rs = 3 * a.heads * D;
-    for (int idx = tid; idx < kTile * D; idx += 256) {
-        const int i = idx / D, e = idx % D;
+    for (int idx = tid; idx < kTile * (D / 8); idx += 256) {     // 16-byte loads: 8 values each
+        const int i = idx / (D / 8), e0 = 8 * (idx % (D / 8));
         const int64_t r = row0 + i;
-        vs[i][e] = r < gend ? bf16_bits_to_f32(qkv[r * rs + (int64_t)(2 * a.heads + h) * D + e]) : 0.f;
+        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (r < gend) {
+            const uint4 u = *reinterpret_cast<const uint4 *>(qkv + r * rs + (int64_t)(2 * a.heads + h) * D + e0);
+            unpack_bf16x2(u.x, x[0], x[1]);
+            unpack_bf16x2(u.y, x[2], x[3]);
+            unpack_bf16x2(u.z, x[4], x[5]);
+            unpack_bf16x2(u.w, x[6], x[7]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vs[i][e0 + j] = x[j];
     }
     __syncthreads();
-    const float amax = __uint_as_float(a.vmax[(int64_t)g * a.heads + h]);
+    // The group's amax of v: the largest of its tiles' (written by the quantizing kernel).
+    float amax = 0.f;
+    for (int tt = 0; tt < a.tiles; ++tt) amax = fmaxf(amax, a.vmax[((int64_t)g * a.tiles + tt) * a.heads + h]);
     const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
     const float inv = __fdiv_rn(1.0f, s);
     uint8_t *tile = a.v8t + (((int64_t)g * a.tiles + t) * a.heads + h) * D * kTile;
@@ -354,21 +384,22 @@ __global__ __launch_bounds__(256) void attn8_kernel(const Rows8Launch a) {
                 const i32x4 ka = *reinterpret_cast<const i32x4 *>(buf + k_lane + kb * 32 * G::kKPitch + 32 * c);
                 si[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qf[c], si[kb], 0, 0, 0);
             }
+        // Scores in base-2 units are si * f (f >= 0), so the tile max is taken on the integers.
         const float f = arow * a.sk[((int64_t)grp * a.tiles + kt) * a.heads + h];
-        float s[2][16];
         const int key0 = kt * kTile;
+        if (key0 + kTile > len) {          // the group's last, ragged tile (block-uniform)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (key0 + 32 * kb + 8 * (i / 4) + 4 * g + (i % 4) >= len) si[kb][i] = INT32_MIN;
+        }
+        int mi = si[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                s[kb][i] = (float)si[kb][i] * f;
-                if (key0 + 32 * kb + 8 * (i / 4) + 4 * g + (i % 4) >= len) s[kb][i] = -INFINITY;
-            }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+            for (int i = 0; i < 16; ++i) mi = max(mi, si[kb][i]);
+        float mx = mi == INT32_MIN ? -INFINITY : (float)mi * f;
         mx = fmaxf(mx, lane_pair8(mx, g));
         const float m_new = fmaxf(m_run, mx);
         if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
@@ -388,7 +419,8 @@ __global__ __launch_bounds__(256) void attn8_kernel(const Rows8Launch a) {
             float p[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                p[j] = fast_exp2(s[kb][i0 + j] + bias);
+                // a masked key (INT32_MIN) gives 2^-huge = 0; f is finite, so no inf - inf
+                p[j] = fast_exp2(fmaf((float)si[kb][i0 + j], f, bias));
                 l_run += p[j];
             }
             int v = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
@@ -439,9 +471,6 @@ void launch_quant_d(const Rows8Launch &a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_rows8_quantize(const Rows8Launch &a, hipStream_t stream) {
-    const int64_t nv = a.groups * a.heads;
-    hipLaunchKernelGGL(rows8_zero_kernel, dim3((unsigned)std::min<int64_t>((nv + 255) / 256, 1024)), dim3(256), 0, stream,
-                       a.vmax, nv);
     if (a.d == 64) launch_quant_d<64>(a, stream); else launch_quant_d<128>(a, stream);
     return hipGetLastError();
 }

@@ -205,7 +205,8 @@ def main() -> int:
     out3 = torch.empty_like(q3)
     prep3 = tah.HeadPrep(to(ip["qw"], "f32"), to(ip["kw"], "f32"), to(ip["cos"], "f32"),
                          to(ip["sin"], "f32"), wp.eps)
-    prep3_q = tah.HeadPrep(prep3.qw, None, prep3.cos, prep3.sin, wp.eps)   # k already prepped
+    # k already prepped (by attn_prep with kw): its rows' norms are within key_bound(kw)
+    prep3_q = tah.HeadPrep(prep3.qw, None, prep3.cos, prep3.sin, wp.eps, kmax=tah.key_bound(ip["kw"], wp.d))
 
     # decode operands: caches prepped on the GPU (HeadPrep at positions 0 .. 4095)
     prep4 = tah.HeadPrep(to(idc["qw"], "f32"), to(idc["kw"], "f32"), to(idc["cos"], "f32"),
@@ -313,7 +314,7 @@ def main() -> int:
         out5 = torch.empty_like(q5)
         prep5 = tah.HeadPrep(to(il["qw"], "f32"), to(il["kw"], "f32"), to(il["cos"], "f32"),
                              to(il["sin"], "f32"), wl.eps)
-        prep5_q = tah.HeadPrep(prep5.qw, None, prep5.cos, prep5.sin, wl.eps)
+        prep5_q = tah.HeadPrep(prep5.qw, None, prep5.cos, prep5.sin, wl.eps, kmax=tah.key_bound(il["kw"], wl.d))
 
         def call5():
             tah.attn_prep(None, k5, prep5, pos0=0, stream=stream)
@@ -346,7 +347,7 @@ def main() -> int:
         n_past, tq = wc.extra["n_past"], wc.extra["tq"]
         ic = synthetic.make_prefill(wc)
         prep6 = tah.HeadPrep(to(ic["qw"], "f32"), to(ic["kw"], "f32"), to(ic["cos"], "f32"),
-                             to(ic["sin"], "f32"), wc.eps)
+                             to(ic["sin"], "f32"), wc.eps, kmax=tah.key_bound(ic["kw"], wc.d))
         kc6, vc6 = to(ic["k"]), to(ic["v"])                  # [4, 4096, 8, 128]: the cache
         tah.attn_prep(None, kc6, prep6, pos0=0)              # rows 0 .. 3583 hold prepped keys
         q6 = to(ic["q"][:, n_past:])

@@ -81,7 +81,17 @@ typedef enum attn_status {
  *                    HeadPrep: loaded with its even values first, a head turns as
  *                    split halves; pairs = 1 takes the head as stored, interleaved).
  *               Values from 2 * half on keep their normed, weighted value either way.
- *               A zero-initialised record is the split-halves HeadPrep.
+ *   kmax        0, or a bound the caller guarantees on the L2 norm of every key row
+ *               the attention reads (as stored, after its HeadPrep); finite, >= 0.
+ *               attn_key_bound gives the bound HeadPrep with weights kw guarantees.
+ *               With a bound (kmax, or kw when the call preps k itself), the bf16
+ *               prefill with q's HeadPrep fused shifts each query row's softmax by
+ *               |q| times the bound (which no score of the row can exceed) instead of
+ *               tracking a running maximum: the same softmax, in fewer instructions
+ *               per key tile.  Rows whose shift would exceed 48 (in log2 units) keep
+ *               the running maximum.  An understated kmax can overflow the weights.
+ *               Other entry points ignore it.
+ *               A zero-initialised record is the split-halves HeadPrep with no bound.
  */
 typedef struct attn_headprep {
     const float *qw;
@@ -92,7 +102,18 @@ typedef struct attn_headprep {
     int64_t table_rows;
     double eps;
     int64_t pairs;
+    double kmax;
 } attn_headprep_t;
+
+/*
+ * attn_key_bound -- the bound on the norm of every key row that HeadPrep with norm
+ * weights kw writes, for attn_headprep_t.kmax: sqrt(d) max|kw| (an RMS-normed row
+ * has norm at most sqrt(d), the weights scale it by at most max|kw|, the turn keeps
+ * it) times 1 + 2^-7 (rounding to bf16 changes each value by at most 2^-9 of it).
+ *   kw  HOST pointer to d floats.  Returns -1 if kw is NULL or d <= 0, NaN if a
+ *   weight is not finite.
+ */
+double attn_key_bound(const float *kw, int64_t d);
 
 /*
  * attn_prep -- HeadPrep in place on q and k (gizml:netops, Functions >

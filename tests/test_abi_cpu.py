@@ -41,8 +41,8 @@ def test_status_strings(lib):
     assert lib.attn_supported(128, 7) == 0
 
 
-def _prep(half=64, rows=4096, qw=FAKE, kw=FAKE, cos=FAKE, sin=FAKE, eps=1e-6, pairs=0):
-    return A.attn_headprep_t(qw, kw, cos, sin, half, rows, eps, pairs)
+def _prep(half=64, rows=4096, qw=FAKE, kw=FAKE, cos=FAKE, sin=FAKE, eps=1e-6, pairs=0, kmax=0.0):
+    return A.attn_headprep_t(qw, kw, cos, sin, half, rows, eps, pairs, kmax)
 
 
 def _prefill(lib, **kw):
@@ -76,6 +76,9 @@ def _prefill(lib, **kw):
     (dict(prep=_prep(qw=None)), A.ATTN_ERR_ARG),
     (dict(prep=_prep(eps=-1.0)), A.ATTN_ERR_ARG),
     (dict(prep=_prep(eps=float("nan"))), A.ATTN_ERR_ARG),
+    (dict(prep=_prep(kmax=-1.0)), A.ATTN_ERR_ARG),
+    (dict(prep=_prep(kmax=float("nan"))), A.ATTN_ERR_ARG),
+    (dict(prep=_prep(kmax=float("inf"))), A.ATTN_ERR_ARG),
     (dict(scale=float("inf")), A.ATTN_ERR_ARG),
     (dict(scale=0.0), A.ATTN_ERR_ARG),
     (dict(scale=-0.1), A.ATTN_ERR_ARG),
@@ -84,6 +87,42 @@ def _prefill(lib, **kw):
 def test_prefill_rejects(lib, kw, code):
     assert _prefill(lib, **kw) == code
     assert lib.attn_last_error()
+
+
+def test_key_bound(lib):
+    """attn_key_bound (host only): sqrt(d) max|kw| (1 + 2^-7); -1 for bad arguments."""
+    import numpy as np
+    kw = np.array([0.5, -1.75, 1.25, 0.0] * 32, dtype=np.float32)
+    got = lib.attn_key_bound(kw.ctypes.data, 128)
+    assert got == pytest.approx(np.sqrt(128) * 1.75 * (1 + 2.0 ** -7), rel=1e-12)
+    assert tah.key_bound(kw, 128) == got
+    assert lib.attn_key_bound(None, 128) == -1.0
+    assert lib.attn_key_bound(kw.ctypes.data, 0) == -1.0
+    bad = kw.copy()
+    bad[7] = np.inf
+    assert np.isnan(lib.attn_key_bound(bad.ctypes.data, 128))
+
+
+def test_key_bound_holds_for_headprep_rows():
+    """Every key row the oracle's HeadPrep writes (then rounded to bf16) has norm within
+    key_bound(kw); a row with all its mass on the largest weight comes within 1 % of it."""
+    import numpy as np
+    import oracle
+    import synthetic
+    rng = np.random.default_rng(17)
+    d, half = 128, 64
+    kw = rng.uniform(0.3, 1.7, d).astype(np.float32)
+    kw[37] = -2.5
+    x = rng.standard_normal((1, 300, 2, d)) * rng.uniform(0.01, 100, (1, 300, 2, 1))
+    x[0, 0, 0] = 0.0
+    x[0, 0, 0, 37] = 3.0                       # all mass on the largest |weight|
+    x[0, 1, 1] = 1e-30                         # eps dominates: a tiny row
+    cos, sin = synthetic.rope_tables(300, half, d, 1e4)
+    k = synthetic.bf16_round(oracle.headprep(x, kw, cos, sin, half, np.arange(300)[None], 1e-6))
+    norms = np.sqrt((k.astype(np.float64) ** 2).sum(-1))
+    bound = tah.key_bound(kw, d)
+    assert norms.max() <= bound
+    assert norms[0, 0, 0] >= 0.99 * bound
 
 
 def test_prefill_empty_is_a_no_op(lib):

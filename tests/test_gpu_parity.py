@@ -218,6 +218,34 @@ def test_prefill_softmax_max_stress():
     assert_close(host(out), oracle.attention(qh, kh, inp["v"], w.scale, True), "bf16", "stress")
 
 
+@pytest.mark.parametrize("mode", ["kmax", "kmax_loose", "kw_large"])
+def test_prefill_key_bound_paths(mode):
+    """The fixed softmax shift (|q| times a bound on every key row's norm).  The bound
+    the call derives from kw when it preps k itself is the default path of the bf16
+    tests above; here: keys prepped by attn_prep with the bound passed as kmax (fixed
+    shift), a bound so loose the shift passes 48 (running maximum), and one weight so
+    large that the bound from kw passes it too (running maximum)."""
+    require_gpu()
+    w = synthetic.Workload("kb", "prefill", "bf16", 2, 8, 2, 300, 128, 64, 1e4, 29)
+    inp = synthetic.make_prefill(w)
+    if mode == "kw_large":
+        inp["kw"] = inp["kw"].copy()
+        inp["kw"][5] = 8.0                     # max|kw| 8: the bound passes 48, the scores stay moderate
+    q, k, v = dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16")
+    prep = _prep_dev(inp)
+    if mode == "kw_large":
+        out = tah.attn_prefill(q, k, v, prep=prep, causal=True, scale=w.scale)
+    else:
+        tah.attn_prep(None, k, prep, pos0=0)
+        kmax = tah.key_bound(inp["kw"], w.d) * (1.0 if mode == "kmax" else 50.0)
+        prep_q = tah.HeadPrep(prep.qw, None, prep.cos, prep.sin, prep.eps, kmax=kmax)
+        out = tah.attn_prefill(q, k, v, prep=prep_q, causal=True, scale=w.scale)
+    ref, kh = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["qw"], inp["kw"], inp["cos"], inp["sin"],
+                             w.half, w.eps, 0, w.scale, True)
+    assert_close(host(out), ref, "bf16", mode)
+    assert_close(host(k), kh, "bf16", mode + " keys")
+
+
 # ------------------------------------------------------------------- attn_prefill_chunk
 
 def _chunk_inputs(dtype, d, half, hq, hkv, n_past, tq, seed, batch=2, spare=9):
@@ -237,13 +265,14 @@ def _chunk_inputs(dtype, d, half, hq, hkv, n_past, tq, seed, batch=2, spare=9):
     return w, inp, kc, vc
 
 
-def _run_chunk(w, inp, kc, vc, n_past, causal, prep_k=True, k_new=None):
+def _run_chunk(w, inp, kc, vc, n_past, causal, prep_k=True, k_new=None, kmax=0.0):
     dt = w.dtype
     sl = slice(n_past, None)
     kcd, vcd = dev(kc, dt), dev(vc, dt)
     prep = _prep_dev(inp)
+    prep.kmax = kmax
     if not prep_k:
-        prep = tah.HeadPrep(prep.qw, None, prep.cos, prep.sin, prep.eps)
+        prep = tah.HeadPrep(prep.qw, None, prep.cos, prep.sin, prep.eps, kmax=kmax)
     kn = inp["k"][:, sl] if k_new is None else k_new
     out = tah.attn_prefill_chunk(dev(inp["q"][:, sl], dt), dev(kn, dt), dev(inp["v"][:, sl], dt), kcd, vcd,
                                  n_past, prep=prep, causal=causal, scale=w.scale)
@@ -288,6 +317,19 @@ def test_prefill_chunk_with_prepped_keys():
     ref, _, _ = oracle.prefill_chunk(inp["q"][:, 260:], kh, inp["v"][:, 260:], kc, vc, 260, inp["qw"], inp["kw"],
                                      inp["cos"], inp["sin"], 64, w.eps, w.scale, True, prep_k=False)
     assert_close(got, ref, "bf16", "chunk with prepped keys")
+
+
+@pytest.mark.parametrize("n_past,tq", [(700, 300), (37, 200)])
+def test_prefill_chunk_with_kmax(n_past, tq):
+    """kmax on a chunk: the cached rows (the oracle's prepped keys in bf16) and the new
+    rows the call preps are all within key_bound(kw), so each row's shift is fixed."""
+    require_gpu()
+    w, inp, kc, vc = _chunk_inputs("bf16", 128, 64, 8, 2, n_past, tq, seed=83 + n_past)
+    got, _, _ = _run_chunk(w, inp, kc, vc, n_past, True, kmax=tah.key_bound(inp["kw"], 128))
+    sl = slice(n_past, None)
+    ref, _, _ = oracle.prefill_chunk(inp["q"][:, sl], inp["k"][:, sl], inp["v"][:, sl], kc, vc, n_past,
+                                     inp["qw"], inp["kw"], inp["cos"], inp["sin"], 64, w.eps, w.scale, True)
+    assert_close(got, ref, "bf16", "chunk with kmax")
 
 
 def test_prefill_chunks_equal_one_shot_prefill():

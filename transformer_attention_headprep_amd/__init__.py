@@ -26,5 +26,6 @@ from .attn import (  # noqa: F401
     decode_default_splits,
     decode_q_default_splits,
     decode_workspace_size,
+    key_bound,
     load_library,
 )

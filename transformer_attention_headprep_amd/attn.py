@@ -22,8 +22,8 @@ ATTN_OK, ATTN_ERR_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 
 # The entry points include/attn.h declares (checked by the CPU test suite).
 EXPORTS = ("attn_prep", "attn_prefill", "attn_prefill_chunk", "attn_decode", "attn_decode_workspace_size",
            "attn_decode_default_splits", "attn_kv_quantize", "attn_decode_q", "attn_decode_q_default_splits", "attn_rows", "attn_rows8_layout", "attn_rows8_quantize",
-           "attn_rows8_attend", "attn_rows8", "attn_row_norm_rope", "attn_supported", "attn_status_str",
-           "attn_last_error")
+           "attn_rows8_attend", "attn_rows8", "attn_row_norm_rope", "attn_key_bound", "attn_supported",
+           "attn_status_str", "attn_last_error")
 
 
 class AttnError(RuntimeError):
@@ -35,7 +35,7 @@ class AttnError(RuntimeError):
 class attn_headprep_t(ctypes.Structure):
     _fields_ = [("qw", ctypes.c_void_p), ("kw", ctypes.c_void_p), ("cos", ctypes.c_void_p),
                 ("sin", ctypes.c_void_p), ("half", ctypes.c_int64), ("table_rows", ctypes.c_int64),
-                ("eps", ctypes.c_double), ("pairs", ctypes.c_int64)]
+                ("eps", ctypes.c_double), ("pairs", ctypes.c_int64), ("kmax", ctypes.c_double)]
 
 
 _lib = None
@@ -86,6 +86,8 @@ def load_library(path: str = LIB_PATH):
     lib.attn_rows.restype = ctypes.c_int
     lib.attn_row_norm_rope.argtypes = [_vp] + [_i64] * 4 + [_vp, _vp, _vp, _dbl, ctypes.c_int, _vp]
     lib.attn_row_norm_rope.restype = ctypes.c_int
+    lib.attn_key_bound.argtypes = [_vp, _i64]
+    lib.attn_key_bound.restype = _dbl
     lib.attn_supported.argtypes = [_i64, ctypes.c_int]
     lib.attn_supported.restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
@@ -136,13 +138,16 @@ def _row_stride(t: torch.Tensor, name: str) -> int:
 @dataclass
 class HeadPrep:
     """The HeadPrep record {qw, kw, cos, sin, eps} as device f32 tensors; pairs=True turns
-    adjacent values (2i, 2i + 1) rather than split halves (i, i + half)."""
+    adjacent values (2i, 2i + 1) rather than split halves (i, i + half).  kmax > 0 is the
+    caller's bound on the norm of every key row the attention reads (see attn_headprep_t;
+    key_bound() gives the one HeadPrep with weights kw guarantees)."""
     qw: torch.Tensor
     kw: torch.Tensor
     cos: torch.Tensor | None
     sin: torch.Tensor | None
     eps: float
     pairs: bool = False
+    kmax: float = 0.0
 
     @property
     def half(self) -> int:
@@ -158,7 +163,21 @@ class HeadPrep:
             self.qw.data_ptr() if self.qw is not None else None,
             self.kw.data_ptr() if self.kw is not None else None,
             self.cos.data_ptr() if half else None, self.sin.data_ptr() if half else None,
-            half, int(self.cos.shape[0]) if half else 0, float(self.eps), int(bool(self.pairs)))
+            half, int(self.cos.shape[0]) if half else 0, float(self.eps), int(bool(self.pairs)),
+            float(self.kmax))
+
+
+def key_bound(kw, d: int) -> float:
+    """attn_key_bound: the bound HeadPrep with weights kw (host array or tensor of d
+    values) guarantees on the norm of every key row it writes, for HeadPrep.kmax."""
+    if isinstance(kw, torch.Tensor):
+        kw = kw.detach().to("cpu", torch.float32).contiguous()
+    else:
+        kw = torch.as_tensor(kw, dtype=torch.float32).contiguous()
+    if kw.numel() != d:
+        raise ValueError("kw must hold d = %d values" % d)
+    lib = load_library()
+    return float(lib.attn_key_bound(ctypes.c_void_p(kw.data_ptr()), ctypes.c_int64(d)))
 
 
 def attn_supported(d: int, dtype: torch.dtype) -> bool:

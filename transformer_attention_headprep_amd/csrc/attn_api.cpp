@@ -72,6 +72,8 @@ attn_status_t check_prep(const attn_headprep_t *p, int64_t d, bool need_qw, bool
         return fail(ATTN_ERR_ARG, "prep weights are not 16-byte aligned");
     if (!(p->eps >= 0.0) || !std::isfinite(p->eps)) return fail(ATTN_ERR_ARG, "prep->eps must be finite and >= 0");
     if (p->pairs != 0 && p->pairs != 1) return fail(ATTN_ERR_ARG, "prep->pairs = %lld not 0 or 1", (long long)p->pairs);
+    if (!(p->kmax >= 0.0) || !std::isfinite(p->kmax) || p->kmax > 3.0e38)
+        return fail(ATTN_ERR_ARG, "prep->kmax must be finite and >= 0");
     if (p->half < 0 || 2 * p->half > d)
         return fail(ATTN_ERR_ARG, "prep->half = %lld outside [0, d/2]", (long long)p->half);
     if (p->half > 0) {
@@ -308,6 +310,8 @@ attn_status_t attn_prefill(const void *q, void *k, const void *v, void *out, int
         if (fused) {
             a.prep_q = true;
             a.qw = prep->qw; a.cos = prep->cos; a.sin = prep->sin; a.half = prep->half; a.eps = (float)prep->eps;
+            a.kwb = prep->kw;            // k was prepped with kw just above
+            a.kmax = (float)prep->kmax;
         } else {
             a.q = out; a.q_rs = o_row_stride;
         }
@@ -389,6 +393,7 @@ attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v
         if (!prep->pairs && attn::prefill_fuses_half(d, prep->half, bf16)) {
             a.prep_q = true;
             a.qw = prep->qw; a.cos = prep->cos; a.sin = prep->sin; a.half = prep->half; a.eps = (float)prep->eps;
+            a.kmax = (float)prep->kmax;  // cached rows: only the caller's bound
         } else {
             // q prepped into out first; each attention block reads exactly the rows it writes.
             attn::PrepLaunch pq{};
@@ -671,6 +676,16 @@ attn_status_t attn_decode_q(const void *q, const uint8_t *k_codes, const float *
     a.bf16 = true;
     a.kpar = k_params; a.vpar = v_params; a.kbits = (int)k_bits; a.vbits = (int)v_bits;
     return hip_status(attn::launch_decode(a, static_cast<hipStream_t>(stream)), "attn_decode_q");
+}
+
+double attn_key_bound(const float *kw, int64_t d) {
+    if (!kw || d <= 0) return -1.0;
+    double m = 0.0;
+    for (int64_t i = 0; i < d; ++i) {
+        if (!std::isfinite(kw[i])) return std::nan("");
+        m = std::max(m, (double)std::fabs(kw[i]));
+    }
+    return std::sqrt((double)d) * m * (1.0 + 1.0 / 128);
 }
 
 }  // extern "C"

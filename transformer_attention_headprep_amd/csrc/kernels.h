@@ -39,6 +39,8 @@ struct PrefillLaunch {
     int64_t batch, seq, tk, hq, hkv, d, pos0;
     bool prep_q;                 // apply HeadPrep to q in the prologue
     const float *qw, *cos, *sin;
+    const float *kwb;            // non-NULL: k was prepped with these weights (bounds |k|)
+    float kmax;                  // > 0: caller's bound on every key row's norm
     int64_t half;
     float eps;
     bool causal;

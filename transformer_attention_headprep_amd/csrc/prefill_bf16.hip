@@ -68,6 +68,7 @@ constexpr int kBM = 32 * kWaves;   // query rows per block
 constexpr int kBN = 64;            // keys per tile
 constexpr int kXcds = 8;
 constexpr float kRaiseAbove = 8.0f;   // base-2 headroom before the running max moves
+constexpr float kFixedShiftMax = 48.0f;   // largest fixed softmax shift (base 2) a row may take
 
 extern __shared__ __attribute__((aligned(16))) unsigned char prefill_smem[];
 
@@ -78,28 +79,37 @@ __device__ __forceinline__ float lane_pair(float x, int g) {
 }
 
 // Split-half turn of a lane's q values held as NC chunks of 8 (chunk c = d 16c + 8g ..):
-// chunk c < HC pairs with chunk c + HC (half = 16 HC), using table entries d0 .. d0 + 7.
+// chunk c < HC pairs with chunk c + HC (half = 16 HC); cv / sv hold the table entries
+// 16c + 8g .. + 7 of the row for each c < HC.
 template <int NC, int HC>
-__device__ __forceinline__ void turn_chunks(float (&x)[NC][8], const float *cr, const float *sr, int g) {
+__device__ __forceinline__ void turn_chunks(float (&x)[NC][8], const f32x4 (&cv)[NC / 2][2],
+                                            const f32x4 (&sv)[NC / 2][2]) {
     if constexpr (HC >= 1 && 2 * HC <= NC) {
 #pragma unroll
         for (int c = 0; c < HC; ++c) {
-            const int d0 = 16 * c + 8 * g;
-            const float4 c0 = *reinterpret_cast<const float4 *>(cr + d0);
-            const float4 c1 = *reinterpret_cast<const float4 *>(cr + d0 + 4);
-            const float4 s0 = *reinterpret_cast<const float4 *>(sr + d0);
-            const float4 s1 = *reinterpret_cast<const float4 *>(sr + d0 + 4);
-            const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-            const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
+                const float co = cv[c][e / 4][e % 4], si = sv[c][e / 4][e % 4];
                 const float a = x[c][e], b = x[c + HC][e];
-                x[c][e] = a * cv[e] - b * sv[e];
-                x[c + HC][e] = b * cv[e] + a * sv[e];
+                x[c][e] = a * co - b * si;
+                x[c + HC][e] = b * co + a * si;
             }
         }
     }
 }
+
+// How a launch's grid carries the block coordinates (see launch_bf16_d): the query tile
+// is z (reversed: longest causal tiles first); the (batch, kv head) pair and the q head
+// within its kv group sit on x and y, so a block finds them with no division but one
+// multiply-shift by hkv.
+struct PrefillGrid {
+    int mode;          // 0: x = 8 group (x % 8 = pair % 8, x / 8 = head in group), y = pair / 8
+                       // 1: x = head in group, y = pair;  2: x = pair, y = head in group
+    int group;         // q heads per kv head
+    int hkv;
+    uint32_t hkv_mul;  // pair / hkv = (pair hkv_mul) >> hkv_shift for 0 <= pair < 2^31
+    int hkv_shift;
+};
 
 // LDS geometry of one tile buffer for head dim D.
 template <int D>
@@ -120,47 +130,38 @@ struct Geo {
 };
 
 template <int D, bool CAUSAL, bool PREP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(const PrefillLaunch p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(const PrefillLaunch p,
+                                                                                                    const PrefillGrid gr) {
     typedef Geo<D> G;
     unsigned char *smem = prefill_smem;                                  // 2 tile buffers
     constexpr int NC = D / 16;       // 16-wide d chunks of the q.k product
     constexpr int NDB = D / 32;      // 32-wide d blocks of the output
 
-    const int tid = threadIdx.x;
-    const int w = tid / 64, lane = tid % 64;
+    const int lane = threadIdx.x % 64;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);   // wave-uniform: scalar addressing
     const int n = lane % 32, g = lane / 32;
 
     // ---- which (batch, q head, query tile) this block owns
-    const int nq_tiles = (int)((p.seq + kBM - 1) / kBM);
     const int tq = (int)p.seq, tk = (int)p.tk, qoff = tk - tq;   // query i sits at key position i + qoff
-    const int group = (int)(p.hq / p.hkv);
-    const int pairs = (int)(p.batch * p.hkv);
-    int b, h, qtile;
-    {
-        const int i = blockIdx.x;
-        int pair, hg;
-        if (pairs % kXcds == 0) {
-            const int ppx = pairs / kXcds;                 // pairs per XCD
-            const int x = i % kXcds;
-            const int j = i / kXcds;
-            const int per_tile = ppx * group;
-            qtile = nq_tiles - 1 - j / per_tile;
-            const int rem = j % per_tile;
-            pair = x + kXcds * (rem / group);
-            hg = rem % group;
-        } else {
-            const int per_tile = pairs * group;
-            qtile = nq_tiles - 1 - i / per_tile;
-            const int rem = i % per_tile;
-            pair = rem / group;
-            hg = rem % group;
-        }
-        b = pair / (int)p.hkv;
-        h = (pair % (int)p.hkv) * group + hg;
+    const int qtile = (int)gridDim.z - 1 - (int)blockIdx.z;
+    int pair, hg;
+    if (gr.mode == 0) {
+        pair = (int)(blockIdx.x % kXcds) + kXcds * (int)blockIdx.y;
+        hg = (int)(blockIdx.x / kXcds);
+    } else if (gr.mode == 1) {
+        pair = (int)blockIdx.y;
+        hg = (int)blockIdx.x;
+    } else {
+        pair = (int)blockIdx.x;
+        hg = (int)blockIdx.y;
     }
-    const int kvh = h / group;
+    const int b = (int)(((uint64_t)(uint32_t)pair * gr.hkv_mul) >> gr.hkv_shift);
+    const int kvh = pair - b * gr.hkv;
+    const int h = kvh * gr.group + hg;
 
-    const int64_t r = (int64_t)qtile * kBM + 32 * w + n;
+    const int64_t row0w = (int64_t)qtile * kBM + 32 * w;           // first row of this wave
+    const int wrows = (int)max<int64_t>(0, min<int64_t>(32, tq - row0w));   // its rows inside the sequence
+    const int64_t r = row0w + n;
     const bool row_ok = r < tq;
 
     const int64_t last_key = CAUSAL ? min<int64_t>(tk - 1, (int64_t)qtile * kBM + kBM - 1 + qoff) : tk - 1;
@@ -175,12 +176,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t rs = loads_k ? p.k_rs : p.v_rs;
     const uint16_t *src = static_cast<const uint16_t *>(loads_k ? p.k : p.v) +
                           (int64_t)b * (loads_k ? p.k_bs : p.v_bs) + (int64_t)kvh * D;
-    const int slots = loads_k ? G::kKSlots : G::kVSlots;
     int voff[G::kPerWave];
 #pragma unroll
     for (int t = 0; t < G::kPerWave; ++t) {
         const int sidx = (wl + 2 * t) * 64 + lane;
-        const int row = sidx / slots, col = sidx % slots;
+        const int row = loads_k ? sidx / G::kKSlots : sidx / G::kVSlots;   // constant divisors
+        const int col = sidx - row * (loads_k ? G::kKSlots : G::kVSlots);
         voff[t] = (int)(row * rs + 8 * min(col, G::kChunks - 1)) * 2;
     }
     auto load_tile = [&](int kt, int bsel) {
@@ -199,60 +200,106 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     const float C = p.scale * kLog2e;       // q is scaled by this before it is rounded
 
-    // ---- q prologue: load this lane's 64 (or 32) values of its row, HeadPrep, bf16.
+    // ---- q prologue: this lane's 64 (or 32) values of its row, HeadPrep, bf16.  Every
+    // load is issued before anything waits; rows past the sequence (and table rows past
+    // them) read as zeros through the wave's descriptors.
     bf16x8 qf[NC];
+    float kb = 0.f;        // PREP: bound on the norm of every key row (0: none known)
+    float shift = 0.f;     // |q| kb, a bound on every score of the row
     {
-        const uint16_t *qrow = static_cast<const uint16_t *>(p.q) + (int64_t)b * p.q_bs +
-                               (row_ok ? r : 0) * p.q_rs + (int64_t)h * D;
-        uint4 raw[NC];
+        const __amdgpu_buffer_rsrc_t qsrc =
+            seq_rsrc(static_cast<const uint16_t *>(p.q) + (int64_t)b * p.q_bs + row0w * p.q_rs + (int64_t)h * D,
+                     wrows > 0 ? ((int64_t)(wrows - 1) * p.q_rs + D) * 2 : 0);
+        const int qoff_lane = (n * (int)p.q_rs + 8 * g) * 2;
+        u32x4 raw[NC];
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-            raw[c] = row_ok ? *reinterpret_cast<const uint4 *>(qrow + 16 * c + 8 * g) : make_uint4(0, 0, 0, 0);
+        for (int c = 0; c < NC; ++c) raw[c] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, qoff_lane + 32 * c, 0, 0);
         if constexpr (PREP) {
-            float x[NC][8];
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                unpack_bf16x2(raw[c].x, x[c][0], x[c][1]);
-                unpack_bf16x2(raw[c].y, x[c][2], x[c][3]);
-                unpack_bf16x2(raw[c].z, x[c][4], x[c][5]);
-                unpack_bf16x2(raw[c].w, x[c][6], x[c][7]);
-            }
-            float ss = 0.f;
+            const int hc = (int)p.half / 16;     // turned pairs are hc chunks apart
+            f32x4 wv[NC][2], cv[NC / 2][2], sv[NC / 2][2];
 #pragma unroll
             for (int c = 0; c < NC; ++c)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ss += x[c][e] * x[c][e];
-            ss += __shfl_xor(ss, 32, 64);
-            const float inv = 1.0f / __builtin_sqrtf(ss * (1.0f / D) + p.eps);
+                for (int j = 0; j < 2; ++j) wv[c][j] = *reinterpret_cast<const f32x4 *>(p.qw + 16 * c + 8 * g + 4 * j);
+            if (hc > 0) {
+                const int64_t tbytes = (int64_t)wrows * p.half * 4;
+                const __amdgpu_buffer_rsrc_t crs = seq_rsrc(p.cos + (p.pos0 + row0w) * p.half, tbytes);
+                const __amdgpu_buffer_rsrc_t srs = seq_rsrc(p.sin + (p.pos0 + row0w) * p.half, tbytes);
+                const int toff = (n * (int)p.half + 8 * g) * 4;
+#pragma unroll
+                for (int c = 0; c < NC / 2; ++c)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        if (c < hc) {
+                            cv[c][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, toff + 64 * c + 16 * j, 0, 0));
+                            sv[c][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, toff + 64 * c + 16 * j, 0, 0));
+                        }
+            }
+            // Sum of squares straight from the bf16 pairs (exact products, f32 sums).
+            float ss = 0.f;
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const float4 w0 = *reinterpret_cast<const float4 *>(p.qw + 16 * c + 8 * g);
-                const float4 w1 = *reinterpret_cast<const float4 *>(p.qw + 16 * c + 8 * g + 4);
-                const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+                const bf16x8 v8 = __builtin_bit_cast(bf16x8, raw[c]);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[c][e] = x[c][e] * inv * wv[e];
-            }
-
-            const int hc = (int)p.half / 16;     // turned pairs are hc chunks apart
-            if (hc > 0 && row_ok) {
-                const float *cr = p.cos + (p.pos0 + r) * p.half;
-                const float *sr = p.sin + (p.pos0 + r) * p.half;
-                // hc is a run-time value; dispatch to unrolled code so x stays in registers.
-                switch (hc) {
-                    case 1: turn_chunks<NC, 1>(x, cr, sr, g); break;
-                    case 2: turn_chunks<NC, 2>(x, cr, sr, g); break;
-                    case 3: turn_chunks<NC, 3>(x, cr, sr, g); break;
-                    default: turn_chunks<NC, NC / 2>(x, cr, sr, g); break;
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x2 pr = {v8[2 * j], v8[2 * j + 1]};
+                    ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
                 }
             }
+            ss += __shfl_xor(ss, 32, 64);
+            // x qw, turned, then one multiply by the row's 1 / rms and scale log2 e (both
+            // steps are linear, so the order is the method's up to rounding).
+            float x[NC][8];
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float lo, hi;
+                    unpack_bf16x2(raw[c][j], lo, hi);
+                    x[c][2 * j] = lo * wv[c][j / 2][(2 * j) % 4];
+                    x[c][2 * j + 1] = hi * wv[c][j / 2][(2 * j + 1) % 4];
+                }
+            // hc is a run-time value; dispatch to unrolled code so x stays in registers.
+            switch (hc) {
+                case 0: break;
+                case 1: turn_chunks<NC, 1>(x, cv, sv); break;
+                case 2: turn_chunks<NC, 2>(x, cv, sv); break;
+                case 3: turn_chunks<NC, 3>(x, cv, sv); break;
+                default: turn_chunks<NC, NC / 2>(x, cv, sv); break;
+            }
+            const float f = C * __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps);
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 uint4 u;
-                u.x = pack_bf16x2(x[c][0] * C, x[c][1] * C);
-                u.y = pack_bf16x2(x[c][2] * C, x[c][3] * C);
-                u.z = pack_bf16x2(x[c][4] * C, x[c][5] * C);
-                u.w = pack_bf16x2(x[c][6] * C, x[c][7] * C);
+                u.x = pack_bf16x2(x[c][0] * f, x[c][1] * f);
+                u.y = pack_bf16x2(x[c][2] * f, x[c][3] * f);
+                u.z = pack_bf16x2(x[c][4] * f, x[c][5] * f);
+                u.w = pack_bf16x2(x[c][6] * f, x[c][7] * f);
                 qf[c] = __builtin_bit_cast(bf16x8, u);
+            }
+            // Key-norm bound: the caller's kmax, and when this call prepped k from kw,
+            // sqrt(D) max|kw| (each prepped key row is its RMS-normed values times kw,
+            // turned, rounded to bf16) -- whichever is smaller.
+            kb = p.kmax;
+            if (p.kwb) {
+                float a = fabsf(p.kwb[lane % D]);
+                if constexpr (D > 64) a = fmaxf(a, fabsf(p.kwb[64 + lane % (D - 64)]));
+                const float kw_bound = __builtin_sqrtf((float)D) * max_lanes<64>(a) * (1.0f + 1.0f / 128);
+                kb = kb > 0.f ? fminf(kb, kw_bound) : kw_bound;
+            }
+            if (kb > 0.f) {
+                // |q| of the bf16 values the products take; Cauchy-Schwarz bounds each
+                // score by |q| kb, and the margin covers the f32 accumulation.
+                float qn = 0.f;
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bf16x2 pr = {qf[c][2 * j], qf[c][2 * j + 1]};
+                        qn = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, qn, false);
+                    }
+                qn += __shfl_xor(qn, 32, 64);
+                shift = __builtin_sqrtf(qn) * kb * (1.0f + 1.0f / 1024);
             }
         } else {
             // q is taken as given: scaling it before the product would round it twice.
@@ -263,10 +310,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // Accumulator units: base 2 when q carries scale log2 e (PREP), else raw q.k, which
     // the exponent then scales.
     const float sc = PREP ? 1.0f : C;
-    float m_run = -INFINITY, l_run = 0.f;   // l_run: this lane's share of the row sum
+    // Fixed shift: when every row of the wave has a score bound no larger than
+    // kFixedShiftMax, each row's softmax is shifted by its bound from the start (the
+    // same softmax: numerator and denominator share the shift; every weight lies in
+    // [2^-96, 1], where f32 and bf16 keep their relative precision) and no running
+    // maximum is kept.  Otherwise the running maximum below.
+    const bool fixed = PREP && kb > 0.f &&
+                       __builtin_amdgcn_ballot_w64(!(shift <= kFixedShiftMax)) == 0;   // wave-uniform
+    float m_run = fixed ? shift : -INFINITY, l_run = 0.f;   // l_run: this lane's share of the row sum
     f32x16 bias;                             // -m_run (0 until the first visible key)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) bias[i] = 0.f;
+    for (int i = 0; i < 16; ++i) bias[i] = fixed ? -shift : 0.f;
     f32x16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -282,11 +336,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
+    // Key positions of this wave's first and last row: a tile whose first key lies past the
+    // last row's is skipped by the wave (it still loads and waits with the block).
+    const int64_t wfirst = row0w + qoff, wlast = row0w + 31 + qoff;
     for (int kt = 0; kt < ntiles; ++kt) {
         const int key0 = kt * kBN;
         const int bsel = kt & 1;
         if (kt + 1 < ntiles) load_tile(kt + 1, bsel ^ 1);
         const unsigned char *buf = smem + bsel * G::kBufBytes;
+        if (wrows == 0 || (CAUSAL && key0 > wlast)) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            continue;
+        }
 
         // S^T = K Q^T - m for 2 blocks of 32 keys (two independent accumulation chains).
         f32x16 s[2];
@@ -299,7 +361,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
         // Mask: register 4i+jj of block kb holds key key0 + 32 kb + 8 i + 4 g + jj.
-        const bool need_mask = (key0 + kBN > tk) || (CAUSAL && key0 + kBN - 1 > qtile * kBM + qoff);
+        const bool need_mask = (key0 + kBN > tk) || (CAUSAL && key0 + kBN - 1 > wfirst);
         if (need_mask) {
             const int lim = (CAUSAL ? min(tk - 1, (int)r + qoff) : tk - 1) - (key0 + 4 * g);   // last visible
 #pragma unroll
@@ -308,14 +370,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 for (int i = 0; i < 16; ++i)
                     if (32 * kb + 8 * (i / 4) + (i % 4) > lim) s[kb][i] = -INFINITY;
         }
-        float mx = fmaxf(s[0][0], s[0][1]);
+        float mx = -INFINITY;
+        if (!fixed) {
+            mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-        for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[0][i], s[0][i + 1]));
+            for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[0][i], s[0][i + 1]));
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[1][i], s[1][i + 1]));
-        mx = fmaxf(mx, lane_pair(mx, g));                     // tile max of s - m
+            for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[1][i], s[1][i + 1]));
+            mx = fmaxf(mx, lane_pair(mx, g));                 // tile max of s - m
+        }
         const bool first = m_run == -INFINITY;
-        const bool raise = first ? mx > -INFINITY : mx * sc > kRaiseAbove;
+        const bool raise = !fixed && (first ? mx > -INFINITY : mx * sc > kRaiseAbove);
         if (__builtin_amdgcn_ballot_w64(raise)) {            // wave-uniform, rare
             const float delta = raise ? mx : 0.f;
             const float alpha = fast_exp2(-delta * sc);
@@ -387,15 +452,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
+// Grid: z = query tile; when the (batch, kv head) pairs divide evenly over the XCDs,
+// x = 8 group so that consecutive blocks (dealt to XCDs round-robin) put each pair's
+// blocks on one XCD; else x and y carry head-in-group and pair.  Launch order is x,
+// then y, then z: the heads of one kv group run side by side, longest tiles first.
 template <int D, bool CAUSAL>
-void launch_bf16_d(const PrefillLaunch &a, hipStream_t stream) {
+hipError_t launch_bf16_d(const PrefillLaunch &a, hipStream_t stream) {
     const int64_t nq_tiles = (a.seq + kBM - 1) / kBM;
-    const dim3 grid((unsigned)(nq_tiles * a.batch * a.hq));
+    const int64_t group = a.hq / a.hkv, pairs = a.batch * a.hkv;
+    if (nq_tiles > 65535 || group > 65535 || pairs >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    PrefillGrid gr;
+    dim3 grid;
+    if (pairs % kXcds == 0 && kXcds * group <= 65535 && pairs / kXcds <= 65535) {
+        gr.mode = 0;
+        grid = dim3((unsigned)(kXcds * group), (unsigned)(pairs / kXcds), (unsigned)nq_tiles);
+    } else if (pairs <= 65535) {
+        gr.mode = 1;
+        grid = dim3((unsigned)group, (unsigned)pairs, (unsigned)nq_tiles);
+    } else {
+        gr.mode = 2;
+        grid = dim3((unsigned)pairs, (unsigned)group, (unsigned)nq_tiles);
+    }
+    gr.group = (int)group;
+    gr.hkv = (int)a.hkv;
+    int l = 0;
+    while (((int64_t)1 << l) < a.hkv) ++l;                    // ceil(log2 hkv)
+    gr.hkv_mul = (uint32_t)((((uint64_t)1 << (31 + l)) + (uint64_t)a.hkv - 1) / (uint64_t)a.hkv);
+    gr.hkv_shift = 31 + l;
     const size_t lds = 2 * Geo<D>::kBufBytes;
     if (a.prep_q)
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true>), grid, dim3(256), lds, stream, a);
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true>), grid, dim3(256), lds, stream, a, gr);
     else
-        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false>), grid, dim3(256), lds, stream, a);
+        hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, false>), grid, dim3(256), lds, stream, a, gr);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -417,12 +506,8 @@ hipError_t launch_prefill(const PrefillLaunch &a0, hipStream_t stream) {
     PrefillLaunch a = a0;
     prefill_defaults(a);
     if (!a.bf16) return launch_prefill_f32(a, stream);
-    if (a.d == 64) {
-        if (a.causal) launch_bf16_d<64, true>(a, stream); else launch_bf16_d<64, false>(a, stream);
-    } else {
-        if (a.causal) launch_bf16_d<128, true>(a, stream); else launch_bf16_d<128, false>(a, stream);
-    }
-    return hipGetLastError();
+    if (a.d == 64) return a.causal ? launch_bf16_d<64, true>(a, stream) : launch_bf16_d<64, false>(a, stream);
+    return a.causal ? launch_bf16_d<128, true>(a, stream) : launch_bf16_d<128, false>(a, stream);
 }
 
 }  // namespace attn

@@ -157,6 +157,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cache-copies", type=int, default=3)
     ap.add_argument("--long-calls", type=int, default=20, help="timed calls of the long prefill (0: skip)")
+    ap.add_argument("--paged-calls", type=int, default=30, help="timed calls of the paged decode (0: skip)")
     ap.add_argument("--chunk-calls", type=int, default=20, help="timed calls of the chunked prefill (0: skip)")
     ap.add_argument("--quant-calls", type=int, default=30,
                     help="timed calls of the decode against 8/8, 4/4 and 4/2-bit caches (0: skip)")
@@ -301,6 +302,40 @@ def main() -> int:
                 "frac_of_hbm_peak": round(gbq / PEAK_HBM_GBPS, 4), "splits": sq,
                 "speedup_vs_bf16_cache": round(float(dec_ms.mean() / msq.mean()), 3)}
             del qk, qv
+        torch.cuda.empty_cache()
+
+    # ---- the same decode through a paged pool: 64-row pages in a random order
+    paged_line = None
+    if args.paged_calls > 0:
+        page_rows = 64
+        per_seq = wd.seq // page_rows
+        num_pages = wd.batch * per_seq
+        perm = torch.from_numpy(np.random.default_rng(7).permutation(num_pages).astype(np.int64)).to(dev)
+        table = perm.view(wd.batch, per_seq).to(torch.int32).contiguous()
+        kps, vps = [], []
+        for c in range(len(kcs)):
+            kp = torch.empty_like(kcs[c]).view(num_pages, page_rows, wd.hkv, wd.d)
+            vp = torch.empty_like(vcs[c]).view(num_pages, page_rows, wd.hkv, wd.d)
+            kp[perm] = kcs[c].view(num_pages, page_rows, wd.hkv, wd.d)
+            vp[perm] = vcs[c].view(num_pages, page_rows, wd.hkv, wd.d)
+            kps.append(kp)
+            vps.append(vp)
+        turn = [0]
+
+        def callp():
+            c = turn[0] % len(kps)
+            turn[0] += 1
+            tah.attn_decode_paged(q4, kps[c], vps[c], table, lens, pos, wd.seq, prep=prep4, scale=wd.scale,
+                                  splits=splits, workspace=ws, out=out4, stream=stream)
+
+        msp = time_calls(callp, args.paged_calls)
+        gbp = nbytes / (msp.mean() * 1e-3) / 1e9
+        paged_line = {"workload": "the bf16 decode workload read through a paged pool (64-row pages, the page "
+                                  "table a random permutation), 3 pools in turn",
+                      "value": round(gbp, 2), "unit": "GB/s", "ms": stats_ms(msp), "bytes": nbytes,
+                      "frac_of_hbm_peak": round(gbp / PEAK_HBM_GBPS, 4),
+                      "vs_contiguous": round(float(dec_ms.mean() / msp.mean()), 3)}
+        del kps, vps
         torch.cuda.empty_cache()
 
     del q3, k3, v3, out3, kcs, vcs, k_raw, v_raw
@@ -486,6 +521,8 @@ def main() -> int:
         line["long_prefill"] = long_line
     if chunk_line is not None:
         line["chunk_prefill"] = chunk_line
+    if paged_line is not None:
+        line["decode_paged"] = paged_line
     if quant_lines:
         line["decode_quantized"] = dict(
             workload="bf16 decode workload against quantised caches (keys and values in k / v bits, per-head "

@@ -212,6 +212,30 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
                           void *stream);
 
 /*
+ * attn_decode_paged -- attn_decode over a paged KV pool (compute guide "Tensors, GPU
+ * kernels and AI models", Step 5: the engine's KV pool, which slots share by reading one
+ * copy of a common start's keys and values).  bf16 only.
+ *   k_pool, v_pool  [num_pages, page_rows, hkv, d]: each page is laid out as a cache of
+ *                   batch 1 and capacity page_rows (attn_prep and plain copies write rows
+ *                   into a page in place).
+ *   pages           [batch, max_pages] int32, device: key j of sequence b is row
+ *                   j % page_rows of page pages[b * max_pages + j / page_rows].  Pages may
+ *                   be shared between sequences (a common prefix is read from one copy).
+ *   page_rows       a power of two in [16, 2^20]; num_pages * page_rows < 2^31;
+ *                   max_len <= max_pages * page_rows.
+ *   Everything else is attn_decode's.  A page id outside [0, num_pages) among the pages
+ *   a sequence reads gives NaN rows for it (reads stay inside the pool).
+ *   ATTN_ERR_UNSUPPORTED for f32.
+ */
+attn_status_t attn_decode_paged(const void *q, const void *k_pool, const void *v_pool, void *out,
+                                int64_t batch, int64_t hq, int64_t hkv, int64_t d, int64_t num_pages,
+                                int64_t page_rows, const int32_t *pages, int64_t max_pages,
+                                const int32_t *lens, const int32_t *pos, int64_t max_len,
+                                const attn_headprep_t *prep, double scale, int64_t splits,
+                                void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
+                                void *stream);
+
+/*
  * Quantised KV cache (compute guide "Tensors, GPU kernels and AI models", Step 5: Run a
  * language model: keys and values kept in 8, 4 or 2 bits, or keys in 4 and values in 2,
  * each head coded over the range that returns it with the least squared error).
@@ -271,6 +295,22 @@ attn_status_t attn_decode_q(const void *q, const uint8_t *k_codes, const float *
                             int64_t v_bits, const int32_t *lens, const int32_t *pos, int64_t max_len,
                             const attn_headprep_t *prep, double scale, int64_t splits, void *workspace,
                             size_t workspace_bytes, attn_dtype_t dtype, void *stream);
+
+/*
+ * attn_decode_q_paged -- attn_decode_q over a paged pool of coded rows.  Each page is a
+ * quantised cache of batch 1 and capacity page_rows (codes [num_pages, hkv, page_rows,
+ * d bits / 8], params [num_pages, hkv, page_rows, 2]), so attn_kv_quantize with
+ * batch 1, capacity page_rows and row0 = the row in the page codes rows into a page.
+ * pages, page_rows, num_pages, max_pages and the bad-page rule are attn_decode_paged's.
+ */
+attn_status_t attn_decode_q_paged(const void *q, const uint8_t *k_codes, const float *k_params,
+                                  const uint8_t *v_codes, const float *v_params, void *out,
+                                  int64_t batch, int64_t hq, int64_t hkv, int64_t d, int64_t num_pages,
+                                  int64_t page_rows, int64_t k_bits, int64_t v_bits,
+                                  const int32_t *pages, int64_t max_pages, const int32_t *lens,
+                                  const int32_t *pos, int64_t max_len, const attn_headprep_t *prep,
+                                  double scale, int64_t splits, void *workspace, size_t workspace_bytes,
+                                  attn_dtype_t dtype, void *stream);
 
 /*
  * attn_rows -- full attention of packed rows, for image and video models (gizml:netops,

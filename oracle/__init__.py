@@ -17,6 +17,8 @@ chunked prefill against a KV cache, decode):
   "Functions > attentionRows" and "Functions > attendedRows".
 * the quantised KV cache's coding -- compute guide "Tensors, GPU kernels and AI models",
   "Step 5: Run a language model" (8, 4 or 2 bits, least-squared-error range per head).
+* the paged KV pool the engine's slots read their keys and values from (a page table
+  mapping each sequence's rows to pool pages) -- compute guide, Step 5.
 * headPrepInPlace's position rule (the table row of a token is its sequence row,
   ``row0`` being the row of the first) -- same page, "Functions > headPrepInPlace".
 """
@@ -27,6 +29,9 @@ from .oracle import (  # noqa: F401
     row_norm_rope,
     attention,
     attention_rows,
+    paged_rows,
+    gather_paged,
+    decode_paged,
     prefill,
     prefill_chunk,
     attended_rows,

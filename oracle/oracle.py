@@ -312,6 +312,35 @@ def decode(q, k_cache, v_cache, lens, pos, qw, cos, sin, half: int, eps: float,
     return out[:, 0]
 
 
+def paged_rows(pool, pages, length: int) -> np.ndarray:
+    """The first `length` cache rows of one sequence out of a paged pool (compute guide
+    "Tensors, GPU kernels and AI models", Step 5: the engine's KV pool): row j is row
+    j mod page_rows of page pages[j // page_rows].  pool [num_pages, page_rows, ...]."""
+    pool = np.asarray(pool)
+    page_rows = pool.shape[1]
+    j = np.arange(length)
+    return pool[np.asarray(pages, dtype=np.int64)[j // page_rows], j % page_rows]
+
+
+def gather_paged(pool, pages, lens) -> np.ndarray:
+    """Every sequence's cache out of a paged pool: [B, max(lens), ...], rows past lens[b]
+    zero (they are never attended)."""
+    pool = np.asarray(pool)
+    lens = [int(n) for n in lens]
+    out = np.zeros((len(lens), max(1, max(lens))) + pool.shape[2:], dtype=pool.dtype)
+    for b, n in enumerate(lens):
+        out[b, :n] = paged_rows(pool, pages[b], n)
+    return out
+
+
+def decode_paged(q, k_pool, v_pool, pages, lens, pos, qw, cos, sin, half: int, eps: float,
+                 scale: float) -> np.ndarray:
+    """decode over the caches a paged pool [num_pages, page_rows, hkv, d] holds for each
+    sequence (pages [B, max_pages])."""
+    return decode(q, gather_paged(k_pool, pages, lens), gather_paged(v_pool, pages, lens), lens, pos, qw, cos, sin,
+                  half, eps, scale)
+
+
 def decode_q(q, k_codes, k_lo, k_step, v_codes, v_lo, v_step, lens, pos, qw, cos, sin, half: int,
              eps: float, scale: float) -> np.ndarray:
     """Decode against a quantised cache: the cache [B, capacity, hkv, d] gives back

@@ -226,6 +226,55 @@ def test_decode_rejects(lib, kw, code):
     assert _decode(lib, **kw) == code
 
 
+def _decode_paged(lib, **kw):
+    # splits=4 and a bad argument in every case: each call fails on the host.
+    a = dict(q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), out=FAKE + (3 << 32), batch=32, hq=32,
+             hkv=8, d=128, num_pages=2048, page_rows=64, pages=FAKE + (7 << 32), max_pages=64,
+             lens=FAKE + (4 << 32), pos=FAKE + (5 << 32), max_len=4096, prep=_prep(rows=4097), scale=0.088,
+             splits=4, ws=FAKE + (6 << 32), ws_bytes=1 << 30, dtype=A.ATTN_BF16)
+    a.update(kw)
+    prep = ctypes.byref(a["prep"]) if a["prep"] is not None else None
+    return lib.attn_decode_paged(a["q"], a["k"], a["v"], a["out"], a["batch"], a["hq"], a["hkv"], a["d"],
+                                 a["num_pages"], a["page_rows"], a["pages"], a["max_pages"], a["lens"], a["pos"],
+                                 a["max_len"], prep, a["scale"], a["splits"], a["ws"], a["ws_bytes"], a["dtype"],
+                                 None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=A.ATTN_F32), A.ATTN_ERR_UNSUPPORTED),
+    (dict(pages=None), A.ATTN_ERR_ARG),
+    (dict(pages=FAKE + (7 << 32) + 2), A.ATTN_ERR_ARG),     # misaligned table
+    (dict(page_rows=48), A.ATTN_ERR_ARG),                    # not a power of two
+    (dict(page_rows=8, max_pages=512), A.ATTN_ERR_ARG),      # below 16
+    (dict(num_pages=0), A.ATTN_ERR_ARG),
+    (dict(num_pages=1 << 25), A.ATTN_ERR_ARG),               # num_pages * page_rows >= 2^31
+    (dict(max_pages=63), A.ATTN_ERR_ARG),                    # max_len > max_pages * page_rows
+    (dict(max_pages=0), A.ATTN_ERR_ARG),
+    (dict(ws_bytes=1000), A.ATTN_ERR_WORKSPACE),
+    (dict(lens=None), A.ATTN_ERR_ARG),
+    (dict(out=FAKE + (7 << 32)), A.ATTN_ERR_ARG),            # out overlaps the page table
+])
+def test_decode_paged_rejects(lib, kw, code):
+    assert _decode_paged(lib, **kw) == code
+    assert lib.attn_last_error()
+
+
+def test_decode_q_paged_rejects(lib):
+    def call(**kw):
+        a = dict(bits=(4, 4), page_rows=64, pages=FAKE + (7 << 32), dtype=A.ATTN_BF16, ws_bytes=1000)
+        a.update(kw)
+        prep = _prep(rows=4097)
+        return lib.attn_decode_q_paged(FAKE, FAKE + (1 << 32), FAKE + (2 << 32), FAKE + (3 << 32), FAKE + (4 << 32),
+                                       FAKE + (5 << 32), 32, 32, 8, 128, 2048, a["page_rows"], a["bits"][0],
+                                       a["bits"][1], a["pages"], 64, FAKE + (6 << 32), FAKE + (8 << 32), 4096,
+                                       ctypes.byref(prep), 0.088, 4, FAKE + (9 << 32), a["ws_bytes"], a["dtype"], None)
+    assert call() == A.ATTN_ERR_WORKSPACE
+    assert call(bits=(8, 4)) == A.ATTN_ERR_ARG
+    assert call(page_rows=100) == A.ATTN_ERR_ARG
+    assert call(pages=None) == A.ATTN_ERR_ARG
+    assert call(dtype=A.ATTN_F32) == A.ATTN_ERR_UNSUPPORTED
+
+
 def test_decode_sizes(lib):
     # 256 (sequence, kv head) units already give every CU a block: one split, no workspace
     assert lib.attn_decode_default_splits(32, 32, 8, 4096) == 1

@@ -646,3 +646,70 @@ def test_workload_shapes_and_tables():
     cos, sin = synthetic.rope_tables(5, 64, 128, 1e6)
     ang = 3 * 1e6 ** (-2 * 5 / 128)
     assert cos[3, 5] == np.float32(math.cos(ang)) and sin[3, 5] == np.float32(math.sin(ang))
+
+
+# ----------------------------------------------------------------------- paged KV pool
+
+def _scatter_pool(caches, lens, page_rows, num_pages, shared, rng):
+    """Write each sequence's rows into pages of a pool, page by page, with a loop of its
+    own: a random distinct page per (sequence, page slot), except that the first `shared`
+    page slots of every sequence point at sequence 0's pages (their rows must be equal)."""
+    B = caches.shape[0]
+    max_pages = (caches.shape[1] + page_rows - 1) // page_rows
+    free = list(rng.permutation(num_pages))
+    pages = np.full((B, max_pages), -1, dtype=np.int32)
+    pool = np.full((num_pages, page_rows) + caches.shape[2:], np.nan)
+    for b in range(B):
+        for slot in range((lens[b] + page_rows - 1) // page_rows):
+            if b > 0 and slot < shared:
+                pages[b, slot] = pages[0, slot]
+                continue
+            pages[b, slot] = free.pop()
+            for r in range(page_rows):
+                j = slot * page_rows + r
+                if j < lens[b]:
+                    pool[pages[b, slot], r] = caches[b, j]
+    return pool, pages
+
+
+def test_paged_rows_give_back_the_scattered_caches():
+    """Gathering through the page table returns every sequence's rows exactly, with shared
+    prefix pages read by several sequences from one copy."""
+    rng = np.random.default_rng(41)
+    B, L, P = 3, 70, 16
+    caches = rng.standard_normal((B, L, 2, 8))
+    caches[1:, :32] = caches[0, :32]                 # a common start of two full pages
+    lens = [70, 45, 33]
+    pool, pages = _scatter_pool(caches, lens, P, 20, shared=2, rng=rng)
+    assert (pages[1, :2] == pages[0, :2]).all() and (pages[2, :2] == pages[0, :2]).all()
+    for b in range(B):
+        np.testing.assert_array_equal(oracle.paged_rows(pool, pages[b], lens[b]), caches[b, :lens[b]])
+    got = oracle.gather_paged(pool, pages, lens)
+    for b in range(B):
+        np.testing.assert_array_equal(got[b, :lens[b]], caches[b, :lens[b]])
+        assert (got[b, lens[b]:] == 0).all()
+
+
+def test_decode_paged_is_decode_of_the_gathered_caches():
+    """decode_paged equals decode on contiguous caches holding the same rows (and is not
+    fooled by NaN rows of unused pool slots)."""
+    rng = np.random.default_rng(43)
+    B, L, hq, hkv, d, P = 2, 50, 4, 2, 16, 16
+    k = rng.standard_normal((B, L, hkv, d))
+    v = rng.standard_normal((B, L, hkv, d))
+    lens = [50, 21]
+    kp, pages = _scatter_pool(k, lens, P, 10, shared=0, rng=np.random.default_rng(1))
+    vp, pages_v = _scatter_pool(v, lens, P, 10, shared=0, rng=np.random.default_rng(1))
+    assert (pages == pages_v).all()
+    q = rng.standard_normal((B, hq, d))
+    qw = np.ones(d)
+    cos, sin = synthetic.rope_tables(64, d // 2, d, 1e4)
+    kc = np.zeros((B, L, hkv, d))
+    vc = np.zeros((B, L, hkv, d))
+    for b in range(B):
+        kc[b, :lens[b]] = k[b, :lens[b]]
+        vc[b, :lens[b]] = v[b, :lens[b]]
+    ref = oracle.decode(q, kc, vc, lens, [50, 21], qw, cos, sin, d // 2, 1e-6, 0.25)
+    got = oracle.decode_paged(q, kp, vp, pages, lens, [50, 21], qw, cos, sin, d // 2, 1e-6, 0.25)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+    assert np.isfinite(got).all()

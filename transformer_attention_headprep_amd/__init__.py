@@ -11,7 +11,9 @@ from .attn import (  # noqa: F401
     LIB_PATH,
     EXPORTS,
     attn_decode,
+    attn_decode_paged,
     attn_decode_q,
+    attn_decode_q_paged,
     attn_kv_quantize,
     attn_prefill,
     attn_prefill_chunk,

@@ -21,7 +21,8 @@ ATTN_OK, ATTN_ERR_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 
 
 # The entry points include/attn.h declares (checked by the CPU test suite).
 EXPORTS = ("attn_prep", "attn_prefill", "attn_prefill_chunk", "attn_decode", "attn_decode_workspace_size",
-           "attn_decode_default_splits", "attn_kv_quantize", "attn_decode_q", "attn_decode_q_default_splits", "attn_rows", "attn_rows8_layout", "attn_rows8_quantize",
+           "attn_decode_default_splits", "attn_decode_paged", "attn_kv_quantize", "attn_decode_q",
+           "attn_decode_q_paged", "attn_decode_q_default_splits", "attn_rows", "attn_rows8_layout", "attn_rows8_quantize",
            "attn_rows8_attend", "attn_rows8", "attn_row_norm_rope", "attn_key_bound", "attn_supported",
            "attn_status_str", "attn_last_error")
 
@@ -86,6 +87,12 @@ def load_library(path: str = LIB_PATH):
     lib.attn_rows.restype = ctypes.c_int
     lib.attn_row_norm_rope.argtypes = [_vp] + [_i64] * 4 + [_vp, _vp, _vp, _dbl, ctypes.c_int, _vp]
     lib.attn_row_norm_rope.restype = ctypes.c_int
+    lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 6 + [_vp, _i64, _vp, _vp, _i64, hp, _dbl, _i64,
+                                                                            _vp, ctypes.c_size_t, ctypes.c_int, _vp]
+    lib.attn_decode_paged.restype = ctypes.c_int
+    lib.attn_decode_q_paged.argtypes = [_vp] * 6 + [_i64] * 8 + [_vp, _i64, _vp, _vp, _i64, hp, _dbl, _i64, _vp,
+                                                                  ctypes.c_size_t, ctypes.c_int, _vp]
+    lib.attn_decode_q_paged.restype = ctypes.c_int
     lib.attn_key_bound.argtypes = [_vp, _i64]
     lib.attn_key_bound.restype = _dbl
     lib.attn_supported.argtypes = [_i64, ctypes.c_int]
@@ -306,6 +313,39 @@ def attn_decode_q(q, k: QuantCache, v: QuantCache, lens, pos, max_len: int, prep
     return out
 
 
+def attn_decode_q_paged(q, k: QuantCache, v: QuantCache, pages, lens, pos, max_len: int,
+                        prep: HeadPrep | None = None, scale: float | None = None, splits: int = 0, workspace=None,
+                        out=None, stream=None) -> torch.Tensor:
+    """attn_decode_q over a paged pool: k and v are QuantCaches whose batch axis is the pool's
+    pages (capacity = page_rows); pages [B, max_pages] int32 maps sequence rows to pages."""
+    lib = load_library()
+    B, hq, D = q.shape
+    num_pages, hkv, page_rows = k.codes.shape[0], k.codes.shape[1], k.capacity
+    if q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bfloat16 tensor")
+    if pages.dtype != torch.int32 or pages.dim() != 2 or pages.shape[0] != B or not pages.is_contiguous():
+        raise TypeError("pages must be a contiguous int32 [B, max_pages] device tensor")
+    if lens.dtype != torch.int32 or (pos is not None and pos.dtype != torch.int32):
+        raise TypeError("lens and pos must be int32 device tensors")
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if splits == 0:
+        splits = int(lib.attn_decode_q_default_splits(B, hq, hkv, max_len, k.bits))
+    need = decode_workspace_size(B, hq, hkv, D, max_len, splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = prep.struct() if prep is not None else None
+    _check(lib.attn_decode_q_paged(_ptr(q), _ptr(k.codes), _ptr(k.params), _ptr(v.codes), _ptr(v.params), _ptr(out),
+                                   B, hq, hkv, D, num_pages, page_rows, k.bits, v.bits, _ptr(pages), pages.shape[1],
+                                   _ptr(lens), _ptr(pos), max_len, ctypes.byref(st) if st is not None else None,
+                                   float(scale), splits, _ptr(workspace),
+                                   0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                   ATTN_BF16, _stream(stream)))
+    return out
+
+
 def attn_rows(qkv, heads: int, head: int, group: int = 0, queries: int = 0, out=None,
               prep: HeadPrep | None = None, stream=None) -> torch.Tensor:
     """Full attention of packed rows qkv [n, 3 * heads * head] (q, k, v of every head), each
@@ -437,4 +477,35 @@ def attn_decode(q, k_cache, v_cache, lens, pos, max_len: int, prep: HeadPrep | N
                            ctypes.byref(st) if st is not None else None, float(scale), splits,
                            _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
                            _dtype_code(q), _stream(stream)))
+    return out
+
+
+def attn_decode_paged(q, k_pool, v_pool, pages, lens, pos, max_len: int, prep: HeadPrep | None = None,
+                      scale: float | None = None, splits: int = 0, workspace=None, out=None,
+                      stream=None) -> torch.Tensor:
+    """One bf16 query row per sequence (q [B, Hq, D]) against a paged pool k_pool, v_pool
+    [num_pages, page_rows, Hkv, D]; pages [B, max_pages] int32 maps sequence rows to pages."""
+    lib = load_library()
+    B, hq, D = q.shape
+    num_pages, page_rows, hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("pages", pages)):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if pages.dtype != torch.int32 or pages.dim() != 2 or pages.shape[0] != B:
+        raise TypeError("pages must be an int32 [B, max_pages] device tensor")
+    if lens.dtype != torch.int32 or (pos is not None and pos.dtype != torch.int32):
+        raise TypeError("lens and pos must be int32 device tensors")
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = decode_workspace_size(B, hq, hkv, D, max_len, splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = prep.struct() if prep is not None else None
+    _check(lib.attn_decode_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), B, hq, hkv, D, num_pages, page_rows,
+                                 _ptr(pages), pages.shape[1], _ptr(lens), _ptr(pos), max_len,
+                                 ctypes.byref(st) if st is not None else None, float(scale), splits,
+                                 _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                 _dtype_code(q), _stream(stream)))
     return out

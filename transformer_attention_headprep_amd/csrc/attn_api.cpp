@@ -170,6 +170,31 @@ attn_status_t rows8_launch(const void *qkv, int64_t n, int64_t heads, int64_t he
     return ATTN_OK;
 }
 
+// A paged KV pool: the page table and its sizes.
+struct Paging {
+    const int32_t *pages;      // [batch, max_pages] pool page of each sequence's rows
+    int64_t page_rows, max_pages, num_pages;
+};
+
+attn_status_t check_paging(const Paging &pg, int64_t max_len, int64_t batch) {
+    if (!pg.pages) return fail(ATTN_ERR_ARG, "pages is NULL");
+    if ((reinterpret_cast<uintptr_t>(pg.pages) & 3) != 0) return fail(ATTN_ERR_ARG, "pages is not 4-byte aligned");
+    if (pg.page_rows < 16 || pg.page_rows > ((int64_t)1 << 20) || (pg.page_rows & (pg.page_rows - 1)) != 0)
+        return fail(ATTN_ERR_ARG, "page_rows %lld is not a power of two in [16, 2^20]", (long long)pg.page_rows);
+    if (pg.num_pages < 1 || pg.num_pages * pg.page_rows >= ((int64_t)1 << 31))
+        return fail(ATTN_ERR_ARG, "num_pages %lld outside [1, 2^31 / page_rows)", (long long)pg.num_pages);
+    if (pg.max_pages < 1 || batch * pg.max_pages >= ((int64_t)1 << 31))
+        return fail(ATTN_ERR_ARG, "max_pages %lld outside [1, 2^31 / batch)", (long long)pg.max_pages);
+    if (max_len < 1 || max_len > pg.max_pages * pg.page_rows)
+        return fail(ATTN_ERR_ARG, "max_len %lld outside [1, max_pages * page_rows]", (long long)max_len);
+    return ATTN_OK;
+}
+
+Span table_span(const Paging &pg, int64_t batch) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(pg.pages);
+    return Span{a, a + (uintptr_t)(batch * pg.max_pages * 4)};
+}
+
 }  // namespace
 
 extern "C" {
@@ -522,14 +547,15 @@ size_t attn_decode_workspace_size(int64_t batch, int64_t hq, int64_t hkv, int64_
     return attn::decode_workspace_bytes(batch, hq, d, splits);
 }
 
-attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *out, int64_t batch,
-                          int64_t hq, int64_t hkv, int64_t d, int64_t capacity, const int32_t *lens,
-                          const int32_t *pos, int64_t max_len, const attn_headprep_t *prep, double scale,
-                          int64_t splits, void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
-                          void *stream) {
+static attn_status_t decode_impl(const void *q, const void *k_cache, const void *v_cache, void *out, int64_t batch,
+                                 int64_t hq, int64_t hkv, int64_t d, int64_t capacity, const Paging *pg,
+                                 const int32_t *lens, const int32_t *pos, int64_t max_len,
+                                 const attn_headprep_t *prep, double scale, int64_t splits, void *workspace,
+                                 size_t workspace_bytes, attn_dtype_t dtype, void *stream, const char *name) {
     g_last_error[0] = 0;
     attn_status_t st = check_dtype_d(dtype, d);
     if (st) return st;
+    if (pg && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "paged pools hold bf16 rows");
     if (batch < 0) return fail(ATTN_ERR_ARG, "negative batch");
     if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
         return fail(ATTN_ERR_ARG, "hq = %lld must be a positive multiple of hkv = %lld", (long long)hq, (long long)hkv);
@@ -538,8 +564,15 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
     if ((st = check_rows("v_cache", v_cache, hkv, d, hkv * d))) return st;
     if ((st = check_rows("out", out, hq, d, hq * d))) return st;
     if (!lens) return fail(ATTN_ERR_ARG, "lens is NULL");
-    if (capacity <= 0 || capacity >= ((int64_t)1 << 31)) return fail(ATTN_ERR_ARG, "capacity %lld outside [1, 2^31)", (long long)capacity);
-    if (max_len < 1 || max_len > capacity) return fail(ATTN_ERR_ARG, "max_len %lld outside [1, capacity]", (long long)max_len);
+    int64_t rows;                              // cache rows the pointers span
+    if (pg) {
+        if ((st = check_paging(*pg, max_len, batch))) return st;
+        rows = pg->num_pages * pg->page_rows;
+    } else {
+        if (capacity <= 0 || capacity >= ((int64_t)1 << 31)) return fail(ATTN_ERR_ARG, "capacity %lld outside [1, 2^31)", (long long)capacity);
+        if (max_len < 1 || max_len > capacity) return fail(ATTN_ERR_ARG, "max_len %lld outside [1, capacity]", (long long)max_len);
+        rows = batch * capacity;
+    }
     if (splits < 0 || splits > max_len) return fail(ATTN_ERR_ARG, "splits %lld outside [0, max_len]", (long long)splits);
     if (!std::isfinite(scale) || !(scale > 0.0)) return fail(ATTN_ERR_ARG, "scale must be finite and > 0");
     if (prep) {
@@ -561,14 +594,18 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
     const Span so = span(out, batch, hq * d, hq, d, es);
     const Span sw{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
     if (overlap(so, span(q, batch, hq * d, hq, d, es)) || overlap(so, sw) ||
-        overlap(so, span(k_cache, batch * capacity, hkv * d, hkv, d, es)) ||
-        overlap(so, span(v_cache, batch * capacity, hkv * d, hkv, d, es)))
+        overlap(so, span(k_cache, rows, hkv * d, hkv, d, es)) ||
+        overlap(so, span(v_cache, rows, hkv * d, hkv, d, es)) ||
+        (pg && overlap(so, table_span(*pg, batch))))
         return fail(ATTN_ERR_ARG, "out overlaps an input or the workspace");
 
     attn::DecodeLaunch a{};
     a.q = q; a.k = k_cache; a.v = v_cache; a.out = out;
-    a.batch = batch; a.hq = hq; a.hkv = hkv; a.d = d; a.capacity = capacity; a.max_len = max_len;
+    a.batch = batch; a.hq = hq; a.hkv = hkv; a.d = d; a.capacity = pg ? pg->page_rows : capacity; a.max_len = max_len;
     a.lens = lens; a.pos = pos;
+    if (pg) {
+        a.pages = pg->pages; a.page_rows = pg->page_rows; a.max_pages = pg->max_pages; a.num_pages = pg->num_pages;
+    }
     a.prep_q = prep != nullptr;
     if (prep) {
         a.qw = prep->qw; a.cos = prep->cos; a.sin = prep->sin; a.half = prep->half;
@@ -576,7 +613,26 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
     }
     a.scale = (float)scale; a.splits = splits; a.work = static_cast<float *>(workspace);
     a.bf16 = dtype == ATTN_BF16;
-    return hip_status(attn::launch_decode(a, static_cast<hipStream_t>(stream)), "attn_decode");
+    return hip_status(attn::launch_decode(a, static_cast<hipStream_t>(stream)), name);
+}
+
+attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *out, int64_t batch,
+                          int64_t hq, int64_t hkv, int64_t d, int64_t capacity, const int32_t *lens,
+                          const int32_t *pos, int64_t max_len, const attn_headprep_t *prep, double scale,
+                          int64_t splits, void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
+                          void *stream) {
+    return decode_impl(q, k_cache, v_cache, out, batch, hq, hkv, d, capacity, nullptr, lens, pos, max_len, prep,
+                       scale, splits, workspace, workspace_bytes, dtype, stream, "attn_decode");
+}
+
+attn_status_t attn_decode_paged(const void *q, const void *k_pool, const void *v_pool, void *out, int64_t batch,
+                                int64_t hq, int64_t hkv, int64_t d, int64_t num_pages, int64_t page_rows,
+                                const int32_t *pages, int64_t max_pages, const int32_t *lens, const int32_t *pos,
+                                int64_t max_len, const attn_headprep_t *prep, double scale, int64_t splits,
+                                void *workspace, size_t workspace_bytes, attn_dtype_t dtype, void *stream) {
+    const Paging pg{pages, page_rows, max_pages, num_pages};
+    return decode_impl(q, k_pool, v_pool, out, batch, hq, hkv, d, 0, &pg, lens, pos, max_len, prep, scale, splits,
+                       workspace, workspace_bytes, dtype, stream, "attn_decode_paged");
 }
 
 attn_status_t attn_kv_quantize(const void *x, int64_t batch, int64_t seq, int64_t heads, int64_t d,
@@ -608,12 +664,13 @@ attn_status_t attn_kv_quantize(const void *x, int64_t batch, int64_t seq, int64_
     return hip_status(attn::launch_kv_quantize(a, static_cast<hipStream_t>(stream)), "attn_kv_quantize");
 }
 
-attn_status_t attn_decode_q(const void *q, const uint8_t *k_codes, const float *k_params, const uint8_t *v_codes,
-                            const float *v_params, void *out, int64_t batch, int64_t hq, int64_t hkv, int64_t d,
-                            int64_t capacity, int64_t k_bits, int64_t v_bits, const int32_t *lens,
-                            const int32_t *pos, int64_t max_len, const attn_headprep_t *prep, double scale,
-                            int64_t splits, void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
-                            void *stream) {
+static attn_status_t decode_q_impl(const void *q, const uint8_t *k_codes, const float *k_params,
+                                   const uint8_t *v_codes, const float *v_params, void *out, int64_t batch,
+                                   int64_t hq, int64_t hkv, int64_t d, int64_t capacity, const Paging *pg,
+                                   int64_t k_bits, int64_t v_bits, const int32_t *lens, const int32_t *pos,
+                                   int64_t max_len, const attn_headprep_t *prep, double scale, int64_t splits,
+                                   void *workspace, size_t workspace_bytes, attn_dtype_t dtype, void *stream,
+                                   const char *name) {
     g_last_error[0] = 0;
     attn_status_t st = check_dtype_d(dtype, d);
     if (st) return st;
@@ -631,8 +688,15 @@ attn_status_t attn_decode_q(const void *q, const uint8_t *k_codes, const float *
     if (!aligned16(k_codes) || !aligned16(k_params) || !aligned16(v_codes) || !aligned16(v_params))
         return fail(ATTN_ERR_ARG, "cache pointers must be 16-byte aligned");
     if (!lens) return fail(ATTN_ERR_ARG, "lens is NULL");
-    if (capacity <= 0 || capacity >= ((int64_t)1 << 31)) return fail(ATTN_ERR_ARG, "capacity %lld outside [1, 2^31)", (long long)capacity);
-    if (max_len < 1 || max_len > capacity) return fail(ATTN_ERR_ARG, "max_len %lld outside [1, capacity]", (long long)max_len);
+    int64_t units, urows;                      // the caches' units (sequences or pages) and rows per unit
+    if (pg) {
+        if ((st = check_paging(*pg, max_len, batch))) return st;
+        units = pg->num_pages; urows = pg->page_rows;
+    } else {
+        if (capacity <= 0 || capacity >= ((int64_t)1 << 31)) return fail(ATTN_ERR_ARG, "capacity %lld outside [1, 2^31)", (long long)capacity);
+        if (max_len < 1 || max_len > capacity) return fail(ATTN_ERR_ARG, "max_len %lld outside [1, capacity]", (long long)max_len);
+        units = batch; urows = capacity;
+    }
     if (splits < 0 || splits > max_len) return fail(ATTN_ERR_ARG, "splits %lld outside [0, max_len]", (long long)splits);
     if (!std::isfinite(scale) || !(scale > 0.0)) return fail(ATTN_ERR_ARG, "scale must be finite and > 0");
     if (prep) {
@@ -643,7 +707,7 @@ attn_status_t attn_decode_q(const void *q, const uint8_t *k_codes, const float *
     if (batch == 0) return ATTN_OK;
     if (splits == 0) splits = attn::decode_q_default_splits(batch, hq, hkv, max_len, k_bits);
     if (splits * batch >= ((int64_t)1 << 31) || splits >= 65536 || batch >= 65536 || hkv * hq >= 65536 ||
-        batch * hkv * capacity * d >= ((int64_t)1 << 40))
+        units * hkv * urows * d >= ((int64_t)1 << 40) || units * hkv * urows >= ((int64_t)1 << 31))
         return fail(ATTN_ERR_ARG, "problem too large for one launch");
     const size_t need = attn::decode_workspace_bytes(batch, hq, d, splits);
     if (need > 0) {
@@ -657,16 +721,20 @@ attn_status_t attn_decode_q(const void *q, const uint8_t *k_codes, const float *
         const uintptr_t a = reinterpret_cast<uintptr_t>(ptr);
         return Span{a, a + (uintptr_t)n};
     };
-    const int64_t rows = batch * hkv * capacity;
+    const int64_t rows = units * hkv * urows;
     if (overlap(so, span(q, batch, hq * d, hq, d, 2)) || overlap(so, sw) ||
         overlap(so, bytes_span(k_codes, rows * d * k_bits / 8)) || overlap(so, bytes_span(v_codes, rows * d * v_bits / 8)) ||
-        overlap(so, bytes_span(k_params, rows * 8)) || overlap(so, bytes_span(v_params, rows * 8)))
+        overlap(so, bytes_span(k_params, rows * 8)) || overlap(so, bytes_span(v_params, rows * 8)) ||
+        (pg && overlap(so, table_span(*pg, batch))))
         return fail(ATTN_ERR_ARG, "out overlaps an input or the workspace");
 
     attn::DecodeLaunch a{};
     a.q = q; a.k = k_codes; a.v = v_codes; a.out = out;
-    a.batch = batch; a.hq = hq; a.hkv = hkv; a.d = d; a.capacity = capacity; a.max_len = max_len;
+    a.batch = batch; a.hq = hq; a.hkv = hkv; a.d = d; a.capacity = urows; a.max_len = max_len;
     a.lens = lens; a.pos = pos;
+    if (pg) {
+        a.pages = pg->pages; a.page_rows = pg->page_rows; a.max_pages = pg->max_pages; a.num_pages = pg->num_pages;
+    }
     a.prep_q = prep != nullptr;
     if (prep) {
         a.qw = prep->qw; a.cos = prep->cos; a.sin = prep->sin; a.half = prep->half;
@@ -675,7 +743,31 @@ attn_status_t attn_decode_q(const void *q, const uint8_t *k_codes, const float *
     a.scale = (float)scale; a.splits = splits; a.work = static_cast<float *>(workspace);
     a.bf16 = true;
     a.kpar = k_params; a.vpar = v_params; a.kbits = (int)k_bits; a.vbits = (int)v_bits;
-    return hip_status(attn::launch_decode(a, static_cast<hipStream_t>(stream)), "attn_decode_q");
+    return hip_status(attn::launch_decode(a, static_cast<hipStream_t>(stream)), name);
+}
+
+attn_status_t attn_decode_q(const void *q, const uint8_t *k_codes, const float *k_params, const uint8_t *v_codes,
+                            const float *v_params, void *out, int64_t batch, int64_t hq, int64_t hkv, int64_t d,
+                            int64_t capacity, int64_t k_bits, int64_t v_bits, const int32_t *lens,
+                            const int32_t *pos, int64_t max_len, const attn_headprep_t *prep, double scale,
+                            int64_t splits, void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
+                            void *stream) {
+    return decode_q_impl(q, k_codes, k_params, v_codes, v_params, out, batch, hq, hkv, d, capacity, nullptr, k_bits,
+                         v_bits, lens, pos, max_len, prep, scale, splits, workspace, workspace_bytes, dtype, stream,
+                         "attn_decode_q");
+}
+
+attn_status_t attn_decode_q_paged(const void *q, const uint8_t *k_codes, const float *k_params,
+                                  const uint8_t *v_codes, const float *v_params, void *out, int64_t batch, int64_t hq,
+                                  int64_t hkv, int64_t d, int64_t num_pages, int64_t page_rows, int64_t k_bits,
+                                  int64_t v_bits, const int32_t *pages, int64_t max_pages, const int32_t *lens,
+                                  const int32_t *pos, int64_t max_len, const attn_headprep_t *prep, double scale,
+                                  int64_t splits, void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
+                                  void *stream) {
+    const Paging pg{pages, page_rows, max_pages, num_pages};
+    return decode_q_impl(q, k_codes, k_params, v_codes, v_params, out, batch, hq, hkv, d, 0, &pg, k_bits, v_bits, lens,
+                         pos, max_len, prep, scale, splits, workspace, workspace_bytes, dtype, stream,
+                         "attn_decode_q_paged");
 }
 
 double attn_key_bound(const float *kw, int64_t d) {

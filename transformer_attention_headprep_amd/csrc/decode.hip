@@ -44,9 +44,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
     // One LDS region, reused: q rows (prologue), then one K and one V chunk per wave,
     // then the waves' outputs (after a block barrier); the q fragments follow it.
     __shared__ __attribute__((aligned(16))) unsigned char smem[kTiles + kQFrag];
+    __shared__ int s_page_bad;                 // some wave met a page id outside the pool
 
     const int tid = threadIdx.x, lane = tid % 64;
     const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+    if (tid == 0) s_page_bad = 0;              // seen by all after the prologue's barriers
     const BlockCoord bc = block_coord(p);
     const int b = bc.b, split = bc.split;
     const int h0 = bc.kvh * p.group + bc.grp * GB;
@@ -59,8 +61,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
     const int end = min(len, start + (int)p.per_split);
 
     const int64_t rowb = p.hkv * D * 2;       // bytes between consecutive cache rows
-    const uint8_t *kbase = static_cast<const uint8_t *>(p.k) + ((int64_t)b * p.capacity * p.hkv + bc.kvh) * D * 2;
-    const uint8_t *vbase = static_cast<const uint8_t *>(p.v) + ((int64_t)b * p.capacity * p.hkv + bc.kvh) * D * 2;
+    // Cache row r (of every sequence, or of the pool) starts at r rowb; this kv head's
+    // part of it kvh D 2 bytes further.
+    const uint8_t *kbase = static_cast<const uint8_t *>(p.k) + (int64_t)bc.kvh * D * 2;
+    const uint8_t *vbase = static_cast<const uint8_t *>(p.v) + (int64_t)bc.kvh * D * 2;
+    const int64_t urows = unit_rows(p);
+    bool page_bad = false;
     unsigned char *kbuf = smem + w * 2 * G::kBuf;    // this wave's K chunk
     unsigned char *vbuf = kbuf + G::kBuf;            // and V chunk
 
@@ -80,14 +86,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
     };
     // Chunk j's rows, read through descriptors that end at the cache's last valid row
     // (rows past it, and every row of a chunk past the end, read as zero without a fetch).
+    // A chunk's 16 rows lie in one unit (pages hold a multiple of 16 rows).
     auto issue = [&](int j, Regs &r) {
         const int key0 = first + kChunk * kWaves * j;
         const int64_t bytes = (int64_t)min(kChunk, end - key0) * rowb;
+        const CacheSlot cs = key0 < end ? cache_slot(p, b, key0, page_bad) : CacheSlot{0, 0};
+        const int64_t crow = (int64_t)cs.unit * urows + cs.row;
 #pragma unroll
         for (int i = 0; i < G::kLoads; ++i) {
             const int64_t skip = (int64_t)(G::kRpi * i) * rowb;
-            r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(seq_rsrc(kbase + key0 * rowb + skip, bytes - skip), loff, 0, 0);
-            r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(seq_rsrc(vbase + key0 * rowb + skip, bytes - skip), loff, 0, 0);
+            r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(seq_rsrc(kbase + crow * rowb + skip, bytes - skip), loff, 0, 0);
+            r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(seq_rsrc(vbase + crow * rowb + skip, bytes - skip), loff, 0, 0);
         }
     };
 
@@ -197,6 +206,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
     // ---- merge: the lanes of one head (kk), then the waves.
     float l_head = l_lane + __shfl_xor(l_lane, 16, 64);
     l_head += __shfl_xor(l_head, 32, 64);
+    if (page_bad && lane == 0) s_page_bad = 1;
     __syncthreads();                          // every wave is done with its chunk buffers
     float (*wo)[GB][D] = reinterpret_cast<float (*)[GB][D]>(smem);
     float (*wm)[GB] = reinterpret_cast<float (*)[GB]>(smem + kWaves * GB * D * 4);
@@ -210,7 +220,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
         }
     }
     __syncthreads();
-    write_partial<true, D, GB>(p, split, b, h0, nh, wm, wl, wo);
+    write_partial<true, D, GB>(p, split, b, h0, nh, wm, wl, wo, s_page_bad != 0);
 }
 
 // ---------------------------------------------------------------------------------
@@ -390,7 +400,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float *work, void
         }
     }
     float y = L > 0.f ? A / L : 0.f;
-    if (bad) y = __builtin_nanf("");
+    if (bad || L != L) y = __builtin_nanf("");
     if constexpr (BF16) {
         f32x2 v2 = {y, 0.f};
         bf16x2 hv = __builtin_convertvector(v2, bf16x2);
@@ -479,6 +489,12 @@ DecodeParams make_decode_params(const DecodeLaunch &a) {
     p.prep_q = a.prep_q;
     p.pairs = a.prep_q && a.pairs;
     p.kpar = a.kpar; p.vpar = a.vpar;
+    p.pages = a.pages;
+    p.page_shift = 0;
+    if (a.pages)
+        while (((int64_t)1 << p.page_shift) < a.page_rows) ++p.page_shift;
+    p.max_pages = (int)a.max_pages;
+    p.num_pages = (int)a.num_pages;
     return p;
 }
 

@@ -21,6 +21,10 @@ struct DecodeParams {
     float eps, C;
     bool prep_q, pairs;
     const float *kpar, *vpar;   // quantised caches: (lo, step) of every cached head
+    // Paged pool (pages != NULL): key j of sequence b lives in pool page
+    // pages[b max_pages + j / page_rows], row j % page_rows; page_rows = 2^page_shift.
+    const int32_t *pages;
+    int page_shift, max_pages, num_pages;
 };
 
 namespace {
@@ -43,6 +47,27 @@ __device__ __forceinline__ BlockCoord block_coord(const DecodeParams &p) {
     c.split = blockIdx.y;
     c.b = blockIdx.z;
     return c;
+}
+
+// Where key `key` (< max_len) of sequence b lives: the unit (sequence b of a contiguous
+// cache, or the pool page holding it) and the row within it.  A page id outside the pool
+// is replaced by page 0 (every read stays inside the pool) and sets `bad`.
+struct CacheSlot {
+    int unit, row;
+};
+__device__ __forceinline__ CacheSlot cache_slot(const DecodeParams &p, int b, int key, bool &bad) {
+    if (!p.pages) return CacheSlot{b, key};
+    int id = p.pages[(int64_t)b * p.max_pages + (key >> p.page_shift)];
+    if ((unsigned)id >= (unsigned)p.num_pages) {
+        bad = true;
+        id = 0;
+    }
+    return CacheSlot{id, key & ((1 << p.page_shift) - 1)};
+}
+
+// Rows per unit: the capacity of a contiguous cache, or the page size.
+__device__ __forceinline__ int64_t unit_rows(const DecodeParams &p) {
+    return p.pages ? ((int64_t)1 << p.page_shift) : p.capacity;
 }
 
 // Load the block's q heads, RMS-normalise with qw and turn at table row pos[b] (when
@@ -116,12 +141,12 @@ __device__ void q_prologue(const DecodeParams &p, int b, int h0, int nh, float (
 // empty row, NaN for a row with invalid lens or pos).
 template <bool BF16, int D, int GB>
 __device__ void write_partial(const DecodeParams &p, int split, int b, int h0, int nh, const float (*wm)[GB],
-                              const float (*wl)[GB], const float (*wo)[GB][D]) {
+                              const float (*wl)[GB], const float (*wo)[GB][D], bool page_bad = false) {
     const int64_t stride = (int64_t)D + 2;
-    bool bad = false;
+    bool bad = page_bad;
     if (p.direct) {
         const int len = p.lens[b];
-        bad = len < 0 || len > p.max_len;
+        bad = bad || len < 0 || len > p.max_len;
         if (p.check_pos) {
             const int pr = p.pos[b];
             bad = bad || pr < 0 || pr >= p.table_rows;
@@ -157,7 +182,7 @@ __device__ void write_partial(const DecodeParams &p, int split, int b, int h0, i
             dst[e] = A;
             if (e == 0) {
                 dst[D] = M;
-                dst[D + 1] = L;
+                dst[D + 1] = page_bad ? __builtin_nanf("") : L;   // the merge turns a NaN sum into NaN rows
             }
         }
     }

@@ -94,6 +94,11 @@ struct DecodeLaunch {
     // [batch, hkv, capacity, 2]; q and out are then bf16.
     const float *kpar, *vpar;
     int kbits, vbits;
+    // Paged pool (pages != NULL): k and v hold num_pages pages of page_rows rows (a power
+    // of two >= 16), each laid out as a cache of batch 1 and capacity page_rows; key j of
+    // sequence b is row j % page_rows of page pages[b max_pages + j / page_rows].
+    const int32_t *pages;
+    int64_t page_rows, max_pages, num_pages;
 };
 hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream);
 hipError_t launch_decode_q(const DecodeLaunch &a, hipStream_t stream);

@@ -232,9 +232,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
     static_assert(kQBytes <= kTiles && kOBytes <= kTiles, "prologue and merge fit the tile region");
     constexpr int kQFrag = 2 * G::kKMfma * 64 * 16;
     __shared__ __attribute__((aligned(16))) unsigned char smem[kTiles + kQFrag];
+    __shared__ int s_page_bad;                 // some wave met a page id outside the pool
 
     const int tid = threadIdx.x, lane = tid % 64;
     const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+    if (tid == 0) s_page_bad = 0;              // seen by all after the prologue's barriers
     const BlockCoord bc = block_coord(p);
     const int b = bc.b, split = bc.split;
     const int h0 = bc.kvh * p.group + bc.grp * GB;
@@ -245,12 +247,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
     const int start = split * (int)p.per_split;
     const int end = min(len, start + (int)p.per_split);
 
-    // This (sequence, kv head)'s rows are contiguous: codes, then (lo, step) pairs.
-    const int64_t hrow = ((int64_t)b * p.hkv + bc.kvh) * p.capacity;
-    const uint8_t *kbase = static_cast<const uint8_t *>(p.k) + hrow * GK::kRB;
-    const uint8_t *vbase = static_cast<const uint8_t *>(p.v) + hrow * GV::kRB;
-    const float *kpbase = p.kpar + hrow * 2;
-    const float *vpbase = p.vpar + hrow * 2;
+    // Codes and (lo, step) pairs are head-major in each unit (a sequence's cache, or a
+    // pool page): row r of kv head kvh of unit u is coded row (u hkv + kvh) rows + r.
+    const int64_t urows = unit_rows(p);
+    bool page_bad = false;
+    auto coded_row = [&](int key0) -> int64_t {
+        const CacheSlot cs = key0 < end ? cache_slot(p, b, key0, page_bad) : CacheSlot{0, 0};
+        return ((int64_t)cs.unit * p.hkv + bc.kvh) * urows + cs.row;
+    };
     unsigned char *kbuf = smem + w * 2 * G::kBuf;
     unsigned char *vbuf = kbuf + G::kBuf;
 
@@ -264,13 +268,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
         u32x4 kp[2], vp[2];          // (lo, step) of keys 4 kk .. 4 kk + 3
     };
     // Chunk j: descriptors end at the last valid row (rows past it read as zeros).
+    // A chunk's 16 rows lie in one unit (pages hold a multiple of 16 rows).
     auto issue = [&](int j, Regs &r) {
         const int key0 = first + kChunk * kWaves * j;
-        const int rows = end - key0;
-        const __amdgpu_buffer_rsrc_t kr = seq_rsrc(kbase + (int64_t)key0 * GK::kRB, (int64_t)rows * GK::kRB);
-        const __amdgpu_buffer_rsrc_t vr = seq_rsrc(vbase + (int64_t)key0 * GV::kRB, (int64_t)rows * GV::kRB);
-        const __amdgpu_buffer_rsrc_t kpr = seq_rsrc(kpbase + (int64_t)key0 * 2, (int64_t)rows * 8);
-        const __amdgpu_buffer_rsrc_t vpr = seq_rsrc(vpbase + (int64_t)key0 * 2, (int64_t)rows * 8);
+        const int rows = min(kChunk, end - key0);
+        const int64_t cr = coded_row(key0);
+        const __amdgpu_buffer_rsrc_t kr = seq_rsrc(static_cast<const uint8_t *>(p.k) + cr * GK::kRB, (int64_t)rows * GK::kRB);
+        const __amdgpu_buffer_rsrc_t vr = seq_rsrc(static_cast<const uint8_t *>(p.v) + cr * GV::kRB, (int64_t)rows * GV::kRB);
+        const __amdgpu_buffer_rsrc_t kpr = seq_rsrc(p.kpar + cr * 2, (int64_t)rows * 8);
+        const __amdgpu_buffer_rsrc_t vpr = seq_rsrc(p.vpar + cr * 2, (int64_t)rows * 8);
 #pragma unroll
         for (int i = 0; i < GK::kNL; ++i) load_words<GK::kLB>(r.k[i], kr, (64 * i + lane) * GK::kLB);
 #pragma unroll
@@ -411,6 +417,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
     b_head += __shfl_xor(b_head, 32, 64);
 #pragma unroll
     for (int t = 0; t < G::kNT; ++t) acc[t] += b_head;
+    if (page_bad && lane == 0) s_page_bad = 1;
     __syncthreads();
     float (*wo)[GB][D] = reinterpret_cast<float (*)[GB][D]>(smem);
     float (*wm)[GB] = reinterpret_cast<float (*)[GB]>(smem + kWaves * GB * D * 4);
@@ -424,7 +431,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
         }
     }
     __syncthreads();
-    write_partial<true, D, GB>(p, split, b, h0, nh, wm, wl, wo);
+    write_partial<true, D, GB>(p, split, b, h0, nh, wm, wl, wo, s_page_bad != 0);
 }
 
 template <int D, int KB, int VB>

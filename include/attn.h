@@ -176,6 +176,24 @@ attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v
                                  attn_dtype_t dtype, void *stream);
 
 /*
+ * attn_prefill_chunk_paged -- attn_prefill_chunk with the cache in a paged KV pool
+ * (compute guide "Tensors, GPU kernels and AI models", Step 5): k_pool, v_pool
+ * [num_pages, page_rows, hkv, d] and the page table pages [batch, max_pages] (device
+ * int32) as in attn_decode_paged, with page_rows a power of two in [64, 2^20].  The
+ * chunk's keys (prepped when prep->kw is set) and values are written to rows n_past ..
+ * n_past + tq - 1 of each sequence's pages; its queries then attend rows 0 .. n_past +
+ * tq - 1 read through the table.  n_past + tq <= max_pages * page_rows.  A page id
+ * outside [0, num_pages) is not written and gives NaN output rows for its sequence.
+ * bf16 only (ATTN_ERR_UNSUPPORTED for f32).
+ */
+attn_status_t attn_prefill_chunk_paged(const void *q, const void *k_new, const void *v_new, void *k_pool,
+                                       void *v_pool, void *out, int64_t batch, int64_t tq, int64_t hq,
+                                       int64_t hkv, int64_t d, int64_t num_pages, int64_t page_rows,
+                                       const int32_t *pages, int64_t max_pages, int64_t n_past,
+                                       const attn_headprep_t *prep, int causal, double scale,
+                                       attn_dtype_t dtype, void *stream);
+
+/*
  * attn_decode -- one new query row per sequence against a KV cache whose keys are
  * already prepped (gizml:netops, Functions > attention with tq = 1 < tk: the row
  * attends the whole cache).

@@ -275,6 +275,26 @@ def test_decode_q_paged_rejects(lib):
     assert call(dtype=A.ATTN_F32) == A.ATTN_ERR_UNSUPPORTED
 
 
+def test_prefill_chunk_paged_rejects(lib):
+    def call(**kw):
+        a = dict(page_rows=64, pages=FAKE + (7 << 32), max_pages=64, n_past=3584, tq=512, dtype=A.ATTN_BF16,
+                 scale=0.088)
+        a.update(kw)
+        prep = _prep(rows=4097)
+        return lib.attn_prefill_chunk_paged(FAKE, FAKE + (1 << 32), FAKE + (2 << 32), FAKE + (3 << 32),
+                                            FAKE + (4 << 32), FAKE + (5 << 32), 4, a["tq"], 32, 8, 128, 256,
+                                            a["page_rows"], a["pages"], a["max_pages"], a["n_past"],
+                                            ctypes.byref(prep), 1, a["scale"], a["dtype"], None)
+    assert call(scale=0.0) == A.ATTN_ERR_ARG                  # every case fails on the host
+    assert call(dtype=A.ATTN_F32) == A.ATTN_ERR_UNSUPPORTED
+    assert call(page_rows=32, max_pages=128) == A.ATTN_ERR_ARG    # pages below 64 rows
+    assert call(page_rows=96) == A.ATTN_ERR_ARG                   # not a power of two
+    assert call(pages=None) == A.ATTN_ERR_ARG
+    assert call(max_pages=63) == A.ATTN_ERR_ARG                   # n_past + tq > max_pages * page_rows
+    assert call(n_past=-1) == A.ATTN_ERR_ARG
+    assert lib.attn_last_error()
+
+
 def test_decode_sizes(lib):
     # 256 (sequence, kv head) units already give every CU a block: one split, no workspace
     assert lib.attn_decode_default_splits(32, 32, 8, 4096) == 1

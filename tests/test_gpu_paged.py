@@ -210,3 +210,92 @@ def test_kv_quantize_into_pages_then_paged_decode():
     cont = host(tah.attn_decode_q(dev(inp["q"], "bf16"), kcont, vcont, _i32(lens), _i32(pos), 200, prep=prep,
                                   scale=w.scale))
     np.testing.assert_array_equal(got, cont)
+
+
+def _chunk_case(B, n_past, tq, hq, hkv, d, page_rows, num_pages, seed, shared=0):
+    """Contiguous caches (the first n_past rows: the oracle's prepped keys, in bf16) and the
+    same rows in a pool laid out by a random page table (the first `shared` pages of
+    every sequence shared with sequence 0, whose prefix rows the others then copy)."""
+    L = n_past + tq
+    w = synthetic.Workload("pc", "prefill", "bf16", B, hq, hkv, L, d, d // 2, 1e4, seed)
+    inp = synthetic.make_prefill(w)
+    cap = L + 5
+    kc = np.full((B, cap, hkv, d), np.nan)
+    vc = np.full((B, cap, hkv, d), np.nan)
+    pos = np.arange(n_past)[None].repeat(B, 0)
+    kc[:, :n_past] = synthetic.bf16_round(oracle.headprep(inp["k"][:, :n_past], inp["kw"], inp["cos"], inp["sin"],
+                                                          d // 2, pos, w.eps))
+    vc[:, :n_past] = inp["v"][:, :n_past]
+    if shared:
+        kc[1:, :shared * page_rows] = kc[0, :shared * page_rows]
+        vc[1:, :shared * page_rows] = vc[0, :shared * page_rows]
+    lens = [L] * B
+    pages = _page_table(lens, page_rows, num_pages, shared, seed=seed)
+    kpool = _fill_pool(kc, pages, [n_past] * B, page_rows, num_pages)
+    vpool = _fill_pool(vc, pages, [n_past] * B, page_rows, num_pages)
+    return w, inp, kc, vc, kpool, vpool, pages
+
+
+@pytest.mark.parametrize("page_rows,n_past,tq", [(64, 700, 300), (256, 300, 77), (64, 0, 200), (128, 1000, 1)])
+def test_prefill_chunk_paged_matches_contiguous(page_rows, n_past, tq):
+    """The same chunk against the same rows, in contiguous caches and in a pool: outputs and
+    appended rows equal bit for bit; rows outside the sequences' pages untouched; and the
+    output within the bf16 tolerance of the oracle."""
+    require_gpu()
+    B, hq, hkv, d = 2, 8, 2, 128
+    L = n_past + tq
+    num_pages = B * ((L + page_rows - 1) // page_rows) + 3
+    w, inp, kc, vc, kpool, vpool, pages = _chunk_case(B, n_past, tq, hq, hkv, d, page_rows, num_pages,
+                                                      seed=page_rows + n_past)
+    hp = tah.HeadPrep(dev(inp["qw"], "f32"), dev(inp["kw"], "f32"), dev(inp["cos"], "f32"), dev(inp["sin"], "f32"),
+                      w.eps)
+    sl = slice(n_past, None)
+    q, kn, vn = dev(inp["q"][:, sl], "bf16"), dev(inp["k"][:, sl], "bf16"), dev(inp["v"][:, sl], "bf16")
+    kcd, vcd = dev(kc, "bf16"), dev(vc, "bf16")
+    ref_out = host(tah.attn_prefill_chunk(q, kn, vn, kcd, vcd, n_past, prep=hp, causal=True, scale=w.scale))
+    kpd, vpd = dev(kpool, "bf16"), dev(vpool, "bf16")
+    got = host(tah.attn_prefill_chunk_paged(q, kn, vn, kpd, vpd, _i32(pages), n_past, prep=hp, causal=True,
+                                            scale=w.scale))
+    np.testing.assert_array_equal(got, ref_out)
+    kp_after, vp_after = host(kpd), host(vpd)
+    kc_after, vc_after = host(kcd), host(vcd)
+    lens = [L] * B
+    np.testing.assert_array_equal(oracle.gather_paged(kp_after, pages, lens), kc_after[:, :max(L, 1)])
+    np.testing.assert_array_equal(oracle.gather_paged(vp_after, pages, lens), vc_after[:, :max(L, 1)])
+    used = set(int(x) for x in pages.reshape(-1) if x >= 0)
+    for pg in range(num_pages):
+        if pg not in used:
+            assert np.isnan(kp_after[pg]).all() and np.isnan(vp_after[pg]).all(), "page %d written" % pg
+    ref, _, _ = oracle.prefill_chunk(inp["q"][:, sl], inp["k"][:, sl], inp["v"][:, sl], kc, vc, n_past, inp["qw"],
+                                     inp["kw"], inp["cos"], inp["sin"], d // 2, w.eps, w.scale, True)
+    assert_close(got, ref, "bf16", "paged chunk")
+
+
+def test_prefill_chunk_paged_shared_prefix_and_bad_page():
+    """Two sequences on one copy of a 128-row start, each appending into its own pages,
+    give what private copies give; a page id outside the pool among the pages a chunk
+    writes gives NaN rows for its sequence and writes nothing."""
+    require_gpu()
+    B, n_past, tq, hq, hkv, d, P = 2, 200, 100, 8, 2, 128, 64
+    num_pages = 12
+    w, inp, kc, vc, kpool, vpool, pages = _chunk_case(B, n_past, tq, hq, hkv, d, P, num_pages, seed=77, shared=2)
+    assert (pages[1, :2] == pages[0, :2]).all()
+    hp = tah.HeadPrep(dev(inp["qw"], "f32"), dev(inp["kw"], "f32"), dev(inp["cos"], "f32"), dev(inp["sin"], "f32"),
+                      w.eps)
+    sl = slice(n_past, None)
+    q, kn, vn = dev(inp["q"][:, sl], "bf16"), dev(inp["k"][:, sl], "bf16"), dev(inp["v"][:, sl], "bf16")
+    got = host(tah.attn_prefill_chunk_paged(q, kn, vn, dev(kpool, "bf16"), dev(vpool, "bf16"), _i32(pages), n_past,
+                                            prep=hp, causal=True, scale=w.scale))
+    ref = host(tah.attn_prefill_chunk(q, kn, vn, dev(kc, "bf16"), dev(vc, "bf16"), n_past, prep=hp, causal=True,
+                                      scale=w.scale))
+    np.testing.assert_array_equal(got, ref)
+    bad = pages.copy()
+    bad[1, 4] = num_pages + 5                      # rows 256 .. 299 of sequence 1: written by this chunk
+    kpd, vpd = dev(kpool, "bf16"), dev(vpool, "bf16")
+    got_bad = host(tah.attn_prefill_chunk_paged(q, kn, vn, kpd, vpd, _i32(bad), n_past, prep=hp, causal=True,
+                                                scale=w.scale))
+    assert np.isnan(got_bad[1]).all()
+    np.testing.assert_array_equal(got_bad[0], ref[0])
+    kp_after = host(kpd)
+    for pg in set(range(num_pages)) - set(int(x) for x in bad.reshape(-1) if 0 <= x < num_pages):
+        assert np.isnan(kp_after[pg]).all(), "page %d written" % pg

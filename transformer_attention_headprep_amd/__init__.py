@@ -17,6 +17,7 @@ from .attn import (  # noqa: F401
     attn_kv_quantize,
     attn_prefill,
     attn_prefill_chunk,
+    attn_prefill_chunk_paged,
     attn_prep,
     attn_row_norm_rope,
     attn_rows,

@@ -20,7 +20,7 @@ ATTN_F32, ATTN_BF16 = 0, 1
 ATTN_OK, ATTN_ERR_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = 0, -1, -2, -3, -4
 
 # The entry points include/attn.h declares (checked by the CPU test suite).
-EXPORTS = ("attn_prep", "attn_prefill", "attn_prefill_chunk", "attn_decode", "attn_decode_workspace_size",
+EXPORTS = ("attn_prep", "attn_prefill", "attn_prefill_chunk", "attn_prefill_chunk_paged", "attn_decode", "attn_decode_workspace_size",
            "attn_decode_default_splits", "attn_decode_paged", "attn_kv_quantize", "attn_decode_q",
            "attn_decode_q_paged", "attn_decode_q_default_splits", "attn_rows", "attn_rows8_layout", "attn_rows8_quantize",
            "attn_rows8_attend", "attn_rows8", "attn_row_norm_rope", "attn_key_bound", "attn_supported",
@@ -60,6 +60,9 @@ def load_library(path: str = LIB_PATH):
     lib.attn_prefill.restype = ctypes.c_int
     lib.attn_prefill_chunk.argtypes = [_vp] * 6 + [_i64] * 7 + [hp, ctypes.c_int, _dbl, ctypes.c_int, _vp]
     lib.attn_prefill_chunk.restype = ctypes.c_int
+    lib.attn_prefill_chunk_paged.argtypes = [_vp] * 6 + [_i64] * 7 + [_vp, _i64, _i64, hp, ctypes.c_int, _dbl,
+                                                                      ctypes.c_int, _vp]
+    lib.attn_prefill_chunk_paged.restype = ctypes.c_int
     lib.attn_decode.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 5 + [_vp, _vp, _i64, hp, _dbl, _i64,
                                                                     _vp, ctypes.c_size_t,
                                                                     ctypes.c_int, _vp]
@@ -251,6 +254,33 @@ def attn_prefill_chunk(q, k_new, v_new, k_cache, v_cache, n_past: int, out=None,
                                   B, tq, hq, hkv, D, cap, n_past,
                                   ctypes.byref(st) if st is not None else None, int(bool(causal)),
                                   float(scale), _dtype_code(q), _stream(stream)))
+    return out
+
+
+def attn_prefill_chunk_paged(q, k_new, v_new, k_pool, v_pool, pages, n_past: int, out=None,
+                             prep: HeadPrep | None = None, causal: bool = True, scale: float | None = None,
+                             stream=None) -> torch.Tensor:
+    """attn_prefill_chunk with the cache in a paged pool k_pool, v_pool [num_pages, page_rows,
+    Hkv, D]; pages [B, max_pages] int32 maps each sequence's rows to pages."""
+    lib = load_library()
+    B, tq, hq, D = q.shape
+    num_pages, page_rows, hkv = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_pool", k_pool), ("v_pool", v_pool)):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if t.dtype != q.dtype:
+            raise TypeError("all operands must share a dtype")
+    if pages.dtype != torch.int32 or pages.dim() != 2 or pages.shape[0] != B or not pages.is_contiguous():
+        raise TypeError("pages must be a contiguous int32 [B, max_pages] device tensor")
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = prep.struct() if prep is not None else None
+    _check(lib.attn_prefill_chunk_paged(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(out),
+                                        B, tq, hq, hkv, D, num_pages, page_rows, _ptr(pages), pages.shape[1], n_past,
+                                        ctypes.byref(st) if st is not None else None, int(bool(causal)),
+                                        float(scale), _dtype_code(q), _stream(stream)))
     return out
 
 

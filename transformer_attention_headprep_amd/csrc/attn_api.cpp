@@ -344,13 +344,14 @@ attn_status_t attn_prefill(const void *q, void *k, const void *v, void *out, int
     return hip_status(attn::launch_prefill(a, s), "attn_prefill");
 }
 
-attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
-                                 void *out, int64_t batch, int64_t tq, int64_t hq, int64_t hkv, int64_t d,
-                                 int64_t capacity, int64_t n_past, const attn_headprep_t *prep, int causal,
-                                 double scale, attn_dtype_t dtype, void *stream) {
+static attn_status_t chunk_impl(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                                void *out, int64_t batch, int64_t tq, int64_t hq, int64_t hkv, int64_t d,
+                                int64_t capacity, const Paging *pg, int64_t n_past, const attn_headprep_t *prep,
+                                int causal, double scale, attn_dtype_t dtype, void *stream) {
     g_last_error[0] = 0;
     attn_status_t st = check_dtype_d(dtype, d);
     if (st) return st;
+    if (pg && dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "paged pools hold bf16 rows");
     if (batch < 0 || tq < 0) return fail(ATTN_ERR_ARG, "negative batch or tq");
     if (hq <= 0 || hkv <= 0 || hq % hkv != 0)
         return fail(ATTN_ERR_ARG, "hq = %lld must be a positive multiple of hkv = %lld", (long long)hq, (long long)hkv);
@@ -360,10 +361,19 @@ attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v
     if ((st = check_rows("k_cache", k_cache, hkv, d, hkv * d))) return st;
     if ((st = check_rows("v_cache", v_cache, hkv, d, hkv * d))) return st;
     if ((st = check_rows("out", out, hq, d, hq * d))) return st;
-    if (capacity <= 0 || capacity >= ((int64_t)1 << 31)) return fail(ATTN_ERR_ARG, "capacity %lld outside [1, 2^31)", (long long)capacity);
-    if (n_past < 0 || n_past + tq > capacity)
-        return fail(ATTN_ERR_ARG, "n_past %lld + tq %lld outside [0, capacity %lld]", (long long)n_past, (long long)tq,
-                    (long long)capacity);
+    int64_t cache_rows;                        // rows the cache pointers span
+    if (pg) {
+        if (pg->page_rows < 64) return fail(ATTN_ERR_ARG, "page_rows %lld < 64", (long long)pg->page_rows);
+        if (n_past < 0) return fail(ATTN_ERR_ARG, "n_past < 0");
+        if ((st = check_paging(*pg, std::max<int64_t>(n_past + tq, 1), batch))) return st;
+        cache_rows = pg->num_pages * pg->page_rows;
+    } else {
+        if (capacity <= 0 || capacity >= ((int64_t)1 << 31)) return fail(ATTN_ERR_ARG, "capacity %lld outside [1, 2^31)", (long long)capacity);
+        if (n_past < 0 || n_past + tq > capacity)
+            return fail(ATTN_ERR_ARG, "n_past %lld + tq %lld outside [0, capacity %lld]", (long long)n_past, (long long)tq,
+                        (long long)capacity);
+        cache_rows = batch * capacity;
+    }
     if (!std::isfinite(scale) || !(scale > 0.0)) return fail(ATTN_ERR_ARG, "scale must be finite and > 0");
     const bool prep_k = prep && prep->kw;
     if (prep && (st = check_prep(prep, d, true, false, n_past, tq))) return st;
@@ -376,26 +386,38 @@ attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v
     const Span sq = span(q, batch * tq, hq * d, hq, d, es);
     const Span skn = span(k_new, batch * tq, hkv * d, hkv, d, es);
     const Span svn = span(v_new, batch * tq, hkv * d, hkv, d, es);
-    const Span skc = span(k_cache, batch * capacity, hkv * d, hkv, d, es);
-    const Span svc = span(v_cache, batch * capacity, hkv * d, hkv, d, es);
-    if (overlap(so, sq) || overlap(so, skn) || overlap(so, svn) || overlap(so, skc) || overlap(so, svc))
+    const Span skc = span(k_cache, cache_rows, hkv * d, hkv, d, es);
+    const Span svc = span(v_cache, cache_rows, hkv * d, hkv, d, es);
+    if (overlap(so, sq) || overlap(so, skn) || overlap(so, svn) || overlap(so, skc) || overlap(so, svc) ||
+        (pg && overlap(so, table_span(*pg, batch))))
         return fail(ATTN_ERR_ARG, "out overlaps another buffer");
+    if (pg && (overlap(skc, table_span(*pg, batch)) || overlap(svc, table_span(*pg, batch))))
+        return fail(ATTN_ERR_ARG, "the page table overlaps a pool");
     if (overlap(skc, svc) || overlap(skn, skc) || overlap(skn, svc) || overlap(svn, skc) || overlap(svn, svc))
         return fail(ATTN_ERR_ARG, "the caches overlap each other or the new rows");
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf16 = dtype == ATTN_BF16;
-    const int64_t crs = hkv * d, cbs = capacity * crs;    // cache row and sequence strides
+    const int64_t crs = hkv * d, cbs = pg ? 0 : capacity * crs;    // cache row and sequence strides
+    attn::PageMap pm{};
+    if (pg) {
+        pm.pages = pg->pages; pm.max_pages = (int)pg->max_pages; pm.num_pages = (int)pg->num_pages;
+        while (((int64_t)1 << pm.shift) < pg->page_rows) ++pm.shift;
+    }
 
-    // 1-2. Append: prepped keys and values into cache rows n_past .. n_past + tq - 1.
+    // 1-2. Append: prepped keys and values into cache rows n_past .. n_past + tq - 1 (of
+    // each sequence's pages, with a pool).
     attn::CopyRowsLaunch cv{};
-    cv.src = v_new; cv.dst = static_cast<uint8_t *>(v_cache) + (size_t)(n_past * crs) * es;
+    cv.src = v_new;
+    cv.dst = pg ? v_cache : static_cast<uint8_t *>(v_cache) + (size_t)(n_past * crs) * es;
     cv.src_bs = tq * crs; cv.src_rs = crs; cv.dst_bs = cbs; cv.dst_rs = crs;
     cv.batch = batch; cv.rows = tq; cv.row_elems = crs; cv.elem = (int64_t)es;
-    void *k_dst = static_cast<uint8_t *>(k_cache) + (size_t)(n_past * crs) * es;
+    cv.dst_pages = pm; cv.dst_row0 = n_past;
+    void *k_dst = pg ? k_cache : static_cast<uint8_t *>(k_cache) + (size_t)(n_past * crs) * es;
     if (prep_k) {
         attn::PrepLaunch pk{};
         pk.k_src = k_new; pk.k_dst = k_dst; pk.k_src_rs = crs; pk.k_dst_rs = crs; pk.hkv = hkv;
-        pk.k_src_bs = tq * crs; pk.k_dst_bs = cbs;
+        pk.k_src_bs = tq * crs; pk.k_dst_bs = cbs;              // (unused with a pool)
+        pk.k_pages = pm; pk.k_row0 = n_past;
         pk.batch = batch; pk.seq = tq; pk.d = d; pk.pos0 = n_past;
         pk.qw = prep->qw; pk.kw = prep->kw; pk.cos = prep->cos; pk.sin = prep->sin;
         pk.half = prep->half; pk.pairs = prep->pairs != 0; pk.eps = (float)prep->eps; pk.bf16 = bf16;
@@ -411,7 +433,8 @@ attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v
     attn::PrefillLaunch a{};
     a.q = q; a.k = k_cache; a.v = v_cache; a.out = out;
     a.q_rs = hq * d; a.k_rs = crs; a.v_rs = crs; a.o_rs = hq * d;
-    a.k_bs = cbs; a.v_bs = cbs;
+    a.k_bs = cbs; a.v_bs = cbs;                       // (unused with a pool)
+    a.kv_pages = pm;
     a.batch = batch; a.seq = tq; a.tk = n_past + tq; a.hq = hq; a.hkv = hkv; a.d = d; a.pos0 = n_past;
     a.causal = causal != 0; a.scale = (float)scale; a.bf16 = bf16;
     if (prep) {
@@ -430,7 +453,25 @@ attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v
             a.q = out;
         }
     }
-    return hip_status(attn::launch_prefill(a, s), "attn_prefill_chunk");
+    return hip_status(attn::launch_prefill(a, s), pg ? "attn_prefill_chunk_paged" : "attn_prefill_chunk");
+}
+
+attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                                 void *out, int64_t batch, int64_t tq, int64_t hq, int64_t hkv, int64_t d,
+                                 int64_t capacity, int64_t n_past, const attn_headprep_t *prep, int causal,
+                                 double scale, attn_dtype_t dtype, void *stream) {
+    return chunk_impl(q, k_new, v_new, k_cache, v_cache, out, batch, tq, hq, hkv, d, capacity, nullptr, n_past, prep,
+                      causal, scale, dtype, stream);
+}
+
+attn_status_t attn_prefill_chunk_paged(const void *q, const void *k_new, const void *v_new, void *k_pool,
+                                       void *v_pool, void *out, int64_t batch, int64_t tq, int64_t hq, int64_t hkv,
+                                       int64_t d, int64_t num_pages, int64_t page_rows, const int32_t *pages,
+                                       int64_t max_pages, int64_t n_past, const attn_headprep_t *prep, int causal,
+                                       double scale, attn_dtype_t dtype, void *stream) {
+    const Paging pg{pages, page_rows, max_pages, num_pages};
+    return chunk_impl(q, k_new, v_new, k_pool, v_pool, out, batch, tq, hq, hkv, d, 0, &pg, n_past, prep, causal, scale,
+                      dtype, stream);
 }
 
 attn_status_t attn_rows(void *qkv, int64_t n, int64_t heads, int64_t head, int64_t group, int64_t queries, void *out,

@@ -77,6 +77,22 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void *lds) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(lds));
 }
 
+// A paged KV pool seen by a kernel: row `key` of sequence b is pool row
+// (pages[b max_pages + key >> shift] << shift) + (key & (2^shift - 1)).  pages == NULL:
+// no pool.  A page id outside [0, num_pages) sets `bad` and maps to page 0.
+struct PageMap {
+    const int32_t *pages;
+    int shift, max_pages, num_pages;
+};
+__device__ __forceinline__ int64_t pool_row(const PageMap &m, int b, int64_t key, bool &bad) {
+    int id = m.pages[(int64_t)b * m.max_pages + (key >> m.shift)];
+    if ((unsigned)id >= (unsigned)m.num_pages) {
+        bad = true;
+        id = 0;
+    }
+    return ((int64_t)id << m.shift) + (key & (((int64_t)1 << m.shift) - 1));
+}
+
 // Wait until at most n vector-memory loads of this wave are outstanding (vmcnt only).
 #define ATTN_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 

@@ -5,6 +5,8 @@
 // enqueue.  Strides are in elements.
 #pragma once
 
+#include "common.h"
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -23,6 +25,11 @@ struct PrepLaunch {
     bool pairs;                  // turn adjacent pairs (2i, 2i + 1) rather than split halves
     float eps;
     bool bf16;
+    // k_pages != NULL: k_dst is a paged pool and key row t of sequence b goes to pool row
+    // pool_row(k_pages, b, k_row0 + t) (rows k_dst_rs apart); a row whose page id lies
+    // outside the pool is not written.
+    PageMap k_pages;
+    int64_t k_row0;
 };
 hipError_t launch_prep(const PrepLaunch &a, hipStream_t stream);
 
@@ -41,6 +48,8 @@ struct PrefillLaunch {
     const float *qw, *cos, *sin;
     const float *kwb;            // non-NULL: k was prepped with these weights (bounds |k|)
     float kmax;                  // > 0: caller's bound on every key row's norm
+    PageMap kv_pages;            // pages != NULL: k, v are paged pools (rows k_rs / v_rs apart);
+                                 // key j of sequence b is pool row pool_row(kv_pages, b, j)
     int64_t half;
     float eps;
     bool causal;
@@ -73,6 +82,8 @@ struct CopyRowsLaunch {
     const void *src; void *dst;
     int64_t src_bs, src_rs, dst_bs, dst_rs;
     int64_t batch, rows, row_elems, elem;
+    PageMap dst_pages;           // pages != NULL: row t of sequence b goes to pool row
+    int64_t dst_row0;            // pool_row(dst_pages, b, dst_row0 + t); bad ids: not written
 };
 hipError_t launch_copy_rows(const CopyRowsLaunch &a, hipStream_t stream);
 

@@ -44,6 +44,13 @@
 // m.  The row sum adds the bf16-rounded weights that the P V product uses
 // (v_dot2_f32_bf16), so numerator and denominator match.
 //
+// Fixed shift: with q's HeadPrep fused and a bound kb on the norm of every key row
+// (the caller's kmax, or sqrt(D) max|kw| when the call prepped k from kw), no score of
+// query row n exceeds |q_n| kb (Cauchy-Schwarz, on the bf16 values the matrix cores
+// take).  A wave whose rows all have |q_n| kb <= 48 starts every row at m = |q_n| kb and
+// keeps no running maximum: the same softmax (any shift no score exceeds gives it), with
+// every weight in [2^-96, 1], and no max, exchange or raise test per tile.
+//
 // The q prologue applies HeadPrep (RMS, qw, split-half turn at the row's position)
 // in registers before rounding q to bf16; it needs half to be 0 or a multiple of 16
 // (then every turned pair sits in one lane).  Other halves are prepped by the prep
@@ -71,6 +78,7 @@ constexpr float kRaiseAbove = 8.0f;   // base-2 headroom before the running max 
 constexpr float kFixedShiftMax = 48.0f;   // largest fixed softmax shift (base 2) a row may take
 
 extern __shared__ __attribute__((aligned(16))) unsigned char prefill_smem[];
+__shared__ int prefill_bad_page;      // a K/V page id outside the pool was met
 
 // The value held by lane ^ 32 (v_permlane32_swap: no LDS round trip).
 __device__ __forceinline__ float lane_pair(float x, int g) {
@@ -174,8 +182,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int wl = w & 1;
     const int nloads = loads_k ? (G::kKLoads - wl + 1) / 2 : (G::kVLoads - wl + 1) / 2;
     const int64_t rs = loads_k ? p.k_rs : p.v_rs;
+    const bool paged = p.kv_pages.pages != nullptr;
     const uint16_t *src = static_cast<const uint16_t *>(loads_k ? p.k : p.v) +
-                          (int64_t)b * (loads_k ? p.k_bs : p.v_bs) + (int64_t)kvh * D;
+                          (paged ? 0 : (int64_t)b * (loads_k ? p.k_bs : p.v_bs)) + (int64_t)kvh * D;
+    bool bad_page = false;
     int voff[G::kPerWave];
 #pragma unroll
     for (int t = 0; t < G::kPerWave; ++t) {
@@ -184,9 +194,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int col = sidx - row * (loads_k ? G::kKSlots : G::kVSlots);
         voff[t] = (int)(row * rs + 8 * min(col, G::kChunks - 1)) * 2;
     }
+    // A paged pool holds a 64-key tile in one page (pages are a power of two >= 64 rows).
     auto load_tile = [&](int kt, int bsel) {
         const int key0 = kt * kBN;
-        const __amdgpu_buffer_rsrc_t rsrc = seq_rsrc(src + (int64_t)key0 * rs, ((int64_t)(tk - 1 - key0) * rs + D) * 2);
+        __amdgpu_buffer_rsrc_t rsrc;
+        if (paged) {
+            const int64_t prow = pool_row(p.kv_pages, b, key0, bad_page);
+            rsrc = seq_rsrc(src + prow * rs, ((int64_t)(min(kBN, tk - key0) - 1) * rs + D) * 2);
+        } else {
+            rsrc = seq_rsrc(src + (int64_t)key0 * rs, ((int64_t)(tk - 1 - key0) * rs + D) * 2);
+        }
         unsigned char *dst = smem + bsel * G::kBufBytes + (loads_k ? 0 : G::kKBytes);
 #pragma unroll
         for (int t = 0; t < G::kPerWave; ++t) {
@@ -196,6 +213,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
 
     // First tile on its way before the q prologue.
+    if (threadIdx.x == 0) prefill_bad_page = 0;      // read only after the loop's barriers
     load_tile(0, 0);
 
     const float C = p.scale * kLog2e;       // q is scaled by this before it is rounded
@@ -343,6 +361,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int key0 = kt * kBN;
         const int bsel = kt & 1;
         if (kt + 1 < ntiles) load_tile(kt + 1, bsel ^ 1);
+        if (bad_page && lane == 0) prefill_bad_page = 1;   // seen by all after this tile's barrier
         const unsigned char *buf = smem + bsel * G::kBufBytes;
         if (wrows == 0 || (CAUSAL && key0 > wlast)) {
             __builtin_amdgcn_s_waitcnt(0);
@@ -439,6 +458,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (row_ok) {
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        // A bad page: quiet-NaN bf16 bits (set as integers: this file is built without NaN semantics).
+        const uint32_t nan_mask = prefill_bad_page ? 0xFFFFFFFFu : 0u;
         uint16_t *orow = static_cast<uint16_t *>(p.out) + (int64_t)b * p.o_bs + r * p.o_rs + (int64_t)h * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -447,6 +468,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 uint2 u;
                 u.x = pack_bf16x2(o[db][4 * i] * inv, o[db][4 * i + 1] * inv);
                 u.y = pack_bf16x2(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
+                u.x = (u.x & ~nan_mask) | (0x7FC07FC0u & nan_mask);
+                u.y = (u.y & ~nan_mask) | (0x7FC07FC0u & nan_mask);
                 *reinterpret_cast<uint2 *>(orow + 32 * db + 8 * i + 4 * g) = u;
             }
     }

@@ -29,6 +29,8 @@ struct PrepParams {
     const float *qw, *kw, *cos, *sin;
     int half;
     float eps;
+    PageMap k_pages;            // pages != NULL: k rows go to pool rows (see PrepLaunch)
+    int64_t k_row0;
 };
 
 // Turn the adjacent pairs (e, e + 1), e even, of 4 values starting at e0 (a multiple of
@@ -103,6 +105,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepParams p) 
         src = p.k_src; dst = p.k_dst; w = p.kw;
         src_off = bb * p.k_src_bs + t * p.k_src_rs + h * D;
         dst_off = bb * p.k_dst_bs + t * p.k_dst_rs + h * D;
+        if (p.k_pages.pages && valid) {
+            bool bad = false;
+            const int64_t prow = pool_row(p.k_pages, (int)bb, p.k_row0 + t, bad);
+            dst_off = bad ? -1 : prow * p.k_dst_rs + h * D;       // -1: a page outside the pool, not written
+        }
     }
     const int e_lo = 4 * li, e_hi = D / 2 + 4 * li;
 
@@ -170,7 +177,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepParams p) 
             }
         }
     }
-    if (valid) {
+    if (valid && dst_off >= 0) {
         store4<BF16>(dst, dst_off + e_lo, lo);
         store4<BF16>(dst, dst_off + e_hi, hi);
     }
@@ -193,15 +200,25 @@ hipError_t launch_prep_d(const PrepParams &p, int mode, hipStream_t stream) {
 }
 
 // Row copy (16 bytes per lane, grid-stride): row t of sequence b.
+// With a page map, row t of sequence b goes to pool row pool_row(pages, b, row0 + t)
+// (rows dst_rs bytes apart), and rows whose page id lies outside the pool are skipped.
 __global__ __launch_bounds__(256) void copy_rows_kernel(const uint8_t *src, uint8_t *dst, int64_t src_bs,
                                                         int64_t src_rs, int64_t dst_bs, int64_t dst_rs,
-                                                        int64_t rows, int64_t row_bytes, int64_t total16) {
+                                                        int64_t rows, int64_t row_bytes, int64_t total16,
+                                                        const PageMap pages, int64_t row0) {
     const int64_t per_row = row_bytes / 16;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total16; i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t rr = i / per_row, c = i % per_row;
         const int64_t bb = rr / rows, t = rr % rows;
         const uint4 v = *reinterpret_cast<const uint4 *>(src + bb * src_bs + t * src_rs + 16 * c);
-        *reinterpret_cast<uint4 *>(dst + bb * dst_bs + t * dst_rs + 16 * c) = v;
+        int64_t doff = bb * dst_bs + t * dst_rs;
+        if (pages.pages) {
+            bool bad = false;
+            const int64_t prow = pool_row(pages, (int)bb, row0 + t, bad);
+            if (bad) continue;
+            doff = prow * dst_rs;
+        }
+        *reinterpret_cast<uint4 *>(dst + doff + 16 * c) = v;
     }
 }
 
@@ -304,7 +321,8 @@ hipError_t launch_copy_rows(const CopyRowsLaunch &a, hipStream_t stream) {
     const int64_t blocks = std::min<int64_t>((total16 + 255) / 256, 4096);
     hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const uint8_t *>(a.src), static_cast<uint8_t *>(a.dst), a.src_bs * a.elem,
-                       a.src_rs * a.elem, a.dst_bs * a.elem, a.dst_rs * a.elem, a.rows, row_bytes, total16);
+                       a.src_rs * a.elem, a.dst_bs * a.elem, a.dst_rs * a.elem, a.rows, row_bytes, total16,
+                       a.dst_pages, a.dst_row0);
     return hipGetLastError();
 }
 
@@ -325,6 +343,8 @@ hipError_t launch_prep(const PrepLaunch &a, hipStream_t stream) {
     p.qw = a.qw; p.kw = a.kw; p.cos = a.cos; p.sin = a.sin;
     p.half = (int)a.half;
     p.eps = a.eps;
+    p.k_pages = a.k_pages;
+    p.k_row0 = a.k_row0;
     const int mode = a.half == 0 ? 0 : (a.pairs ? 3 : (2 * a.half == a.d ? 1 : 2));
     if (a.d == 64)
         return a.bf16 ? launch_prep_d<true, 64>(p, mode, stream) : launch_prep_d<false, 64>(p, mode, stream);

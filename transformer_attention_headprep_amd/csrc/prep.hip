@@ -73,129 +73,164 @@ __device__ __forceinline__ void store4(void *base, int64_t off, const float (&x)
     }
 }
 
-// MODE 0: no turn (half = 0); MODE 1: half = d/2, pairs in-lane; MODE 2: any half, via LDS;
-// MODE 3: adjacent pairs, any half, in-lane.
+// One head of the launch: where it is read and written, and its values in flight.
 template <bool BF16, int D, int MODE>
+struct PrepUnit {
+    bool valid;
+    const void *src;
+    void *dst;
+    int64_t src_off, dst_off, posrow;   // dst_off < 0: a page outside the pool, not written
+    const float *w;
+    float lo[4], hi[4];
+    float4 wl, wh, cq, sq;
+
+    __device__ __forceinline__ void locate(const PrepParams &p, int64_t unit) {
+        valid = unit < p.n_units;
+        int64_t row;
+        if (unit < p.n_q_units) {
+            const int64_t u = valid ? unit : 0;
+            row = u / p.hq;
+            const int64_t h = u % p.hq, bb = row / p.seq, t = row % p.seq;
+            src = p.q_src; dst = p.q_dst; w = p.qw;
+            src_off = bb * p.q_src_bs + t * p.q_src_rs + h * D;
+            dst_off = bb * p.q_dst_bs + t * p.q_dst_rs + h * D;
+        } else {
+            const int64_t u = valid ? unit - p.n_q_units : 0;
+            row = u / p.hkv;
+            const int64_t h = u % p.hkv, bb = row / p.seq, t = row % p.seq;
+            src = p.k_src; dst = p.k_dst; w = p.kw;
+            src_off = bb * p.k_src_bs + t * p.k_src_rs + h * D;
+            dst_off = bb * p.k_dst_bs + t * p.k_dst_rs + h * D;
+            if (p.k_pages.pages && valid) {
+                bool bad = false;
+                const int64_t prow = pool_row(p.k_pages, (int)bb, p.k_row0 + t, bad);
+                dst_off = bad ? -1 : prow * p.k_dst_rs + h * D;
+            }
+        }
+        posrow = p.pos0 + row % p.seq;
+    }
+
+    // The weights, (split halves, half = D/2) the lane's table entries and the values,
+    // all requested before anything waits: one memory round trip per head.
+    __device__ __forceinline__ void load(const PrepParams &p, int e_lo, int e_hi) {
+        wl = wh = cq = sq = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo[i] = hi[i] = 0.f;
+        if (valid) {
+            wl = *reinterpret_cast<const float4 *>(w + e_lo);
+            wh = *reinterpret_cast<const float4 *>(w + e_hi);
+            if constexpr (MODE == 1) {
+                cq = *reinterpret_cast<const float4 *>(p.cos + posrow * (D / 2) + e_lo);
+                sq = *reinterpret_cast<const float4 *>(p.sin + posrow * (D / 2) + e_lo);
+            }
+            load4<BF16>(src, src_off + e_lo, lo);
+            load4<BF16>(src, src_off + e_hi, hi);
+        }
+    }
+
+    // Norm, weight, turn, store.  `stage` (MODE 2): this head's D floats of LDS; every
+    // thread of the block must call this together then (it holds a block barrier).
+    template <int LPH>
+    __device__ __forceinline__ void finish(const PrepParams &p, int e_lo, int e_hi, float *stage) {
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss += lo[i] * lo[i] + hi[i] * hi[i];
+        ss = sum_lanes<LPH>(ss);
+        const float inv = 1.0f / __builtin_sqrtf(ss * (1.0f / D) + p.eps);
+        if (valid) {
+            lo[0] = lo[0] * inv * wl.x; lo[1] = lo[1] * inv * wl.y;
+            lo[2] = lo[2] * inv * wl.z; lo[3] = lo[3] * inv * wl.w;
+            hi[0] = hi[0] * inv * wh.x; hi[1] = hi[1] * inv * wh.y;
+            hi[2] = hi[2] * inv * wh.z; hi[3] = hi[3] * inv * wh.w;
+        }
+        if constexpr (MODE == 3) {
+            if (valid) {
+                const float *crow = p.cos + posrow * p.half, *srow = p.sin + posrow * p.half;
+                turn_pairs4(lo, e_lo, p.half, crow, srow);
+                turn_pairs4(hi, e_hi, p.half, crow, srow);
+            }
+        } else if constexpr (MODE == 1) {
+            if (valid) {
+                const float cc[4] = {cq.x, cq.y, cq.z, cq.w}, sc[4] = {sq.x, sq.y, sq.z, sq.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float a = lo[i], b = hi[i];
+                    lo[i] = a * cc[i] - b * sc[i];
+                    hi[i] = b * cc[i] + a * sc[i];
+                }
+            }
+        } else if constexpr (MODE == 2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                stage[e_lo + i] = lo[i];
+                stage[e_hi + i] = hi[i];
+            }
+            __syncthreads();
+            if (valid) {
+                const int half = p.half;
+                const float *crow = p.cos + posrow * half;
+                const float *srow = p.sin + posrow * half;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int e = i < 4 ? e_lo + i : e_hi + i - 4;
+                    float y = stage[e];
+                    if (e < half) {
+                        y = stage[e] * crow[e] - stage[e + half] * srow[e];
+                    } else if (e < 2 * half) {
+                        const int f = e - half;
+                        y = stage[e] * crow[f] + stage[f] * srow[f];
+                    }
+                    if (i < 4) lo[i] = y; else hi[i - 4] = y;
+                }
+            }
+        }
+        if (valid && dst_off >= 0) {
+            store4<BF16>(dst, dst_off + e_lo, lo);
+            store4<BF16>(dst, dst_off + e_hi, hi);
+        }
+    }
+};
+
+// MODE 0: no turn (half = 0); MODE 1: half = d/2, pairs in-lane; MODE 2: any half, via LDS;
+// MODE 3: adjacent pairs, any half, in-lane.  A group of D/8 lanes takes U consecutive
+// heads, whose loads are all in flight together (U = 1 for MODE 2, whose LDS stage holds
+// one head per lane group).
+template <bool BF16, int D, int MODE, int U>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepParams p) {
     constexpr int LPH = D / 8;                  // lanes per head
-    constexpr int HPB = kPrepThreads / LPH;     // heads per block
+    constexpr int HPB = kPrepThreads / LPH;     // lane groups per block
+    static_assert(MODE != 2 || U == 1, "the LDS stage holds one head per lane group");
     __shared__ float stage[MODE == 2 ? HPB * D : 1];
 
     const int li = threadIdx.x % LPH;
     const int hb = threadIdx.x / LPH;
-    const int64_t unit = (int64_t)blockIdx.x * HPB + hb;
-    const bool valid = unit < p.n_units;
-    const bool is_q = unit < p.n_q_units;
-
-    const void *src;
-    void *dst;
-    int64_t src_off, dst_off, row;
-    const float *w;
-    if (is_q) {
-        const int64_t u = valid ? unit : 0;
-        row = u / p.hq;
-        const int64_t h = u % p.hq, bb = row / p.seq, t = row % p.seq;
-        src = p.q_src; dst = p.q_dst; w = p.qw;
-        src_off = bb * p.q_src_bs + t * p.q_src_rs + h * D;
-        dst_off = bb * p.q_dst_bs + t * p.q_dst_rs + h * D;
-    } else {
-        const int64_t u = valid ? unit - p.n_q_units : 0;
-        row = u / p.hkv;
-        const int64_t h = u % p.hkv, bb = row / p.seq, t = row % p.seq;
-        src = p.k_src; dst = p.k_dst; w = p.kw;
-        src_off = bb * p.k_src_bs + t * p.k_src_rs + h * D;
-        dst_off = bb * p.k_dst_bs + t * p.k_dst_rs + h * D;
-        if (p.k_pages.pages && valid) {
-            bool bad = false;
-            const int64_t prow = pool_row(p.k_pages, (int)bb, p.k_row0 + t, bad);
-            dst_off = bad ? -1 : prow * p.k_dst_rs + h * D;       // -1: a page outside the pool, not written
-        }
-    }
     const int e_lo = 4 * li, e_hi = D / 2 + 4 * li;
-
-    float lo[4] = {0.f, 0.f, 0.f, 0.f}, hi[4] = {0.f, 0.f, 0.f, 0.f};
-    if (valid) {
-        load4<BF16>(src, src_off + e_lo, lo);
-        load4<BF16>(src, src_off + e_hi, hi);
-    }
-    float ss = 0.f;
+    PrepUnit<BF16, D, MODE> units[U];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ss += lo[i] * lo[i] + hi[i] * hi[i];
-    ss = sum_lanes<LPH>(ss);
-    const float inv = 1.0f / __builtin_sqrtf(ss * (1.0f / D) + p.eps);
-    if (valid) {
-        const float4 wl = *reinterpret_cast<const float4 *>(w + e_lo);
-        const float4 wh = *reinterpret_cast<const float4 *>(w + e_hi);
-        lo[0] = lo[0] * inv * wl.x; lo[1] = lo[1] * inv * wl.y;
-        lo[2] = lo[2] * inv * wl.z; lo[3] = lo[3] * inv * wl.w;
-        hi[0] = hi[0] * inv * wh.x; hi[1] = hi[1] * inv * wh.y;
-        hi[2] = hi[2] * inv * wh.z; hi[3] = hi[3] * inv * wh.w;
-    }
-    const int64_t posrow = p.pos0 + row % p.seq;
-
-    if constexpr (MODE == 3) {
-        if (valid) {
-            const float *crow = p.cos + posrow * p.half, *srow = p.sin + posrow * p.half;
-            turn_pairs4(lo, e_lo, p.half, crow, srow);
-            turn_pairs4(hi, e_hi, p.half, crow, srow);
-        }
-    } else if constexpr (MODE == 1) {
-        if (valid) {
-            const float4 c = *reinterpret_cast<const float4 *>(p.cos + posrow * (D / 2) + e_lo);
-            const float4 s = *reinterpret_cast<const float4 *>(p.sin + posrow * (D / 2) + e_lo);
-            const float cc[4] = {c.x, c.y, c.z, c.w}, sc[4] = {s.x, s.y, s.z, s.w};
+    for (int u = 0; u < U; ++u) units[u].locate(p, ((int64_t)blockIdx.x * HPB + hb) * U + u);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float a = lo[i], b = hi[i];
-                lo[i] = a * cc[i] - b * sc[i];
-                hi[i] = b * cc[i] + a * sc[i];
-            }
-        }
-    } else if constexpr (MODE == 2) {
-        float *st = stage + hb * D;
+    for (int u = 0; u < U; ++u) units[u].load(p, e_lo, e_hi);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            st[e_lo + i] = lo[i];
-            st[e_hi + i] = hi[i];
-        }
-        __syncthreads();
-        if (valid) {
-            const int half = p.half;
-            const float *crow = p.cos + posrow * half;
-            const float *srow = p.sin + posrow * half;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int e = i < 4 ? e_lo + i : e_hi + i - 4;
-                float y = st[e];
-                if (e < half) {
-                    y = st[e] * crow[e] - st[e + half] * srow[e];
-                } else if (e < 2 * half) {
-                    const int f = e - half;
-                    y = st[e] * crow[f] + st[f] * srow[f];
-                }
-                if (i < 4) lo[i] = y; else hi[i - 4] = y;
-            }
-        }
-    }
-    if (valid && dst_off >= 0) {
-        store4<BF16>(dst, dst_off + e_lo, lo);
-        store4<BF16>(dst, dst_off + e_hi, hi);
-    }
+    for (int u = 0; u < U; ++u) units[u].template finish<LPH>(p, e_lo, e_hi, stage + (MODE == 2 ? hb * D : 0));
 }
 
 template <bool BF16, int D>
 hipError_t launch_prep_d(const PrepParams &p, int mode, hipStream_t stream) {
     constexpr int HPB = kPrepThreads / (D / 8);
-    const int64_t blocks = (p.n_units + HPB - 1) / HPB;
-    if (blocks == 0) return hipSuccess;
+    // Heads per lane group for the modes without the LDS stage: 1 (4 heads per group, all
+    // in flight together, measured slower on the 16 MiB prefill keys).
+    constexpr int U = 1;
+    const int64_t blocks1 = (p.n_units + HPB - 1) / HPB;
+    const int64_t blocksU = (p.n_units + HPB * U - 1) / (HPB * U);
+    if (blocks1 == 0) return hipSuccess;
     if (mode == 0)
-        hipLaunchKernelGGL((prep_kernel<BF16, D, 0>), dim3(blocks), dim3(kPrepThreads), 0, stream, p);
+        hipLaunchKernelGGL((prep_kernel<BF16, D, 0, U>), dim3(blocksU), dim3(kPrepThreads), 0, stream, p);
     else if (mode == 1)
-        hipLaunchKernelGGL((prep_kernel<BF16, D, 1>), dim3(blocks), dim3(kPrepThreads), 0, stream, p);
+        hipLaunchKernelGGL((prep_kernel<BF16, D, 1, U>), dim3(blocksU), dim3(kPrepThreads), 0, stream, p);
     else if (mode == 2)
-        hipLaunchKernelGGL((prep_kernel<BF16, D, 2>), dim3(blocks), dim3(kPrepThreads), 0, stream, p);
+        hipLaunchKernelGGL((prep_kernel<BF16, D, 2, 1>), dim3(blocks1), dim3(kPrepThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((prep_kernel<BF16, D, 3>), dim3(blocks), dim3(kPrepThreads), 0, stream, p);
+        hipLaunchKernelGGL((prep_kernel<BF16, D, 3, U>), dim3(blocksU), dim3(kPrepThreads), 0, stream, p);
     return hipGetLastError();
 }
 

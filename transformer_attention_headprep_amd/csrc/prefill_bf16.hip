@@ -18,9 +18,15 @@
 //
 // Tiles move HBM -> LDS by buffer loads that write LDS directly (no registers, no LDS
 // store instructions), double-buffered: tile kt+1 is in flight while tile kt is used,
-// one barrier per tile.  The buffer descriptor of a tile ends with the sequence, so
-// keys past its end arrive as zeros.  K rows are stored 16 bytes wider than their data
-// and V rows 64 bytes wider (the extra slots are filled by the same loads): K row
+// one barrier per tile.  The two buffers are two LDS variables and the tile loop is
+// unrolled by two, so each read names its buffer at compile time: the compiler then
+// knows that a read of one buffer does not depend on the loads still writing the other,
+// and inserts no wait for them (with one buffer array indexed at run time, every
+// transposing V read waited for the next tile's loads).  K fragments are read from LDS
+// two 16-wide chunks ahead of the products that take them.  The buffer descriptor of a
+// tile ends with the sequence, so keys past its end arrive as zeros.  K rows are stored
+// 16 bytes wider than their data and V rows 64 bytes wider (the extra slots are filled by
+// the same loads): K row
 // pitches step 4 banks, so the 16-byte reads of 16 consecutive key rows cover all 64
 // banks once; V row pitches step 16 banks, so the transposing reads of 4 key rows x 64
 // bytes by 32 lanes do too.  Every LDS offset is then an immediate.  Two blocks fit a
@@ -77,7 +83,6 @@ constexpr int kXcds = 8;
 constexpr float kRaiseAbove = 8.0f;   // base-2 headroom before the running max moves
 constexpr float kFixedShiftMax = 48.0f;   // largest fixed softmax shift (base 2) a row may take
 
-extern __shared__ __attribute__((aligned(16))) unsigned char prefill_smem[];
 __shared__ int prefill_bad_page;      // a K/V page id outside the pool was met
 
 // The value held by lane ^ 32 (v_permlane32_swap: no LDS round trip).
@@ -141,7 +146,10 @@ template <int D, bool CAUSAL, bool PREP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(const PrefillLaunch p,
                                                                                                     const PrefillGrid gr) {
     typedef Geo<D> G;
-    unsigned char *smem = prefill_smem;                                  // 2 tile buffers
+    // The two tile buffers are separate variables so that the compiler sees that reads of
+    // one never wait for the loads in flight into the other.
+    __shared__ __attribute__((aligned(16))) unsigned char tb0[G::kBufBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char tb1[G::kBufBytes];
     constexpr int NC = D / 16;       // 16-wide d chunks of the q.k product
     constexpr int NDB = D / 32;      // 32-wide d blocks of the output
 
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         voff[t] = (int)(row * rs + 8 * min(col, G::kChunks - 1)) * 2;
     }
     // A paged pool holds a 64-key tile in one page (pages are a power of two >= 64 rows).
-    auto load_tile = [&](int kt, int bsel) {
+    auto load_tile = [&](int kt, unsigned char *tbuf) {
         const int key0 = kt * kBN;
         __amdgpu_buffer_rsrc_t rsrc;
         if (paged) {
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         } else {
             rsrc = seq_rsrc(src + (int64_t)key0 * rs, ((int64_t)(tk - 1 - key0) * rs + D) * 2);
         }
-        unsigned char *dst = smem + bsel * G::kBufBytes + (loads_k ? 0 : G::kKBytes);
+        unsigned char *dst = tbuf + (loads_k ? 0 : G::kKBytes);
 #pragma unroll
         for (int t = 0; t < G::kPerWave; ++t) {
             if (t < nloads)
@@ -214,7 +222,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     // First tile on its way before the q prologue.
     if (threadIdx.x == 0) prefill_bad_page = 0;      // read only after the loop's barriers
-    load_tile(0, 0);
+    load_tile(0, tb0);
 
     const float C = p.scale * kLog2e;       // q is scaled by this before it is rounded
 
@@ -357,28 +365,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // Key positions of this wave's first and last row: a tile whose first key lies past the
     // last row's is skipped by the wave (it still loads and waits with the block).
     const int64_t wfirst = row0w + qoff, wlast = row0w + 31 + qoff;
-    for (int kt = 0; kt < ntiles; ++kt) {
+    auto step = [&](int kt, const unsigned char *buf, unsigned char *next) __attribute__((always_inline)) {
         const int key0 = kt * kBN;
-        const int bsel = kt & 1;
-        if (kt + 1 < ntiles) load_tile(kt + 1, bsel ^ 1);
+        if (kt + 1 < ntiles) load_tile(kt + 1, next);
         if (bad_page && lane == 0) prefill_bad_page = 1;   // seen by all after this tile's barrier
-        const unsigned char *buf = smem + bsel * G::kBufBytes;
         if (wrows == 0 || (CAUSAL && key0 > wlast)) {
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            continue;
+            return;
         }
 
         // S^T = K Q^T - m for 2 blocks of 32 keys (two independent accumulation chains).
         f32x16 s[2];
+        bf16x8 ka[NC][2];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                ka[c][kb] = *reinterpret_cast<const bf16x8 *>(buf + k_lane + kb * 32 * G::kKStride + 32 * c);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(buf + k_lane + kb * 32 * G::kKStride + 32 * c);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], c == 0 ? bias : s[kb], 0, 0, 0);
-            }
+            for (int kb = 0; kb < 2; ++kb)
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c][kb], qf[c], c == 0 ? bias : s[kb], 0, 0, 0);
         }
+        // reads run two chunks ahead of the products
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * NC - 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         // Mask: register 4i+jj of block kb holds key key0 + 32 kb + 8 i + 4 g + jj.
         const bool need_mask = (key0 + kBN > tk) || (CAUSAL && key0 + kBN - 1 > wfirst);
         if (need_mask) {
@@ -452,6 +470,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         __builtin_amdgcn_s_waitcnt(0);        // this wave's loads of tile kt+1 are in LDS
         __syncthreads();
+    };
+    for (int kt = 0; kt < ntiles; kt += 2) {
+        step(kt, tb0, tb1);
+        if (kt + 1 < ntiles) step(kt + 1, tb1, tb0);
     }
 
     // ---- epilogue: divide by the row sum, round once to bf16, store.
@@ -502,7 +524,7 @@ hipError_t launch_bf16_d(const PrefillLaunch &a, hipStream_t stream) {
     while (((int64_t)1 << l) < a.hkv) ++l;                    // ceil(log2 hkv)
     gr.hkv_mul = (uint32_t)((((uint64_t)1 << (31 + l)) + (uint64_t)a.hkv - 1) / (uint64_t)a.hkv);
     gr.hkv_shift = 31 + l;
-    const size_t lds = 2 * Geo<D>::kBufBytes;
+    const size_t lds = 0;
     if (a.prep_q)
         hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, true>), grid, dim3(256), lds, stream, a, gr);
     else

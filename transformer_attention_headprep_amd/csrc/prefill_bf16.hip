@@ -22,14 +22,16 @@
 // unrolled by two, so each read names its buffer at compile time: the compiler then
 // knows that a read of one buffer does not depend on the loads still writing the other,
 // and inserts no wait for them (with one buffer array indexed at run time, every
-// transposing V read waited for the next tile's loads).  K fragments are read from LDS
-// two 16-wide chunks ahead of the products that take them.  The buffer descriptor of a
-// tile ends with the sequence, so keys past its end arrive as zeros.  K rows are stored
-// 16 bytes wider than their data and V rows 64 bytes wider (the extra slots are filled by
-// the same loads): K row
-// pitches step 4 banks, so the 16-byte reads of 16 consecutive key rows cover all 64
-// banks once; V row pitches step 16 banks, so the transposing reads of 4 key rows x 64
-// bytes by 32 lanes do too.  Every LDS offset is then an immediate.  Two blocks fit a
+// transposing V read waited for the next tile's loads).  A step issues the next tile's
+// loads after its K reads: issued at the top of the step, they made the first unrolled
+// copy's K reads wait for them (the compiler's wait insertion loses the two buffers
+// apart where the loop's state merges), which left that copy with no overlap at all.
+// K fragments are read from LDS two 16-wide chunks ahead of the products that take them.
+// The buffer descriptor of a tile ends with the sequence, so keys past its end arrive as
+// zeros.  K rows are stored 16 bytes wider than their data and V rows 64 bytes wider (the
+// extra slots are filled by the same loads): K row pitches step 4 banks, so the 16-byte
+// reads of 16 consecutive key rows cover all 64 banks once; V row pitches step 16 banks,
+// so the transposing reads of 4 key rows x 64 bytes by 32 lanes do too.  Every LDS offset is then an immediate.  Two blocks fit a
 // CU (2 waves per SIMD).
 //
 // The ds_read_b64_tr_b16 layout (gfx950): in each group of 16 lanes, lane i receives
@@ -367,9 +369,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t wfirst = row0w + qoff, wlast = row0w + 31 + qoff;
     auto step = [&](int kt, const unsigned char *buf, unsigned char *next) __attribute__((always_inline)) {
         const int key0 = kt * kBN;
-        if (kt + 1 < ntiles) load_tile(kt + 1, next);
-        if (bad_page && lane == 0) prefill_bad_page = 1;   // seen by all after this tile's barrier
         if (wrows == 0 || (CAUSAL && key0 > wlast)) {
+            if (kt + 1 < ntiles) load_tile(kt + 1, next);
+            if (bad_page && lane == 0) prefill_bad_page = 1;   // seen by all after this tile's barrier
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             return;
@@ -397,6 +399,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        if (kt + 1 < ntiles) load_tile(kt + 1, next);
+        if (bad_page && lane == 0) prefill_bad_page = 1;   // seen by all after this tile's barrier
         // Mask: register 4i+jj of block kb holds key key0 + 32 kb + 8 i + 4 g + jj.
         const bool need_mask = (key0 + kBN > tk) || (CAUSAL && key0 + kBN - 1 > wfirst);
         if (need_mask) {

@@ -26,6 +26,8 @@
 //   - the running max only moves when a score exceeds it by more than 2^8 (a
 //     wave-uniform branch); otherwise a chunk costs 4 exponentials per lane.
 //   - the loads of chunk j+1 are in flight while chunk j is computed.
+//   - each (sequence, kv head) starts at a hashed chunk of its range and wraps around, so
+//     the blocks' streams do not move through equally spaced sequences in lockstep.
 // f32 caches (decode_f32_kernel): S^T on v_mfma_f32_16x16x4f32, P V on the vector ALUs
 // (D/4 lanes share one value row) with the chunk's weights passed through LDS.
 #include "decode_common.h"
@@ -79,6 +81,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
     // This wave's chunks: keys start + 16 (w + 4 j) .. +15, j < nch.
     const int first = start + kChunk * w;
     const int nch = end > first ? (end - first + kChunk * kWaves - 1) / (kChunk * kWaves) : 0;
+    // Chunks are taken in a rotated order, starting at a chunk hashed from (sequence, kv
+    // head): with every block starting at its first key, the blocks' streams sit at equal
+    // offsets of equally spaced sequences and crowd the same memory channels.  The order
+    // does not change the softmax (up to rounding); chunks past the last (j >= nch) keep
+    // their place, past the end, so they fetch nothing.
+    const int rot = nch > 0 ? (int)((((uint32_t)(b * (int)p.hkv + bc.kvh) * 2654435761u) >> 16) % (uint32_t)nch) : 0;
+    auto chunk_of = [&](int j) { return j < nch ? (j + rot < nch ? j + rot : j + rot - nch) : j; };
 
     struct Regs {
         u32x4 k[G::kLoads];
@@ -88,7 +97,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
     // (rows past it, and every row of a chunk past the end, read as zero without a fetch).
     // A chunk's 16 rows lie in one unit (pages hold a multiple of 16 rows).
     auto issue = [&](int j, Regs &r) {
-        const int key0 = first + kChunk * kWaves * j;
+        const int key0 = first + kChunk * kWaves * chunk_of(j);
         const int64_t bytes = (int64_t)min(kChunk, end - key0) * rowb;
         const CacheSlot cs = key0 < end ? cache_slot(p, b, key0, page_bad) : CacheSlot{0, 0};
         const int64_t crow = (int64_t)cs.unit * urows + cs.row;
@@ -143,7 +152,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
     // A wave's LDS operations run in order, so chunk j+1's stores cannot overtake
     // chunk j's reads of the same buffers.
     auto compute = [&](int j, const Regs &r) {
-        const int key0 = first + kChunk * kWaves * j;
+        const int key0 = first + kChunk * kWaves * chunk_of(j);
 #pragma unroll
         for (int i = 0; i < G::kLoads; ++i) {
             const int row = G::kRpi * i + lrow;

@@ -84,6 +84,18 @@ def recorded_traffic(kernel: str):
     return rec["bytes_per_launch"]
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name as /proc/cpuinfo gives it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, inp) -> dict:
     """The f64 oracle, as it stands, on the full prefill workload (HeadPrep of q and k
     plus attention of every query row) on this host's cores."""
@@ -96,7 +108,7 @@ def cpu_baseline(w, inp) -> dict:
             "cores": oracle.threads(), "kind": "oracle",
             "sample": "the whole bf16 prefill workload (4 x 2048 tokens, 32/8 heads, d 128): "
                       "HeadPrep of q and k and causal attention of every row, f64, %.1f s" % dt,
-            "host_cpu": platform.processor() or platform.machine()}
+            "host_cpu": host_cpu_model(), "cores_in_affinity_mask": len(os.sched_getaffinity(0))}
 
 
 def decode_bytes_q(w, kbits: int, vbits: int) -> int:

@@ -207,6 +207,9 @@ attn_status_t attn_prefill_chunk_paged(const void *q, const void *k_new, const v
  *             prep is given and half > 0; may be NULL otherwise).
  *   max_len   host bound on every lens[b]; 1 <= max_len <= capacity.  It sets how
  *             the keys are split.
+ *   max_pos   host bound on every pos[b]: with a turning HeadPrep (half > 0),
+ *             0 <= max_pos < prep->table_rows is checked before anything is
+ *             enqueued (ATTN_ERR_ARG otherwise); without one it is ignored.
  *   splits    number of key splits per sequence, 0 = the library's choice
  *             (attn_decode_default_splits).  Results do not depend on it beyond
  *             rounding.
@@ -216,7 +219,7 @@ attn_status_t attn_prefill_chunk_paged(const void *q, const void *k_new, const v
  *             size is 0 when the call runs as a single split (the output is then
  *             written directly); workspace may be NULL in that case.
  *   Device-side values the host cannot check: lens[b] == 0 gives a zero output row;
- *   lens[b] < 0, lens[b] > max_len, or a pos[b] outside [0, table_rows) gives NaN in
+ *   lens[b] < 0, lens[b] > max_len, or a pos[b] outside [0, max_pos] gives NaN in
  *   that sequence's output rows (nothing outside the buffers is read).
  */
 size_t attn_decode_workspace_size(int64_t batch, int64_t hq, int64_t hkv, int64_t d,
@@ -224,7 +227,7 @@ size_t attn_decode_workspace_size(int64_t batch, int64_t hq, int64_t hkv, int64_
 int64_t attn_decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len);
 attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *out,
                           int64_t batch, int64_t hq, int64_t hkv, int64_t d, int64_t capacity,
-                          const int32_t *lens, const int32_t *pos, int64_t max_len,
+                          const int32_t *lens, const int32_t *pos, int64_t max_len, int64_t max_pos,
                           const attn_headprep_t *prep, double scale, int64_t splits,
                           void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
                           void *stream);
@@ -248,7 +251,7 @@ attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cach
 attn_status_t attn_decode_paged(const void *q, const void *k_pool, const void *v_pool, void *out,
                                 int64_t batch, int64_t hq, int64_t hkv, int64_t d, int64_t num_pages,
                                 int64_t page_rows, const int32_t *pages, int64_t max_pages,
-                                const int32_t *lens, const int32_t *pos, int64_t max_len,
+                                const int32_t *lens, const int32_t *pos, int64_t max_len, int64_t max_pos,
                                 const attn_headprep_t *prep, double scale, int64_t splits,
                                 void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
                                 void *stream);
@@ -295,7 +298,7 @@ attn_status_t attn_kv_quantize(const void *x, int64_t batch, int64_t seq, int64_
  *   k_codes, k_params, v_codes, v_params   the caches (format above) with hkv heads and
  *                `capacity` rows, coded in k_bits and v_bits: (8, 8), (4, 4), (4, 2) or
  *                (2, 2).
- *   lens, pos, max_len, prep, scale: as attn_decode.
+ *   lens, pos, max_len, max_pos, prep, scale: as attn_decode.
  *   splits       number of key splits per sequence; 0 = attn_decode_q_default_splits
  *                (more splits than the bf16 decode takes: a coded chunk carries fewer
  *                bytes, so more blocks keep the memory busy).
@@ -311,7 +314,7 @@ attn_status_t attn_decode_q(const void *q, const uint8_t *k_codes, const float *
                             const uint8_t *v_codes, const float *v_params, void *out, int64_t batch,
                             int64_t hq, int64_t hkv, int64_t d, int64_t capacity, int64_t k_bits,
                             int64_t v_bits, const int32_t *lens, const int32_t *pos, int64_t max_len,
-                            const attn_headprep_t *prep, double scale, int64_t splits, void *workspace,
+                            int64_t max_pos, const attn_headprep_t *prep, double scale, int64_t splits, void *workspace,
                             size_t workspace_bytes, attn_dtype_t dtype, void *stream);
 
 /*
@@ -326,8 +329,9 @@ attn_status_t attn_decode_q_paged(const void *q, const uint8_t *k_codes, const f
                                   int64_t batch, int64_t hq, int64_t hkv, int64_t d, int64_t num_pages,
                                   int64_t page_rows, int64_t k_bits, int64_t v_bits,
                                   const int32_t *pages, int64_t max_pages, const int32_t *lens,
-                                  const int32_t *pos, int64_t max_len, const attn_headprep_t *prep,
-                                  double scale, int64_t splits, void *workspace, size_t workspace_bytes,
+                                  const int32_t *pos, int64_t max_len, int64_t max_pos,
+                                  const attn_headprep_t *prep, double scale, int64_t splits,
+                                  void *workspace, size_t workspace_bytes,
                                   attn_dtype_t dtype, void *stream);
 
 /*

@@ -199,12 +199,12 @@ def _decode(lib, **kw):
     # splits=4: the call needs a workspace, so every case below fails on the host.
     a = dict(q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), out=FAKE + (3 << 32), batch=32, hq=32,
              hkv=8, d=128, cap=4096, lens=FAKE + (4 << 32), pos=FAKE + (5 << 32), max_len=4096,
-             prep=_prep(rows=4097), scale=0.088, splits=4, ws=FAKE + (6 << 32), ws_bytes=1 << 30,
+             max_pos=4096, prep=_prep(rows=4097), scale=0.088, splits=4, ws=FAKE + (6 << 32), ws_bytes=1 << 30,
              dtype=A.ATTN_BF16)
     a.update(kw)
     prep = ctypes.byref(a["prep"]) if a["prep"] is not None else None
     return lib.attn_decode(a["q"], a["k"], a["v"], a["out"], a["batch"], a["hq"], a["hkv"], a["d"],
-                           a["cap"], a["lens"], a["pos"], a["max_len"], prep, a["scale"], a["splits"],
+                           a["cap"], a["lens"], a["pos"], a["max_len"], a["max_pos"], prep, a["scale"], a["splits"],
                            a["ws"], a["ws_bytes"], a["dtype"], None)
 
 
@@ -221,22 +221,32 @@ def _decode(lib, **kw):
     (dict(d=80), A.ATTN_ERR_UNSUPPORTED),
     (dict(cap=0, max_len=0), A.ATTN_ERR_ARG),
     (dict(out=FAKE + 64), A.ATTN_ERR_ARG),               # out overlaps q
+    (dict(max_pos=4097), A.ATTN_ERR_ARG),                # the bound on pos lies past the table
+    (dict(max_pos=-1), A.ATTN_ERR_ARG),
 ])
 def test_decode_rejects(lib, kw, code):
     assert _decode(lib, **kw) == code
+
+
+def test_decode_max_pos_is_checked_only_with_a_turn(lib):
+    """Without a turning HeadPrep the positions are not read, so max_pos is not checked:
+    the call goes on to fail on its missing workspace instead."""
+    assert _decode(lib, ws=None, max_pos=99999, prep=_prep(half=0, cos=None, sin=None, rows=0)) == A.ATTN_ERR_WORKSPACE
+    assert _decode(lib, ws=None, max_pos=99999, prep=None) == A.ATTN_ERR_WORKSPACE
+    assert _decode(lib, ws=None, max_pos=99999) == A.ATTN_ERR_ARG
 
 
 def _decode_paged(lib, **kw):
     # splits=4 and a bad argument in every case: each call fails on the host.
     a = dict(q=FAKE, k=FAKE + (1 << 32), v=FAKE + (2 << 32), out=FAKE + (3 << 32), batch=32, hq=32,
              hkv=8, d=128, num_pages=2048, page_rows=64, pages=FAKE + (7 << 32), max_pages=64,
-             lens=FAKE + (4 << 32), pos=FAKE + (5 << 32), max_len=4096, prep=_prep(rows=4097), scale=0.088,
-             splits=4, ws=FAKE + (6 << 32), ws_bytes=1 << 30, dtype=A.ATTN_BF16)
+             lens=FAKE + (4 << 32), pos=FAKE + (5 << 32), max_len=4096, max_pos=4096, prep=_prep(rows=4097),
+             scale=0.088, splits=4, ws=FAKE + (6 << 32), ws_bytes=1 << 30, dtype=A.ATTN_BF16)
     a.update(kw)
     prep = ctypes.byref(a["prep"]) if a["prep"] is not None else None
     return lib.attn_decode_paged(a["q"], a["k"], a["v"], a["out"], a["batch"], a["hq"], a["hkv"], a["d"],
                                  a["num_pages"], a["page_rows"], a["pages"], a["max_pages"], a["lens"], a["pos"],
-                                 a["max_len"], prep, a["scale"], a["splits"], a["ws"], a["ws_bytes"], a["dtype"],
+                                 a["max_len"], a["max_pos"], prep, a["scale"], a["splits"], a["ws"], a["ws_bytes"], a["dtype"],
                                  None)
 
 
@@ -253,6 +263,7 @@ def _decode_paged(lib, **kw):
     (dict(ws_bytes=1000), A.ATTN_ERR_WORKSPACE),
     (dict(lens=None), A.ATTN_ERR_ARG),
     (dict(out=FAKE + (7 << 32)), A.ATTN_ERR_ARG),            # out overlaps the page table
+    (dict(max_pos=4097), A.ATTN_ERR_ARG),                    # past the table
 ])
 def test_decode_paged_rejects(lib, kw, code):
     assert _decode_paged(lib, **kw) == code
@@ -261,18 +272,19 @@ def test_decode_paged_rejects(lib, kw, code):
 
 def test_decode_q_paged_rejects(lib):
     def call(**kw):
-        a = dict(bits=(4, 4), page_rows=64, pages=FAKE + (7 << 32), dtype=A.ATTN_BF16, ws_bytes=1000)
+        a = dict(bits=(4, 4), page_rows=64, pages=FAKE + (7 << 32), dtype=A.ATTN_BF16, ws_bytes=1000, max_pos=4096)
         a.update(kw)
         prep = _prep(rows=4097)
         return lib.attn_decode_q_paged(FAKE, FAKE + (1 << 32), FAKE + (2 << 32), FAKE + (3 << 32), FAKE + (4 << 32),
                                        FAKE + (5 << 32), 32, 32, 8, 128, 2048, a["page_rows"], a["bits"][0],
                                        a["bits"][1], a["pages"], 64, FAKE + (6 << 32), FAKE + (8 << 32), 4096,
-                                       ctypes.byref(prep), 0.088, 4, FAKE + (9 << 32), a["ws_bytes"], a["dtype"], None)
+                                       a["max_pos"], ctypes.byref(prep), 0.088, 4, FAKE + (9 << 32), a["ws_bytes"], a["dtype"], None)
     assert call() == A.ATTN_ERR_WORKSPACE
     assert call(bits=(8, 4)) == A.ATTN_ERR_ARG
     assert call(page_rows=100) == A.ATTN_ERR_ARG
     assert call(pages=None) == A.ATTN_ERR_ARG
     assert call(dtype=A.ATTN_F32) == A.ATTN_ERR_UNSUPPORTED
+    assert call(max_pos=4097) == A.ATTN_ERR_ARG
 
 
 def test_prefill_chunk_paged_rejects(lib):
@@ -400,12 +412,13 @@ def test_kv_quantize_empty_is_a_no_op(lib):
 def _decq(lib, **kw):
     a = dict(q=FAKE, kc=FAKE + (1 << 32), kp=FAKE + (2 << 32), vc=FAKE + (3 << 32), vp=FAKE + (4 << 32),
              out=FAKE + (5 << 32), batch=4, hq=32, hkv=8, d=128, cap=4096, kb=8, vb=8, lens=FAKE + (6 << 32),
-             pos=FAKE + (7 << 32), max_len=4096, prep=_prep(), scale=0.088, splits=1, ws=None, wsb=0,
+             pos=FAKE + (7 << 32), max_len=4096, max_pos=4095, prep=_prep(), scale=0.088, splits=1, ws=None, wsb=0,
              dtype=A.ATTN_BF16)
     a.update(kw)
     prep = ctypes.byref(a["prep"]) if a["prep"] is not None else None
     return lib.attn_decode_q(a["q"], a["kc"], a["kp"], a["vc"], a["vp"], a["out"], a["batch"], a["hq"], a["hkv"],
-                             a["d"], a["cap"], a["kb"], a["vb"], a["lens"], a["pos"], a["max_len"], prep, a["scale"],
+                             a["d"], a["cap"], a["kb"], a["vb"], a["lens"], a["pos"], a["max_len"], a["max_pos"], prep,
+                             a["scale"],
                              a["splits"], a["ws"], a["wsb"], a["dtype"], None)
 
 
@@ -426,6 +439,7 @@ def _decq(lib, **kw):
     (dict(splits=4), A.ATTN_ERR_WORKSPACE),                 # a workspace is needed and missing
     (dict(out=FAKE + 256), A.ATTN_ERR_ARG),                 # out overlaps q
     (dict(prep=_prep(pairs=3)), A.ATTN_ERR_ARG),
+    (dict(max_pos=4096), A.ATTN_ERR_ARG),                   # the table has 4096 rows
 ])
 def test_decode_q_rejects(lib, kw, code):
     assert _decq(lib, **kw) == code

@@ -1,8 +1,10 @@
 """GPU parity: libattn's HIP path against the f64 oracle on the same seeded inputs.
 
-Every call goes through the C ABI (via the ctypes binding).  Small cases compare every
-output element; the full-size workloads compare seeded samples of query rows (all
-heads, first and last rows, tile boundaries) plus properties that hold at any size.
+Every call goes through the C ABI (via the ctypes binding).  Small cases and the bf16
+prefill and decode workloads compare every output element; the long prefill compares a
+seeded sample of query rows (every 128-row query tile and 64-key tile boundary for some
+heads of every kv group, the rows at and after each outlier key, first and last rows)
+plus properties that hold at any size.
 Tolerances: f32 max |d| <= 1e-4; bf16 |d| <= 2e-2 + 1e-2 |oracle| (tests/gpu_util.py).
 """
 import numpy as np
@@ -28,19 +30,33 @@ def _tables(rows, half, d, base=1e4):
     return synthetic.rope_tables(rows, half, d, base)
 
 
-def _sample_rows(batch, seq, hq, n_extra, seed):
+def _sample_rows(batch, seq, hq, hkv, n_extra, seed, outliers=()):
+    """Query rows (b, i, h) to compare: for two q heads of every kv group (the first and
+    the last of the group), both rows at every 128-row query-tile boundary and at every
+    64-key tile boundary; for one more head per group the rows at and right after each
+    outlier key (where such a key first becomes visible); rows 0, 1, seq - 2, seq - 1 of
+    every head; and n_extra seeded random rows."""
     rng = np.random.default_rng(seed)
-    rows = sorted({0, 1, 31, 32, 63, 64, 127, 128, 129, seq // 2, seq - 2, seq - 1} & set(range(seq)))
-    sel = []
-    for i, r in enumerate(rows):
-        for b in range(batch):
-            sel.append((b, r, (i + 3 * b) % hq))
-            sel.append((b, r, (i + 3 * b + hq // 2) % hq))
+    group = hq // hkv
+    sel = set()
+    edges = sorted({0, 1, seq - 2, seq - 1} | {e for t in range(64, seq, 64) for e in (t - 1, t)})
+    for kvh in range(hkv):
+        for h in sorted({kvh * group, kvh * group + group - 1}):
+            for i, r in enumerate(edges):
+                if 0 <= r < seq:
+                    sel.add((i % batch, r, h))
+        h_out = kvh * group + (group // 2)
+        for j, o in enumerate(outliers):
+            for r in (int(o), int(o) + 1):
+                if r < seq:
+                    sel.add(((j + kvh) % batch, r, h_out))
+    for h in range(hq):
+        for r in (0, 1, seq - 2, seq - 1):
+            if 0 <= r < seq:
+                sel.add((h % batch, r, h))
     for _ in range(n_extra):
-        sel.append((int(rng.integers(batch)), int(rng.integers(seq)), int(rng.integers(hq))))
-    for h in range(hq):                       # every head at least once
-        sel.append((h % batch, int(rng.integers(seq)), h))
-    return np.array(sel, dtype=np.int64)
+        sel.add((int(rng.integers(batch)), int(rng.integers(seq)), int(rng.integers(hq))))
+    return np.array(sorted(sel), dtype=np.int64)
 
 
 # --------------------------------------------------------------------------- attn_prep
@@ -165,35 +181,41 @@ def test_prefill_packed_qkv_layout():
     assert_close(host(out), ref, "bf16", "packed")
 
 
-def _check_sampled_prefill(name, n_extra):
+def _run_workload_prefill(name):
     w = synthetic.WORKLOADS[name]
     inp = synthetic.make_prefill(w)
     print("workload %s: q %s" % (name, inp["q"].shape), flush=True)
     q, k, v = dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16")
     out = tah.attn_prefill(q, k, v, prep=_prep_dev(inp), causal=True, scale=w.scale)
     torch.cuda.synchronize()
-    sel = _sample_rows(w.batch, w.seq, w.hq, n_extra, seed=w.seed)
-    ref, kh = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["qw"], inp["kw"], inp["cos"], inp["sin"],
-                             w.half, w.eps, 0, w.scale, True, sel=sel)
-    got = host(out)
-    assert np.isfinite(got).all()
-    err = assert_close(got[sel[:, 0], sel[:, 1], sel[:, 2]], ref, "bf16", name)
-    assert_close(host(k), kh, "bf16", name + " k prepped in place")
-    return err, inp, got
+    return w, inp, host(out), host(k)
 
 
-def test_prefill_bf16_workload_sampled():
+def test_prefill_bf16_workload_full():
+    """The bf16 prefill workload (4 x 2048 tokens, 32 q / 8 kv heads, d 128), every element
+    of the output and of the keys prepped in place."""
     require_gpu()
-    _check_sampled_prefill("prefill_bf16", 400)
+    w, inp, got, k_gpu = _run_workload_prefill("prefill_bf16")
+    assert np.isfinite(got).all()
+    ref, kh = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["qw"], inp["kw"], inp["cos"], inp["sin"],
+                             w.half, w.eps, 0, w.scale, True)
+    assert_close(got, ref, "bf16", "prefill_bf16 (every element)")
+    assert_close(k_gpu, kh, "bf16", "prefill_bf16 k prepped in place")
 
 
 def test_long_prefill_workload_sampled():
     """Long prefill with the literal inputs (1 % of raw k rows scaled x8, which HeadPrep's
-    RMS division makes inert), sampled rows; plus the invariant that the output equals
-    the run without the scaled rows."""
+    RMS division makes inert), on the sampled rows; every prepped key; plus the invariant
+    that the output equals the run without the scaled rows."""
     require_gpu()
-    _, inp, got = _check_sampled_prefill("long_prefill_bf16", 200)
-    w = synthetic.WORKLOADS["long_prefill_bf16"]
+    w, inp, got, k_gpu = _run_workload_prefill("long_prefill_bf16")
+    assert np.isfinite(got).all()
+    sel = _sample_rows(w.batch, w.seq, w.hq, w.hkv, 300, seed=w.seed, outliers=inp["outliers"])
+    assert len(sel) > 4000
+    ref, kh = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["qw"], inp["kw"], inp["cos"], inp["sin"],
+                             w.half, w.eps, 0, w.scale, True, sel=sel)
+    assert_close(got[sel[:, 0], sel[:, 1], sel[:, 2]], ref, "bf16", "long_prefill_bf16 (%d rows)" % len(sel))
+    assert_close(k_gpu, kh, "bf16", "long_prefill_bf16 k prepped in place")
     k_plain = inp["k"].copy()
     k_plain[:, inp["outliers"]] = synthetic.bf16_round(k_plain[:, inp["outliers"]] / 8.0)
     q, k, v = dev(inp["q"], "bf16"), dev(k_plain, "bf16"), dev(inp["v"], "bf16")
@@ -467,6 +489,26 @@ def test_decode_empty_and_invalid_rows():
     ok = _oracle_decode(w, {**inp, "q": inp["q"][1:2], "k_cache": inp["k_cache"][1:2], "v": inp["v"][1:2]},
                         lens[1:2], pos[1:2])
     assert_close(got[1:2], ok, "bf16", "valid row beside invalid ones")
+
+
+def test_decode_pos_past_max_pos():
+    """max_pos is the caller's bound on every pos[b]: a position inside the table but past
+    it gives NaN rows for that sequence only, the others are unaffected."""
+    require_gpu()
+    w = synthetic.WORKLOADS["decode_bf16"]
+    inp = _decode_inputs(w, batch=3, cache=200, seed=45)
+    lens = np.array([200, 200, 120], dtype=np.int32)
+    pos = np.array([150, 200, 100], dtype=np.int32)       # table rows 0..200; max_pos 180
+    q, kc, vc = dev(inp["q"], "bf16"), dev(inp["k_cache"], "bf16"), dev(inp["v"], "bf16")
+    for splits in (1, 3):
+        got = host(tah.attn_decode(q, kc, vc, torch.tensor(lens, dtype=torch.int32, device="cuda:0"),
+                                   torch.tensor(pos, dtype=torch.int32, device="cuda:0"), 200, prep=_prep_dev(inp),
+                                   scale=w.scale, splits=splits, max_pos=180))
+        assert np.isnan(got[1]).all()
+        keep = np.array([0, 2])
+        ref = oracle.decode(inp["q"][keep], inp["k_cache"][keep], inp["v"][keep], lens[keep], pos[keep], inp["qw"],
+                            inp["cos"], inp["sin"], w.half, w.eps, w.scale)
+        assert_close(got[keep], ref, "bf16", "splits=%d" % splits)
 
 
 def test_decode_matches_prefill_row():

@@ -63,7 +63,7 @@ def load_library(path: str = LIB_PATH):
     lib.attn_prefill_chunk_paged.argtypes = [_vp] * 6 + [_i64] * 7 + [_vp, _i64, _i64, hp, ctypes.c_int, _dbl,
                                                                       ctypes.c_int, _vp]
     lib.attn_prefill_chunk_paged.restype = ctypes.c_int
-    lib.attn_decode.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 5 + [_vp, _vp, _i64, hp, _dbl, _i64,
+    lib.attn_decode.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 5 + [_vp, _vp, _i64, _i64, hp, _dbl, _i64,
                                                                     _vp, ctypes.c_size_t,
                                                                     ctypes.c_int, _vp]
     lib.attn_decode.restype = ctypes.c_int
@@ -73,7 +73,7 @@ def load_library(path: str = LIB_PATH):
     lib.attn_decode_default_splits.restype = _i64
     lib.attn_kv_quantize.argtypes = [_vp] + [_i64] * 6 + [_vp, _vp, _i64, _i64, ctypes.c_int, _vp]
     lib.attn_kv_quantize.restype = ctypes.c_int
-    lib.attn_decode_q.argtypes = [_vp] * 6 + [_i64] * 7 + [_vp, _vp, _i64, hp, _dbl, _i64, _vp, ctypes.c_size_t,
+    lib.attn_decode_q.argtypes = [_vp] * 6 + [_i64] * 7 + [_vp, _vp, _i64, _i64, hp, _dbl, _i64, _vp, ctypes.c_size_t,
                                                          ctypes.c_int, _vp]
     lib.attn_decode_q.restype = ctypes.c_int
     lib.attn_decode_q_default_splits.argtypes = [_i64] * 5
@@ -90,10 +90,10 @@ def load_library(path: str = LIB_PATH):
     lib.attn_rows.restype = ctypes.c_int
     lib.attn_row_norm_rope.argtypes = [_vp] + [_i64] * 4 + [_vp, _vp, _vp, _dbl, ctypes.c_int, _vp]
     lib.attn_row_norm_rope.restype = ctypes.c_int
-    lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 6 + [_vp, _i64, _vp, _vp, _i64, hp, _dbl, _i64,
+    lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 6 + [_vp, _i64, _vp, _vp, _i64, _i64, hp, _dbl, _i64,
                                                                             _vp, ctypes.c_size_t, ctypes.c_int, _vp]
     lib.attn_decode_paged.restype = ctypes.c_int
-    lib.attn_decode_q_paged.argtypes = [_vp] * 6 + [_i64] * 8 + [_vp, _i64, _vp, _vp, _i64, hp, _dbl, _i64, _vp,
+    lib.attn_decode_q_paged.argtypes = [_vp] * 6 + [_i64] * 8 + [_vp, _i64, _vp, _vp, _i64, _i64, hp, _dbl, _i64, _vp,
                                                                   ctypes.c_size_t, ctypes.c_int, _vp]
     lib.attn_decode_q_paged.restype = ctypes.c_int
     lib.attn_key_bound.argtypes = [_vp, _i64]
@@ -162,6 +162,10 @@ class HeadPrep:
     @property
     def half(self) -> int:
         return 0 if self.cos is None else int(self.cos.shape[1])
+
+    @property
+    def table_rows(self) -> int:
+        return 0 if self.cos is None else int(self.cos.shape[0])
 
     def struct(self) -> attn_headprep_t:
         for name in ("qw", "kw", "cos", "sin"):
@@ -316,7 +320,8 @@ def attn_kv_quantize(x, cache: QuantCache, row0: int = 0, stream=None) -> None:
 
 
 def attn_decode_q(q, k: QuantCache, v: QuantCache, lens, pos, max_len: int, prep: HeadPrep | None = None,
-                  scale: float | None = None, splits: int = 0, workspace=None, out=None, stream=None) -> torch.Tensor:
+                  scale: float | None = None, splits: int = 0, workspace=None, out=None, stream=None,
+                  max_pos: int | None = None) -> torch.Tensor:
     """One bf16 query row per sequence (q [B, Hq, D]) against quantised caches."""
     lib = load_library()
     B, hq, D = q.shape
@@ -337,7 +342,7 @@ def attn_decode_q(q, k: QuantCache, v: QuantCache, lens, pos, max_len: int, prep
     st = prep.struct() if prep is not None else None
     _check(lib.attn_decode_q(_ptr(q), _ptr(k.codes), _ptr(k.params), _ptr(v.codes), _ptr(v.params), _ptr(out),
                              B, hq, hkv, D, cap, k.bits, v.bits, _ptr(lens), _ptr(pos), max_len,
-                             ctypes.byref(st) if st is not None else None, float(scale), splits, _ptr(workspace),
+                             _max_pos(prep, max_pos), ctypes.byref(st) if st is not None else None, float(scale), splits, _ptr(workspace),
                              0 if workspace is None else workspace.numel() * workspace.element_size(),
                              ATTN_BF16, _stream(stream)))
     return out
@@ -345,7 +350,7 @@ def attn_decode_q(q, k: QuantCache, v: QuantCache, lens, pos, max_len: int, prep
 
 def attn_decode_q_paged(q, k: QuantCache, v: QuantCache, pages, lens, pos, max_len: int,
                         prep: HeadPrep | None = None, scale: float | None = None, splits: int = 0, workspace=None,
-                        out=None, stream=None) -> torch.Tensor:
+                        out=None, stream=None, max_pos: int | None = None) -> torch.Tensor:
     """attn_decode_q over a paged pool: k and v are QuantCaches whose batch axis is the pool's
     pages (capacity = page_rows); pages [B, max_pages] int32 maps sequence rows to pages."""
     lib = load_library()
@@ -369,7 +374,8 @@ def attn_decode_q_paged(q, k: QuantCache, v: QuantCache, pages, lens, pos, max_l
     st = prep.struct() if prep is not None else None
     _check(lib.attn_decode_q_paged(_ptr(q), _ptr(k.codes), _ptr(k.params), _ptr(v.codes), _ptr(v.params), _ptr(out),
                                    B, hq, hkv, D, num_pages, page_rows, k.bits, v.bits, _ptr(pages), pages.shape[1],
-                                   _ptr(lens), _ptr(pos), max_len, ctypes.byref(st) if st is not None else None,
+                                   _ptr(lens), _ptr(pos), max_len, _max_pos(prep, max_pos),
+                                   ctypes.byref(st) if st is not None else None,
                                    float(scale), splits, _ptr(workspace),
                                    0 if workspace is None else workspace.numel() * workspace.element_size(),
                                    ATTN_BF16, _stream(stream)))
@@ -478,13 +484,20 @@ def decode_q_default_splits(batch: int, hq: int, hkv: int, max_len: int, k_bits:
     return int(load_library().attn_decode_q_default_splits(batch, hq, hkv, max_len, k_bits))
 
 
+def _max_pos(prep: "HeadPrep | None", max_pos: "int | None") -> int:
+    """The host bound on every pos[b]: the caller's, else the last row of the tables."""
+    if max_pos is not None:
+        return int(max_pos)
+    return prep.table_rows - 1 if prep is not None and prep.half else 0
+
+
 def decode_default_splits(batch: int, hq: int, hkv: int, max_len: int) -> int:
     return int(load_library().attn_decode_default_splits(batch, hq, hkv, max_len))
 
 
 def attn_decode(q, k_cache, v_cache, lens, pos, max_len: int, prep: HeadPrep | None = None,
                 scale: float | None = None, splits: int = 0, workspace=None, out=None,
-                stream=None) -> torch.Tensor:
+                stream=None, max_pos: int | None = None) -> torch.Tensor:
     """One query row per sequence (q [B, Hq, D]) against caches [B, capacity, Hkv, D]."""
     lib = load_library()
     B, hq, D = q.shape
@@ -503,7 +516,7 @@ def attn_decode(q, k_cache, v_cache, lens, pos, max_len: int, prep: HeadPrep | N
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = prep.struct() if prep is not None else None
     _check(lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), B, hq, hkv, D, cap,
-                           _ptr(lens), _ptr(pos), max_len,
+                           _ptr(lens), _ptr(pos), max_len, _max_pos(prep, max_pos),
                            ctypes.byref(st) if st is not None else None, float(scale), splits,
                            _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
                            _dtype_code(q), _stream(stream)))
@@ -512,7 +525,7 @@ def attn_decode(q, k_cache, v_cache, lens, pos, max_len: int, prep: HeadPrep | N
 
 def attn_decode_paged(q, k_pool, v_pool, pages, lens, pos, max_len: int, prep: HeadPrep | None = None,
                       scale: float | None = None, splits: int = 0, workspace=None, out=None,
-                      stream=None) -> torch.Tensor:
+                      stream=None, max_pos: int | None = None) -> torch.Tensor:
     """One bf16 query row per sequence (q [B, Hq, D]) against a paged pool k_pool, v_pool
     [num_pages, page_rows, Hkv, D]; pages [B, max_pages] int32 maps sequence rows to pages."""
     lib = load_library()
@@ -535,7 +548,7 @@ def attn_decode_paged(q, k_pool, v_pool, pages, lens, pos, max_len: int, prep: H
     st = prep.struct() if prep is not None else None
     _check(lib.attn_decode_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), B, hq, hkv, D, num_pages, page_rows,
                                  _ptr(pages), pages.shape[1], _ptr(lens), _ptr(pos), max_len,
-                                 ctypes.byref(st) if st is not None else None, float(scale), splits,
+                                 _max_pos(prep, max_pos), ctypes.byref(st) if st is not None else None, float(scale), splits,
                                  _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
                                  _dtype_code(q), _stream(stream)))
     return out

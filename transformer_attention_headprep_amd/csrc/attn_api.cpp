@@ -590,7 +590,7 @@ size_t attn_decode_workspace_size(int64_t batch, int64_t hq, int64_t hkv, int64_
 
 static attn_status_t decode_impl(const void *q, const void *k_cache, const void *v_cache, void *out, int64_t batch,
                                  int64_t hq, int64_t hkv, int64_t d, int64_t capacity, const Paging *pg,
-                                 const int32_t *lens, const int32_t *pos, int64_t max_len,
+                                 const int32_t *lens, const int32_t *pos, int64_t max_len, int64_t max_pos,
                                  const attn_headprep_t *prep, double scale, int64_t splits, void *workspace,
                                  size_t workspace_bytes, attn_dtype_t dtype, void *stream, const char *name) {
     g_last_error[0] = 0;
@@ -620,6 +620,9 @@ static attn_status_t decode_impl(const void *q, const void *k_cache, const void 
         if ((st = check_prep(prep, d, true, false, 0, 0))) return st;
         if (prep->half > 0 && !pos) return fail(ATTN_ERR_ARG, "pos is NULL with a turning HeadPrep");
         if (prep->table_rows >= ((int64_t)1 << 31)) return fail(ATTN_ERR_ARG, "table too large");
+        if (prep->half > 0 && (max_pos < 0 || max_pos >= prep->table_rows))
+            return fail(ATTN_ERR_ARG, "max_pos %lld outside the table's rows [0, %lld)", (long long)max_pos,
+                        (long long)prep->table_rows);
     }
     if (batch == 0) return ATTN_OK;
     if (splits == 0) splits = attn::decode_default_splits(batch, hq, hkv, max_len);
@@ -650,7 +653,10 @@ static attn_status_t decode_impl(const void *q, const void *k_cache, const void 
     a.prep_q = prep != nullptr;
     if (prep) {
         a.qw = prep->qw; a.cos = prep->cos; a.sin = prep->sin; a.half = prep->half;
-        a.table_rows = prep->table_rows; a.pairs = prep->pairs != 0; a.eps = (float)prep->eps;
+        // positions past max_pos are out of range for the kernel (NaN rows), like those
+        // past the table
+        a.table_rows = prep->half > 0 ? max_pos + 1 : prep->table_rows;
+        a.pairs = prep->pairs != 0; a.eps = (float)prep->eps;
     }
     a.scale = (float)scale; a.splits = splits; a.work = static_cast<float *>(workspace);
     a.bf16 = dtype == ATTN_BF16;
@@ -659,20 +665,21 @@ static attn_status_t decode_impl(const void *q, const void *k_cache, const void 
 
 attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *out, int64_t batch,
                           int64_t hq, int64_t hkv, int64_t d, int64_t capacity, const int32_t *lens,
-                          const int32_t *pos, int64_t max_len, const attn_headprep_t *prep, double scale,
-                          int64_t splits, void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
+                          const int32_t *pos, int64_t max_len, int64_t max_pos, const attn_headprep_t *prep,
+                          double scale, int64_t splits, void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
                           void *stream) {
-    return decode_impl(q, k_cache, v_cache, out, batch, hq, hkv, d, capacity, nullptr, lens, pos, max_len, prep,
+    return decode_impl(q, k_cache, v_cache, out, batch, hq, hkv, d, capacity, nullptr, lens, pos, max_len, max_pos, prep,
                        scale, splits, workspace, workspace_bytes, dtype, stream, "attn_decode");
 }
 
 attn_status_t attn_decode_paged(const void *q, const void *k_pool, const void *v_pool, void *out, int64_t batch,
                                 int64_t hq, int64_t hkv, int64_t d, int64_t num_pages, int64_t page_rows,
                                 const int32_t *pages, int64_t max_pages, const int32_t *lens, const int32_t *pos,
-                                int64_t max_len, const attn_headprep_t *prep, double scale, int64_t splits,
-                                void *workspace, size_t workspace_bytes, attn_dtype_t dtype, void *stream) {
+                                int64_t max_len, int64_t max_pos, const attn_headprep_t *prep, double scale,
+                                int64_t splits, void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
+                                void *stream) {
     const Paging pg{pages, page_rows, max_pages, num_pages};
-    return decode_impl(q, k_pool, v_pool, out, batch, hq, hkv, d, 0, &pg, lens, pos, max_len, prep, scale, splits,
+    return decode_impl(q, k_pool, v_pool, out, batch, hq, hkv, d, 0, &pg, lens, pos, max_len, max_pos, prep, scale, splits,
                        workspace, workspace_bytes, dtype, stream, "attn_decode_paged");
 }
 
@@ -709,7 +716,8 @@ static attn_status_t decode_q_impl(const void *q, const uint8_t *k_codes, const 
                                    const uint8_t *v_codes, const float *v_params, void *out, int64_t batch,
                                    int64_t hq, int64_t hkv, int64_t d, int64_t capacity, const Paging *pg,
                                    int64_t k_bits, int64_t v_bits, const int32_t *lens, const int32_t *pos,
-                                   int64_t max_len, const attn_headprep_t *prep, double scale, int64_t splits,
+                                   int64_t max_len, int64_t max_pos, const attn_headprep_t *prep, double scale,
+                                   int64_t splits,
                                    void *workspace, size_t workspace_bytes, attn_dtype_t dtype, void *stream,
                                    const char *name) {
     g_last_error[0] = 0;
@@ -744,6 +752,9 @@ static attn_status_t decode_q_impl(const void *q, const uint8_t *k_codes, const 
         if ((st = check_prep(prep, d, true, false, 0, 0))) return st;
         if (prep->half > 0 && !pos) return fail(ATTN_ERR_ARG, "pos is NULL with a turning HeadPrep");
         if (prep->table_rows >= ((int64_t)1 << 31)) return fail(ATTN_ERR_ARG, "table too large");
+        if (prep->half > 0 && (max_pos < 0 || max_pos >= prep->table_rows))
+            return fail(ATTN_ERR_ARG, "max_pos %lld outside the table's rows [0, %lld)", (long long)max_pos,
+                        (long long)prep->table_rows);
     }
     if (batch == 0) return ATTN_OK;
     if (splits == 0) splits = attn::decode_q_default_splits(batch, hq, hkv, max_len, k_bits);
@@ -779,7 +790,10 @@ static attn_status_t decode_q_impl(const void *q, const uint8_t *k_codes, const 
     a.prep_q = prep != nullptr;
     if (prep) {
         a.qw = prep->qw; a.cos = prep->cos; a.sin = prep->sin; a.half = prep->half;
-        a.table_rows = prep->table_rows; a.pairs = prep->pairs != 0; a.eps = (float)prep->eps;
+        // positions past max_pos are out of range for the kernel (NaN rows), like those
+        // past the table
+        a.table_rows = prep->half > 0 ? max_pos + 1 : prep->table_rows;
+        a.pairs = prep->pairs != 0; a.eps = (float)prep->eps;
     }
     a.scale = (float)scale; a.splits = splits; a.work = static_cast<float *>(workspace);
     a.bf16 = true;
@@ -790,11 +804,11 @@ static attn_status_t decode_q_impl(const void *q, const uint8_t *k_codes, const 
 attn_status_t attn_decode_q(const void *q, const uint8_t *k_codes, const float *k_params, const uint8_t *v_codes,
                             const float *v_params, void *out, int64_t batch, int64_t hq, int64_t hkv, int64_t d,
                             int64_t capacity, int64_t k_bits, int64_t v_bits, const int32_t *lens,
-                            const int32_t *pos, int64_t max_len, const attn_headprep_t *prep, double scale,
-                            int64_t splits, void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
+                            const int32_t *pos, int64_t max_len, int64_t max_pos, const attn_headprep_t *prep,
+                            double scale, int64_t splits, void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
                             void *stream) {
     return decode_q_impl(q, k_codes, k_params, v_codes, v_params, out, batch, hq, hkv, d, capacity, nullptr, k_bits,
-                         v_bits, lens, pos, max_len, prep, scale, splits, workspace, workspace_bytes, dtype, stream,
+                         v_bits, lens, pos, max_len, max_pos, prep, scale, splits, workspace, workspace_bytes, dtype, stream,
                          "attn_decode_q");
 }
 
@@ -802,12 +816,12 @@ attn_status_t attn_decode_q_paged(const void *q, const uint8_t *k_codes, const f
                                   const uint8_t *v_codes, const float *v_params, void *out, int64_t batch, int64_t hq,
                                   int64_t hkv, int64_t d, int64_t num_pages, int64_t page_rows, int64_t k_bits,
                                   int64_t v_bits, const int32_t *pages, int64_t max_pages, const int32_t *lens,
-                                  const int32_t *pos, int64_t max_len, const attn_headprep_t *prep, double scale,
-                                  int64_t splits, void *workspace, size_t workspace_bytes, attn_dtype_t dtype,
-                                  void *stream) {
+                                  const int32_t *pos, int64_t max_len, int64_t max_pos,
+                                  const attn_headprep_t *prep, double scale, int64_t splits, void *workspace,
+                                  size_t workspace_bytes, attn_dtype_t dtype, void *stream) {
     const Paging pg{pages, page_rows, max_pages, num_pages};
     return decode_q_impl(q, k_codes, k_params, v_codes, v_params, out, batch, hq, hkv, d, 0, &pg, k_bits, v_bits, lens,
-                         pos, max_len, prep, scale, splits, workspace, workspace_bytes, dtype, stream,
+                         pos, max_len, max_pos, prep, scale, splits, workspace, workspace_bytes, dtype, stream,
                          "attn_decode_q_paged");
 }
 

@@ -524,10 +524,10 @@ def main() -> int:
                      "bound": "mfma", "achieved": round(attn_tflops, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic("prefill_bf16_kernel"), "flops_per_launch": flops},
-        "decode_roofline": {"kernel": "decode_bf16_kernel (q HeadPrep fused, one split)",
+        "decode_roofline": {"kernel": "decode_rows_kernel + decode_merge_kernel (q HeadPrep fused, %d key splits)" % splits,
                             "bound": "hbm", "achieved": round(dec_gbps, 2), "peak": PEAK_HBM_GBPS,
                             "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
-                            "traffic": recorded_traffic("decode_bf16_kernel"), "bytes_per_launch": nbytes},
+                            "traffic": recorded_traffic("decode_rows_kernel"), "bytes_per_launch": nbytes},
     }
     if long_line is not None:
         line["long_prefill"] = long_line

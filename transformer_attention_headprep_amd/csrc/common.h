@@ -96,4 +96,45 @@ __device__ __forceinline__ int64_t pool_row(const PageMap &m, int b, int64_t key
 // Wait until at most n vector-memory loads of this wave are outstanding (vmcnt only).
 #define ATTN_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
 
+// Four transposing LDS reads (as lds_read_tr16) that complete before this returns.  Next
+// to loads that write LDS directly, the compiler waits for all of them before an LDS
+// read whenever it cannot tell that the read touches none of their bytes (always for
+// the transposing builtin, and for plain reads in a loop that rotates buffers); these
+// forms leave those waits to the caller.
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+__device__ __forceinline__ void lds_read_tr16_x4(i16x4 &a0, i16x4 &a1, i16x4 &a2, i16x4 &a3, uint32_t o0, uint32_t o1,
+                                                 uint32_t o2, uint32_t o3) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %5\n\t"
+        "ds_read_b64_tr_b16 %2, %6\n\t"
+        "ds_read_b64_tr_b16 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
+        : "v"(o0), "v"(o1), "v"(o2), "v"(o3)
+        : "memory");
+}
+
+// Two 16-byte LDS reads that complete before this returns (the same reason as above).
+__device__ __forceinline__ void lds_read_b128_x2(bf16x8 &a0, bf16x8 &a1, uint32_t o0, uint32_t o1) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a0), "=&v"(a1)
+        : "v"(o0), "v"(o1)
+        : "memory");
+}
+
+// Workgroup barrier that orders LDS accesses only: this wave's LDS reads and writes
+// complete, then the barrier.  __syncthreads() (and a release fence on LDS alone) also
+// waits for every load of this wave that writes LDS directly, loads issued for later
+// tiles included; such loads are waited for explicitly (ATTN_WAIT_VMCNT) before this.
+// The memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace attn

@@ -233,6 +233,320 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
 }
 
 // ---------------------------------------------------------------------------------
+// bf16 caches, whole cache rows per block (decode_rows_kernel).
+//
+// A block owns one (sequence, group of hb consecutive kv heads, key split), hb D = 512
+// (or every kv head when there are fewer): wave w takes kv head hb0 + w and its q heads.
+// Each chunk of 16 cache rows is the group's 1 KB piece of 16 rows of K (and of V) -- a
+// page holds a multiple of 16 rows -- and moves to LDS by buffer loads that write LDS
+// directly, 1 KB (one row piece) each, spread over the waves: memory sees contiguous
+// kilobytes requested together, which streams faster than blocks that read each kv head's
+// 2 D bytes of every row.  In LDS a chunk keeps the cache's layout [row][kv head][D]
+// except that the 16-byte pieces of each head's row sit at the swizzled slots kslot /
+// vslot (each lane of a load fetches the piece that belongs at its slot, so every load
+// still covers contiguous cache bytes); a wave then reads its head's K and V fragments
+// exactly as decode_bf16_kernel does, with the row pitch hb 2 D.  A ring of four chunk
+// buffers keeps three chunks in flight while one is computed, one barrier a chunk.
+// Every wave holds the whole online-softmax state of its heads, so it writes its partial
+// (or, with one split, its output rows) itself.
+// Order one wave's LDS writes before its later reads of what other lanes wrote.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D, int GB>
+__global__ __launch_bounds__(512) void decode_rows_kernel(const DecodeParams p, const int hb) {
+    typedef DecGeo<D> G;
+    // four chunk buffers of 2 kChunk hb 2 D <= 32 KB bytes (K then V): separate variables,
+    // so the compiler sees that reads of one never depend on loads into another
+    constexpr int kSlot = 2 * kChunk * 1024;
+    constexpr int kDepth = 3;                        // chunks in flight while one is computed
+    __shared__ __attribute__((aligned(16))) unsigned char cb0[kSlot];
+    __shared__ __attribute__((aligned(16))) unsigned char cb1[kSlot];
+    __shared__ __attribute__((aligned(16))) unsigned char cb2[kSlot];
+    __shared__ __attribute__((aligned(16))) unsigned char cb3[kSlot];
+    __shared__ float qst[8 * 512];                  // q staging: hb GB D <= 8 x 512 floats
+
+    const int lane = threadIdx.x % 64;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int nw = hb;                               // waves = kv heads of the block
+    const int RPb = nw * G::kRow;                    // LDS row pitch: the group's piece of a row
+    const int64_t RP = p.hkv * G::kRow;              // cache row pitch
+    const int split = (int)blockIdx.y, b = (int)blockIdx.z;
+    const int kvh = (int)blockIdx.x * nw + w;
+    const int h0 = kvh * p.group;
+    const int nh = p.group;                          // <= GB
+
+    int len = p.lens[b];
+    len = len < 0 ? 0 : (len > p.max_len ? (int)p.max_len : len);
+    const int start = split * (int)p.per_split;
+    const int end = min(len, start + (int)p.per_split);
+    const int nch = end > start ? (end - start + kChunk - 1) / kChunk : 0;   // block-uniform
+
+    // ---- the loads of a chunk: K is 16 RPb bytes = 16 RPb / 1024 loads of 1 KB, V the
+    // same; wave w issues loads w, w + nw, ... of each (D / 32 of each).  Lane L of load
+    // i fills LDS bytes 1024 i + 16 L: row r, head h, slot c_pos; it fetches piece c_pos ^
+    // swizzle(r) of that head's row from the cache.
+    constexpr int per_w = D / 32;
+    int64_t koff[per_w], voff[per_w];
+#pragma unroll
+    for (int x = 0; x < per_w; ++x) {
+        const int off = 1024 * (w + nw * x) + 16 * lane;
+        const int r = off / RPb, o = off - r * RPb;
+        const int h = o / G::kRow, cpos = (o - h * G::kRow) / 16;
+        koff[x] = r * RP + h * G::kRow + 16 * kslot<D>(r, cpos);
+        voff[x] = r * RP + h * G::kRow + 16 * vslot<D>(r, cpos);
+    }
+    const int64_t urows = unit_rows(p);
+    const int64_t hoff = (int64_t)blockIdx.x * nw * G::kRow;   // the group's first head in a row
+    bool page_bad = false;
+    // Chunk j into buf.  A chunk past the split (the first three are always issued) is an
+    // empty range: its loads read nothing and write zeros.
+    auto issue = [&](int j, unsigned char *buf) __attribute__((always_inline)) {
+        const int key0 = start + kChunk * j;
+        const bool some = key0 < end;
+        const CacheSlot cs = some ? cache_slot(p, b, key0, page_bad) : CacheSlot{0, 0};
+        const int64_t crow = (int64_t)cs.unit * urows + cs.row;
+        // rows past the end read as zeros: the range ends with the last valid row's piece
+        const int64_t bytes = some ? (int64_t)(min(kChunk, end - key0) - 1) * RP + RPb : 0;
+        const __amdgpu_buffer_rsrc_t kr = seq_rsrc(static_cast<const uint8_t *>(p.k) + crow * RP + hoff, bytes);
+        const __amdgpu_buffer_rsrc_t vr = seq_rsrc(static_cast<const uint8_t *>(p.v) + crow * RP + hoff, bytes);
+#pragma unroll
+        for (int x = 0; x < per_w; ++x) {
+            buffer_to_lds16(kr, buf + 1024 * (w + nw * x), (int)koff[x]);
+            buffer_to_lds16(vr, buf + kChunk * RPb + 1024 * (w + nw * x), (int)voff[x]);
+        }
+    };
+
+    // ---- q prologue (per wave, its q heads).  q, the weights and the turn's cos / sin
+    // are loaded into registers first, so that waiting for them later leaves the first
+    // three chunks in flight: lane (head qi, part li) holds elements li EPL .. +EPL-1.
+    constexpr int LPH = 64 / GB, EPL = D / LPH;
+    const int qi = lane / LPH, li = lane % LPH;
+    float xq[EPL], xw[EPL], xc[EPL], xs[EPL];
+    // Every load is unconditional and in one basic block with the first chunks' issue
+    // (absent inputs read a stand-in element of lens, clamped indices; the values are
+    // selected after), so that they are all in flight together.
+    const bool turn = p.prep_q && p.half > 0;
+    const int pr = p.half > 0 ? p.pos[b] : 0;
+    const int prow = pr < 0 ? 0 : (pr >= p.table_rows ? p.table_rows - 1 : pr);
+    {
+        const uint16_t *qrow = static_cast<const uint16_t *>(p.q) + ((int64_t)b * p.hq + h0 + min(qi, nh - 1)) * D + li * EPL;
+        const float *qwp = p.prep_q ? p.qw + li * EPL : reinterpret_cast<const float *>(p.lens);
+        const float *cp = turn ? p.cos + (int64_t)prow * p.half : reinterpret_cast<const float *>(p.lens);
+        const float *sp = turn ? p.sin + (int64_t)prow * p.half : reinterpret_cast<const float *>(p.lens);
+#pragma unroll
+        for (int e0 = 0; e0 < EPL; ++e0) {
+            const int e = li * EPL + e0;
+            const int f = !turn ? 0 : (p.pairs ? min(e >> 1, p.half - 1) : (e < p.half ? e : min(e - p.half, p.half - 1)));
+            xq[e0] = bf16_bits_to_f32(qrow[e0]);
+            xw[e0] = qwp[p.prep_q ? e0 : 0];
+            xc[e0] = cp[f];
+            xs[e0] = sp[f];
+        }
+    }
+    issue(0, cb0);
+    issue(1, cb1);
+    issue(2, cb2);
+#pragma unroll
+    for (int e0 = 0; e0 < EPL; ++e0) {
+        const int e = li * EPL + e0;
+        const bool turned = turn && (p.pairs ? (e >> 1) < p.half : e < 2 * p.half);
+        if (qi >= nh) xq[e0] = 0.f;
+        if (!p.prep_q) xw[e0] = 1.f;
+        if (!turned) {
+            xc[e0] = 1.f;
+            xs[e0] = 0.f;
+        }
+    }
+
+    // HeadPrep at table row pos[b] through this wave's rows of qst, then the B fragments
+    // of S^T in registers: lane (head n, kk) holds q[n][32c + 8kk .. +7] as a bf16 high
+    // part and a bf16 remainder (about 16 bits of q).
+    float (*qs)[D] = reinterpret_cast<float (*)[D]>(qst + w * GB * D);
+    const int n = lane % 16, kk = lane / 16;
+    u32x4 qhi[G::kKMfma], qlo[G::kKMfma];
+    {
+        if (p.prep_q) {
+            // head qi's sum of squares by its LPH lanes, then x qw / rms
+            float ss = 0.f;
+#pragma unroll
+            for (int e0 = 0; e0 < EPL; ++e0) ss += xq[e0] * xq[e0];
+            ss = sum_lanes<LPH>(ss);
+            const float inv = 1.0f / __builtin_sqrtf(ss * (1.0f / D) + p.eps);
+#pragma unroll
+            for (int e0 = 0; e0 < EPL; ++e0) xq[e0] = xq[e0] * inv * xw[e0];
+        }
+#pragma unroll
+        for (int e0 = 0; e0 < EPL; ++e0) qs[qi][li * EPL + e0] = xq[e0];
+        wave_lds_sync();
+        if (p.prep_q && p.half > 0) {
+            // the turn: each element with its partner (the neighbour in the pair, or the
+            // element half a table row away), read back from LDS
+#pragma unroll
+            for (int e0 = 0; e0 < EPL; ++e0) {
+                const int e = li * EPL + e0;
+                const float c = xc[e0], sn = xs[e0];
+                float y = xq[e0];
+                if (p.pairs) {
+                    if ((e >> 1) < p.half) y = (e & 1) ? xq[e0] * c + qs[qi][e - 1] * sn : xq[e0] * c - qs[qi][e + 1] * sn;
+                } else if (e < p.half) {
+                    y = xq[e0] * c - qs[qi][e + p.half] * sn;
+                } else if (e < 2 * p.half) {
+                    y = xq[e0] * c + qs[qi][e - p.half] * sn;
+                }
+                xc[e0] = y;
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int e0 = 0; e0 < EPL; ++e0) qs[qi][li * EPL + e0] = xc[e0];
+            wave_lds_sync();
+        }
+#pragma unroll
+        for (int c = 0; c < G::kKMfma; ++c) {
+            qhi[c] = u32x4{0u, 0u, 0u, 0u};
+            qlo[c] = u32x4{0u, 0u, 0u, 0u};
+            if (n < nh) {
+                const float *src = &qs[n][32 * c + 8 * kk];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float a = src[2 * e], b2 = src[2 * e + 1];
+                    qhi[c][e] = pack_bf16x2(a, b2);
+                    float ha, hb;
+                    unpack_bf16x2(qhi[c][e], ha, hb);
+                    qlo[c][e] = pack_bf16x2(a - ha, b2 - hb);
+                }
+            }
+        }
+    }
+
+    f32x4 acc[G::kNT];
+#pragma unroll
+    for (int t = 0; t < G::kNT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, thr = -INFINITY, l_lane = 0.f;
+    const int vkey = 4 * kk + (lane % 16) / 4, qq = lane % 4;
+
+    auto compute = [&](int j, const unsigned char *buf) __attribute__((always_inline)) {
+        const int key0 = start + kChunk * j;
+        const unsigned char *kb = buf + w * G::kRow;
+        const unsigned char *vb = buf + kChunk * RPb + w * G::kRow;
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < G::kKMfma; c += 2) {
+            bf16x8 kc[2];
+            lds_read_b128_x2(kc[0], kc[1], lds_offset(kb + n * RPb + 16 * kslot<D>(n, 4 * c + kk)),
+                             lds_offset(kb + n * RPb + 16 * kslot<D>(n, 4 * c + 4 + kk)));
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[u], __builtin_bit_cast(bf16x8, qhi[c + u]), s, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[u], __builtin_bit_cast(bf16x8, qlo[c + u]), s, 0, 0, 0);
+            }
+        }
+        if (key0 + kChunk > end) {            // ragged last chunk (wave-uniform)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (key0 + 4 * kk + i >= end) s[i] = -INFINITY;
+        }
+        const float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {
+            float mh = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mh = fmaxf(mh, __shfl_xor(mh, 32, 64));
+            const float m_new = fmaxf(m_run, mh * p.C);
+            const float alpha = fast_exp2(m_run - m_new);
+            l_lane *= alpha;
+#pragma unroll
+            for (int t = 0; t < G::kNT; ++t) acc[t] *= alpha;
+            m_run = m_new;
+            thr = (m_run + kRaiseAbove) / p.C;
+        }
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(s[i], p.C, -m_run));
+        l_lane += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
+        const i16x4 pf = __builtin_bit_cast(i16x4, make_uint2(p01, p23));
+        const unsigned char *vrow = vb + vkey * RPb + 8 * (qq % 2);
+#pragma unroll
+        for (int t0 = 0; t0 < G::kNT; t0 += 4) {
+            i16x4 a[4];
+            lds_read_tr16_x4(a[0], a[1], a[2], a[3], lds_offset(vrow + 16 * vslot<D>(vkey, 2 * t0 + qq / 2)),
+                             lds_offset(vrow + 16 * vslot<D>(vkey, 2 * t0 + 2 + qq / 2)),
+                             lds_offset(vrow + 16 * vslot<D>(vkey, 2 * t0 + 4 + qq / 2)),
+                             lds_offset(vrow + 16 * vslot<D>(vkey, 2 * t0 + 6 + qq / 2)));
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                acc[t0 + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[u], pf, acc[t0 + u], 0, 0, 0);
+        }
+    };
+    // Chunk j: wait until this wave's loads of it are in (the two younger chunks may
+    // still fly), a barrier publishes every wave's loads and ends every wave's reads of
+    // chunk j-1, chunk j+3 goes into chunk j-1's buffer, chunk j is computed.  Unrolled by
+    // four so each buffer is named at compile time.
+    auto step = [&](int j, const unsigned char *cur, unsigned char *nextd) __attribute__((always_inline)) {
+        const int younger = min(kDepth - 1, max(nch, kDepth) - 1 - j);   // chunks issued after chunk j
+        if (younger >= 2) {
+            ATTN_WAIT_VMCNT(4 * per_w);
+        } else if (younger == 1) {
+            ATTN_WAIT_VMCNT(2 * per_w);
+        } else {
+            ATTN_WAIT_VMCNT(0);
+        }
+        lds_barrier();
+        if (j + kDepth < nch) issue(j + kDepth, nextd);
+        compute(j, cur);
+    };
+    for (int j = 0; j < nch; j += 4) {
+        step(j, cb0, cb3);
+        if (j + 1 >= nch) break;
+        step(j + 1, cb1, cb0);
+        if (j + 2 >= nch) break;
+        step(j + 2, cb2, cb1);
+        if (j + 3 >= nch) break;
+        step(j + 3, cb3, cb2);
+    }
+    ATTN_WAIT_VMCNT(0);       // empty chunks past a short split write LDS too
+
+    // ---- this wave's heads: l over the head's 4 lanes, then the partial or the output.
+    float l_head = l_lane + __shfl_xor(l_lane, 16, 64);
+    l_head += __shfl_xor(l_head, 32, 64);
+    if (n < nh) {
+        const int64_t row = (int64_t)b * p.hq + h0 + n;
+        const int64_t stride = (int64_t)D + 2;
+        if (p.direct) {
+            bool bad = page_bad;
+            const int lr = p.lens[b];
+            bad = bad || lr < 0 || lr > p.max_len;
+            if (p.check_pos) {
+                const int pp = p.pos[b];
+                bad = bad || pp < 0 || pp >= p.table_rows;
+            }
+            const float inv = l_head > 0.f ? 1.0f / l_head : 0.f;
+            const uint32_t nan_mask = bad ? 0xFFFFFFFFu : 0u;
+            uint16_t *orow = static_cast<uint16_t *>(p.out) + row * D;
+#pragma unroll
+            for (int t = 0; t < G::kNT; ++t) {
+                uint2 u;
+                u.x = pack_bf16x2(acc[t][0] * inv, acc[t][1] * inv);
+                u.y = pack_bf16x2(acc[t][2] * inv, acc[t][3] * inv);
+                u.x = (u.x & ~nan_mask) | (0x7FC07FC0u & nan_mask);
+                u.y = (u.y & ~nan_mask) | (0x7FC07FC0u & nan_mask);
+                *reinterpret_cast<uint2 *>(orow + 16 * t + 4 * kk) = u;
+            }
+        } else {
+            float *dst = p.work + ((int64_t)split * p.batch * p.hq + row) * stride;
+#pragma unroll
+            for (int t = 0; t < G::kNT; ++t) *reinterpret_cast<f32x4 *>(dst + 16 * t + 4 * kk) = acc[t];
+            if (kk == 0) {
+                dst[D] = m_run;
+                dst[D + 1] = page_bad ? __builtin_nanf("") : l_head;   // the merge turns a NaN sum into NaN rows
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------
 // f32 caches.
 
 template <int D, int GB>
@@ -381,42 +695,112 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(const DecodeParams
     write_partial<false, D, GB>(p, split, b, h0, nh, wm, wl, wo);
 }
 
-// Merge the splits of one (sequence, q head) and write the output row.
+// Output elements lane + 64 e of row bh: A / L, NaN for a bad row or a NaN sum.
 template <bool BF16, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const float *work, void *out, const int32_t *lens,
-                                                         const int32_t *pos, int64_t batch, int64_t hq,
-                                                         int64_t splits, int64_t max_len, int64_t table_rows,
-                                                         bool check_pos) {
+__device__ __forceinline__ void merge_store(void *out, int64_t bh, int lane, const float (&A)[D / 64], float L, bool bad) {
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) {
+        float y = L > 0.f ? A[e] / L : 0.f;
+        if (bad || L != L) y = __builtin_nanf("");
+        if constexpr (BF16) {
+            f32x2 v2 = {y, 0.f};
+            bf16x2 hv = __builtin_convertvector(v2, bf16x2);
+            static_cast<uint16_t *>(out)[bh * D + lane + 64 * e] = (uint16_t)(__builtin_bit_cast(uint32_t, hv) & 0xFFFFu);
+        } else {
+            static_cast<float *>(out)[bh * D + lane + 64 * e] = y;
+        }
+    }
+}
+
+// Merge the splits of one (sequence, q head) and write the output row: one wave a row.
+// Lane s holds split s's maximum and sum (splits beyond 64 are read again in later
+// passes); the split weights 2^(m_s - M) are computed once, by their lane, and read by
+// every lane for its D / 64 output elements.
+template <bool BF16, int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(const float *work, void *out, const int32_t *lens,
+                                                          const int32_t *pos, int64_t batch, int64_t hq,
+                                                          int64_t splits, int64_t max_len, int64_t table_rows,
+                                                          bool check_pos) {
+    constexpr int EPL = D / 64;
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / hq;
-    const int e = threadIdx.x;
+    const int lane = threadIdx.x;
     const int64_t stride = (int64_t)D + 2;
+    const int64_t sstride = batch * hq * stride;     // from one split's rows to the next's
+    const float *base = work + bh * stride;
     const int len = lens[b];
     bool bad = len < 0 || len > max_len;
     if (check_pos) {
         const int pr = pos[b];
         bad = bad || pr < 0 || pr >= table_rows;
     }
-    float M = -INFINITY;
-    for (int64_t s = 0; s < splits; ++s) M = fmaxf(M, work[(s * batch * hq + bh) * stride + D]);
-    float L = 0.f, A = 0.f;
-    if (M != -INFINITY) {
-        for (int64_t s = 0; s < splits; ++s) {
-            const float *src = work + (s * batch * hq + bh) * stride;
-            const float f = fast_exp2(src[D] - M);
-            L += src[D + 1] * f;
-            A += src[e] * f;
+    if (splits <= 8) {
+        // up to 8 splits: every load at once (indices clamped, values masked after), then
+        // the sums in split order
+        float m[8], l[8], v[8][EPL];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const float *src = base + (s < splits ? s : splits - 1) * sstride;
+            m[s] = src[D];
+            l[s] = src[D + 1];
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) v[s][e] = src[lane + 64 * e];
         }
+        float M = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            if (s < splits) M = fmaxf(M, m[s]);
+        float L = 0.f, A[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) A[e] = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                if (s < splits) {
+                    const float f = fast_exp2(m[s] - M);
+                    L += l[s] * f;
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e) A[e] += v[s][e] * f;
+                }
+            }
+        }
+        merge_store<BF16, D>(out, bh, lane, A, L, bad);
+        return;
     }
-    float y = L > 0.f ? A / L : 0.f;
-    if (bad || L != L) y = __builtin_nanf("");
-    if constexpr (BF16) {
-        f32x2 v2 = {y, 0.f};
-        bf16x2 hv = __builtin_convertvector(v2, bf16x2);
-        static_cast<uint16_t *>(out)[bh * D + e] = (uint16_t)(__builtin_bit_cast(uint32_t, hv) & 0xFFFFu);
-    } else {
-        static_cast<float *>(out)[bh * D + e] = y;
+    float m0 = -INFINITY, l0 = 0.f;
+    if (lane < splits) {
+        m0 = base[lane * sstride + D];
+        l0 = base[lane * sstride + D + 1];
     }
+    float M = m0;
+    for (int64_t s = lane + 64; s < splits; s += 64) M = fmaxf(M, base[s * sstride + D]);
+    M = max_lanes<64>(M);
+    float A[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) A[e] = 0.f;
+    float L = 0.f;
+    if (M != -INFINITY) {
+        for (int64_t s0 = 0; s0 < splits; s0 += 64) {
+            const int64_t s = s0 + lane;
+            float m = m0, l = l0;
+            if (s0 > 0) {
+                m = s < splits ? base[s * sstride + D] : -INFINITY;
+                l = s < splits ? base[s * sstride + D + 1] : 0.f;
+            }
+            const float f = s < splits ? fast_exp2(m - M) : 0.f;
+            L += l * f;
+            const int n = (int)(splits - s0 < 64 ? splits - s0 : 64);
+            const float *src = base + s0 * sstride + lane;
+#pragma unroll 4
+            for (int i = 0; i < n; ++i) {
+                const float fi = __shfl(f, i, 64);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) A[e] += src[i * sstride + 64 * e] * fi;
+            }
+        }
+        L = sum_lanes<64>(L);
+    }
+    merge_store<BF16, D>(out, bh, lane, A, L, bad);
 }
 
 template <bool BF16, int D, int GB>
@@ -438,6 +822,22 @@ void launch_split_gb(const DecodeParams &p, int gb, hipStream_t stream) {
     }
 }
 
+// Launch of decode_rows_kernel: grid (splits, kv-head groups, batch), a wave per kv head
+// of a group of hb D = 512 (or all hkv when fewer).
+int decode_rows_group(int64_t hkv, int64_t d) {
+    int hb = (int)(512 / d);
+    while (hb > 1 && hkv % hb != 0) hb >>= 1;
+    return hb < (int)hkv ? hb : (int)hkv;
+}
+
+template <int D, int GB>
+hipError_t launch_rows(const DecodeLaunch &a, const DecodeParams &p, hipStream_t stream) {
+    const int hb = decode_rows_group(a.hkv, D);
+    hipLaunchKernelGGL((decode_rows_kernel<D, GB>), dim3((unsigned)(a.hkv / hb), (unsigned)a.splits, (unsigned)a.batch),
+                       dim3((unsigned)(64 * hb)), 0, stream, p, hb);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int64_t decode_heads_per_block(int64_t hq, int64_t hkv) {
@@ -447,7 +847,18 @@ int64_t decode_heads_per_block(int64_t hq, int64_t hkv) {
     return gb;
 }
 
+bool decode_rows_fits(int64_t hq, int64_t hkv) {
+    return hkv <= 8 && hq / hkv <= 8;      // a wave per kv head, up to 8 q heads each
+}
+
 int64_t decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len) {
+    if (decode_rows_fits(hq, hkv)) {
+        // a block per (sequence, split): about one block per CU, at least 256 keys each
+        int64_t splits = (kCUs + batch - 1) / batch;
+        const int64_t most = (max_len + 255) / 256;
+        if (splits > most) splits = most;
+        return splits < 1 ? 1 : splits;
+    }
     const int64_t gb = decode_heads_per_block(hq, hkv);
     const int64_t groups = (hq / hkv + gb - 1) / gb;
     const int64_t units = batch * hkv * groups;
@@ -519,9 +930,9 @@ hipError_t launch_decode_merge(const DecodeLaunch &a, hipStream_t stream) {
             hipLaunchKernelGGL((decode_merge_kernel<false, 64>), grid, dim3(64), 0, stream, a.work, a.out, a.lens, a.pos, a.batch, a.hq, a.splits, a.max_len, table_rows, check_pos);
     } else {
         if (a.bf16)
-            hipLaunchKernelGGL((decode_merge_kernel<true, 128>), grid, dim3(128), 0, stream, a.work, a.out, a.lens, a.pos, a.batch, a.hq, a.splits, a.max_len, table_rows, check_pos);
+            hipLaunchKernelGGL((decode_merge_kernel<true, 128>), grid, dim3(64), 0, stream, a.work, a.out, a.lens, a.pos, a.batch, a.hq, a.splits, a.max_len, table_rows, check_pos);
         else
-            hipLaunchKernelGGL((decode_merge_kernel<false, 128>), grid, dim3(128), 0, stream, a.work, a.out, a.lens, a.pos, a.batch, a.hq, a.splits, a.max_len, table_rows, check_pos);
+            hipLaunchKernelGGL((decode_merge_kernel<false, 128>), grid, dim3(64), 0, stream, a.work, a.out, a.lens, a.pos, a.batch, a.hq, a.splits, a.max_len, table_rows, check_pos);
     }
     return hipGetLastError();
 }
@@ -530,6 +941,26 @@ hipError_t launch_decode(const DecodeLaunch &a, hipStream_t stream) {
     if (a.kbits) return launch_decode_q(a, stream);
     const DecodeParams p = make_decode_params(a);
     const int gb = (int)decode_heads_per_block(a.hq, a.hkv);
+    if (a.bf16 && decode_rows_fits(a.hq, a.hkv)) {
+        hipError_t err = hipSuccess;
+        if (a.d == 64) {
+            switch (gb) {
+                case 1: err = launch_rows<64, 1>(a, p, stream); break;
+                case 2: err = launch_rows<64, 2>(a, p, stream); break;
+                case 4: err = launch_rows<64, 4>(a, p, stream); break;
+                default: err = launch_rows<64, 8>(a, p, stream); break;
+            }
+        } else {
+            switch (gb) {
+                case 1: err = launch_rows<128, 1>(a, p, stream); break;
+                case 2: err = launch_rows<128, 2>(a, p, stream); break;
+                case 4: err = launch_rows<128, 4>(a, p, stream); break;
+                default: err = launch_rows<128, 8>(a, p, stream); break;
+            }
+        }
+        if (err != hipSuccess) return err;
+        return launch_decode_merge(a, stream);
+    }
     if (a.d == 64) {
         if (a.bf16) launch_split_gb<true, 64>(p, gb, stream); else launch_split_gb<false, 64>(p, gb, stream);
     } else {

@@ -526,7 +526,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (t < ntiles && visible(t)) g1(kcur);
             __builtin_amdgcn_s_setprio(0);
             if (!loads_k) wait_older(t + 1 < ntiles);      // V_t in LDS (V_{t+1} may fly)
-            __syncthreads();
+            lds_barrier();
             // Both groups issue their loads as their softmax step starts, so each block
             // phase carries one group's load issue and no matrix step carries any.
             if (t + 2 < ntiles) load_tile(t + 2, loads_k ? knext2 : vnext2);
@@ -536,13 +536,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int t = 0;; t += 3) {
             period(t, kb0, kb2, vb2, vb2);
             if (t == ntiles) break;
-            __syncthreads();
+            lds_barrier();
             period(t + 1, kb1, kb0, vb0, vb0);
             if (t + 1 == ntiles) break;
-            __syncthreads();
+            lds_barrier();
             period(t + 2, kb2, kb1, vb1, vb1);
             if (t + 2 == ntiles) break;
-            __syncthreads();
+            lds_barrier();
         }
 
         // ---- epilogue (in the softmax step of period ntiles): divide by the row sum,

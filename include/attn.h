@@ -257,6 +257,29 @@ attn_status_t attn_decode_paged(const void *q, const void *k_pool, const void *v
                                 void *stream);
 
 /*
+ * attn_decode_static -- attn_decode without a workspace, for callers that cannot
+ * allocate device memory (code under stream or graph capture, tight serving loops,
+ * hosts that forbid allocation).  The split partials go to a scratch array of
+ * attn_decode_static_scratch_bytes() (8 MiB) that the library holds in device memory,
+ * one per device, until the process ends.  This call allocates nothing; its first call
+ * on a device looks the array's address up once.
+ *   Every argument is attn_decode's.  splits = 0 takes attn_decode_default_splits,
+ *   lowered until the partials (splits * batch * hq * (d + 2) * 4 bytes when splits > 1;
+ *   none for one split) fit the scratch.  An explicit split count whose partials do not
+ *   fit is rejected with ATTN_ERR_WORKSPACE before anything is enqueued.
+ *   Every call on one device shares that device's scratch, and nothing in it must start
+ *   at zero: calls that overlap in time on one device (other streams, other host
+ *   threads) race and give wrong results.  Results equal attn_decode's with the same
+ *   split count.
+ */
+size_t attn_decode_static_scratch_bytes(void);
+attn_status_t attn_decode_static(const void *q, const void *k_cache, const void *v_cache, void *out,
+                                 int64_t batch, int64_t hq, int64_t hkv, int64_t d, int64_t capacity,
+                                 const int32_t *lens, const int32_t *pos, int64_t max_len, int64_t max_pos,
+                                 const attn_headprep_t *prep, double scale, int64_t splits,
+                                 attn_dtype_t dtype, void *stream);
+
+/*
  * Quantised KV cache (compute guide "Tensors, GPU kernels and AI models", Step 5: Run a
  * language model: keys and values kept in 8, 4 or 2 bits, or keys in 4 and values in 2,
  * each head coded over the range that returns it with the least squared error).

@@ -12,6 +12,7 @@ from .attn import (  # noqa: F401
     EXPORTS,
     attn_decode,
     attn_decode_paged,
+    attn_decode_static,
     attn_decode_q,
     attn_decode_q_paged,
     attn_kv_quantize,
@@ -28,6 +29,7 @@ from .attn import (  # noqa: F401
     attn_supported,
     decode_default_splits,
     decode_q_default_splits,
+    decode_static_scratch_bytes,
     decode_workspace_size,
     key_bound,
     load_library,

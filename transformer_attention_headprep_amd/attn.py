@@ -24,7 +24,7 @@ EXPORTS = ("attn_prep", "attn_prefill", "attn_prefill_chunk", "attn_prefill_chun
            "attn_decode_default_splits", "attn_decode_paged", "attn_kv_quantize", "attn_decode_q",
            "attn_decode_q_paged", "attn_decode_q_default_splits", "attn_rows", "attn_rows8_layout", "attn_rows8_quantize",
            "attn_rows8_attend", "attn_rows8", "attn_row_norm_rope", "attn_key_bound", "attn_supported",
-           "attn_status_str", "attn_last_error")
+           "attn_status_str", "attn_last_error", "attn_decode_static", "attn_decode_static_scratch_bytes")
 
 
 class AttnError(RuntimeError):
@@ -93,6 +93,11 @@ def load_library(path: str = LIB_PATH):
     lib.attn_decode_paged.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 6 + [_vp, _i64, _vp, _vp, _i64, _i64, hp, _dbl, _i64,
                                                                             _vp, ctypes.c_size_t, ctypes.c_int, _vp]
     lib.attn_decode_paged.restype = ctypes.c_int
+    lib.attn_decode_static.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 5 + [_vp, _vp, _i64, _i64, hp, _dbl, _i64,
+                                                                           ctypes.c_int, _vp]
+    lib.attn_decode_static.restype = ctypes.c_int
+    lib.attn_decode_static_scratch_bytes.argtypes = []
+    lib.attn_decode_static_scratch_bytes.restype = ctypes.c_size_t
     lib.attn_decode_q_paged.argtypes = [_vp] * 6 + [_i64] * 8 + [_vp, _i64, _vp, _vp, _i64, _i64, hp, _dbl, _i64, _vp,
                                                                   ctypes.c_size_t, ctypes.c_int, _vp]
     lib.attn_decode_q_paged.restype = ctypes.c_int
@@ -521,6 +526,36 @@ def attn_decode(q, k_cache, v_cache, lens, pos, max_len: int, prep: HeadPrep | N
                            _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
                            _dtype_code(q), _stream(stream)))
     return out
+
+
+def attn_decode_static(q, k_cache, v_cache, lens, pos, max_len: int, prep: HeadPrep | None = None,
+                       scale: float | None = None, splits: int = 0, out=None, stream=None,
+                       max_pos: int | None = None) -> torch.Tensor:
+    """attn_decode with its split partials in the library's own device scratch (no
+    workspace).  `out` should be given by callers that cannot allocate."""
+    lib = load_library()
+    B, hq, D = q.shape
+    cap, hkv = k_cache.shape[1], k_cache.shape[2]
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if lens.dtype != torch.int32 or (pos is not None and pos.dtype != torch.int32):
+        raise TypeError("lens and pos must be int32 device tensors")
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = prep.struct() if prep is not None else None
+    _check(lib.attn_decode_static(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), B, hq, hkv, D, cap,
+                                  _ptr(lens), _ptr(pos), max_len, _max_pos(prep, max_pos),
+                                  ctypes.byref(st) if st is not None else None, float(scale), splits,
+                                  _dtype_code(q), _stream(stream)))
+    return out
+
+
+def decode_static_scratch_bytes() -> int:
+    """Bytes of the device scratch attn_decode_static uses."""
+    return int(load_library().attn_decode_static_scratch_bytes())
 
 
 def attn_decode_paged(q, k_pool, v_pool, pages, lens, pos, max_len: int, prep: HeadPrep | None = None,

@@ -683,6 +683,41 @@ attn_status_t attn_decode_paged(const void *q, const void *k_pool, const void *v
                        workspace, workspace_bytes, dtype, stream, "attn_decode_paged");
 }
 
+size_t attn_decode_static_scratch_bytes(void) { return attn::decode_scratch_bytes(); }
+
+attn_status_t attn_decode_static(const void *q, const void *k_cache, const void *v_cache, void *out, int64_t batch,
+                                 int64_t hq, int64_t hkv, int64_t d, int64_t capacity, const int32_t *lens,
+                                 const int32_t *pos, int64_t max_len, int64_t max_pos, const attn_headprep_t *prep,
+                                 double scale, int64_t splits, attn_dtype_t dtype, void *stream) {
+    g_last_error[0] = 0;
+    const size_t cap = attn::decode_scratch_bytes();
+    int64_t s = splits;
+    // the split count, and the scratch it needs (decode_impl reports bad arguments; the
+    // size is only worked out for sane ones)
+    size_t need = 0;
+    if (batch > 0 && hq > 0 && hkv > 0 && hq % hkv == 0 && (d == 64 || d == 128) && max_len > 0 && s >= 0) {
+        const size_t per_split = attn::decode_workspace_bytes(batch, hq, d, 2) / 2;
+        if (s == 0) {
+            // the library's choice, lowered until the partials fit (one split needs none)
+            s = attn::decode_default_splits(batch, hq, hkv, max_len);
+            if (s > 1 && (size_t)s * per_split > cap) s = std::max<int64_t>(1, (int64_t)(cap / per_split));
+        }
+        need = attn::decode_workspace_bytes(batch, hq, d, s);
+        if (need > cap)
+            return fail(ATTN_ERR_WORKSPACE,
+                        "attn_decode_static: %lld splits need %zu bytes of scratch; the library's scratch holds %zu "
+                        "(ask for fewer splits, or use attn_decode with a workspace)",
+                        (long long)s, need, cap);
+    }
+    void *ws = nullptr;
+    if (need > 0) {
+        const hipError_t err = attn::decode_scratch(&ws);
+        if (err != hipSuccess) return hip_status(err, "attn_decode_static (scratch address)");
+    }
+    return decode_impl(q, k_cache, v_cache, out, batch, hq, hkv, d, capacity, nullptr, lens, pos, max_len, max_pos, prep,
+                       scale, s, ws, need > 0 ? cap : 0, dtype, stream, "attn_decode_static");
+}
+
 attn_status_t attn_kv_quantize(const void *x, int64_t batch, int64_t seq, int64_t heads, int64_t d,
                                int64_t x_row_stride, int64_t bits, uint8_t *codes, float *params,
                                int64_t capacity, int64_t row0, attn_dtype_t dtype, void *stream) {

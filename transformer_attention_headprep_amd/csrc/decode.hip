@@ -30,6 +30,8 @@
 //     the blocks' streams do not move through equally spaced sequences in lockstep.
 // f32 caches (decode_f32_kernel): S^T on v_mfma_f32_16x16x4f32, P V on the vector ALUs
 // (D/4 lanes share one value row) with the chunk's weights passed through LDS.
+#include <mutex>
+
 #include "decode_common.h"
 
 namespace attn {
@@ -886,6 +888,36 @@ int64_t decode_q_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t 
 size_t decode_workspace_bytes(int64_t batch, int64_t hq, int64_t d, int64_t splits) {
     if (splits <= 1) return 0;                                     // one split writes the output
     return (size_t)splits * (size_t)batch * (size_t)hq * (size_t)(d + 2) * sizeof(float);
+}
+
+// The split partials of attn_decode_static: a fixed array in device memory instead of a
+// caller's workspace.  Every device the library runs on holds its own copy, at its own
+// address, until the process ends.  Host code uses only the address that
+// hipGetSymbolAddress returns for the current device (the array's name in host code is
+// a host-side stand-in, not a device address).
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t decode_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 DecodeParams make_decode_params(const DecodeLaunch &a) {

@@ -154,5 +154,9 @@ bool decode_rows_fits(int64_t hq, int64_t hkv);
 int64_t decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len);
 int64_t decode_q_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len, int64_t kbits);
 size_t decode_workspace_bytes(int64_t batch, int64_t hq, int64_t d, int64_t splits);
+// The decode scratch that lives in the library (for callers that cannot allocate): its
+// size, and its address on the current device (looked up once per device).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void **ptr);
 
 }  // namespace attn

@@ -34,6 +34,7 @@ from .oracle import (  # noqa: F401
     decode_paged,
     prefill,
     prefill_chunk,
+    prefill_chunk_ragged,
     attended_rows,
     attended_rows8,
     rows8_operands,

@@ -223,6 +223,27 @@ def prefill_chunk(q, k_new, v_new, k_cache, v_cache, n_past: int, qw, kw, cos, s
     return out, kc, vc
 
 
+def prefill_chunk_ragged(q, k_new, v_new, k_cache, v_cache, past, qw, kw, cos, sin, half: int,
+                         eps: float, scale: float, causal: bool = True, prep: bool = True,
+                         prep_k: bool = True):
+    """One engine step over sequences at different cache lengths (compute guide "Tensors,
+    GPU kernels and AI models", Step 5: one step reads the prompt rows of many sequences):
+    sequence b's chunk of tq tokens goes after its own past[b] cached rows, exactly as
+    prefill_chunk with n_past = past[b] on that sequence alone.  Returns (out, k_cache',
+    v_cache') (copies, f64)."""
+    past = np.asarray(past, dtype=np.int64).reshape(-1)
+    B = q.shape[0]
+    assert past.shape[0] == B
+    out = np.zeros(q.shape[:3] + (v_new.shape[3],), dtype=np.float64)
+    kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
+    for b in range(B):
+        sl = slice(b, b + 1)
+        ob, kb, vb = prefill_chunk(q[sl], k_new[sl], v_new[sl], kc[sl], vc[sl], int(past[b]), qw, kw, cos, sin,
+                                   half, eps, scale, causal, prep=prep, prep_k=prep_k)
+        out[b], kc[b], vc[b] = ob[0], kb[0], vb[0]
+    return out, kc, vc
+
+
 def attended_rows(qkv, heads: int, head: int, group: int = 0, queries: int = 0, prep=None):
     """attentionRows / attendedRows (gizml:netops, Functions > attentionRows): qkv [n, 3 heads
     head] holds each row's q, k and v; with ``prep`` (a dict qw, kw, cos, sin, half, eps and

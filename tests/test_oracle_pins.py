@@ -418,6 +418,64 @@ def test_chunk_of_one_token_is_decode():
         np.testing.assert_allclose(out_nc[:, i], dec, rtol=0, atol=1e-14)
 
 
+def test_ragged_chunks_equal_one_shot_prefill_per_sequence():
+    """Sequences at different cache lengths in one step (compute guide, Step 5): sequence
+    b's chunk after past[b] cached rows gives rows past[b] .. past[b] + tq - 1 of that
+    sequence's one-shot causal prefill, writes its prepped keys and values at those rows,
+    and leaves every later row as it was.  A non-causal chunk's query sees exactly the
+    sequence's first past[b] + tq rows."""
+    w = synthetic.WORKLOADS["prefill_f32"]
+    past = np.array([0, 17, 29, 5], dtype=np.int64)
+    tq, cap, B = 8, 48, 4
+    inp = synthetic.make_prefill(w, seq=40, batch=B)
+    kc = np.full((B, cap, w.hkv, w.d), 7.0)
+    vc = np.full((B, cap, w.hkv, w.d), -3.0)
+    fulls = []
+    for b in range(B):
+        T = int(past[b]) + tq
+        full, kh = oracle.prefill(inp["q"][b:b + 1, :T], inp["k"][b:b + 1, :T], inp["v"][b:b + 1, :T], inp["qw"],
+                                  inp["kw"], inp["cos"], inp["sin"], w.half, w.eps, 0, w.scale, True)
+        fulls.append((full[0], kh[0]))
+        kc[b, :past[b]] = kh[0, :past[b]]
+        vc[b, :past[b]] = inp["v"][b, :past[b]]
+    qn = np.stack([inp["q"][b, past[b]:past[b] + tq] for b in range(B)])
+    kn = np.stack([inp["k"][b, past[b]:past[b] + tq] for b in range(B)])
+    vn = np.stack([inp["v"][b, past[b]:past[b] + tq] for b in range(B)])
+    out, kc2, vc2 = oracle.prefill_chunk_ragged(qn, kn, vn, kc, vc, past, inp["qw"], inp["kw"], inp["cos"],
+                                                inp["sin"], w.half, w.eps, w.scale, True)
+    for b in range(B):
+        T = int(past[b]) + tq
+        full, kh = fulls[b]
+        np.testing.assert_allclose(out[b], full[past[b]:T], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(kc2[b, :T], kh, rtol=0, atol=0)
+        np.testing.assert_array_equal(vc2[b, :T], inp["v"][b, :T])
+        assert (kc2[b, T:] == 7.0).all() and (vc2[b, T:] == -3.0).all()
+    # non-causal: query i of sequence b is the decode of position past[b] + i over T rows
+    out_nc, kc3, vc3 = oracle.prefill_chunk_ragged(qn, kn, vn, kc, vc, past, inp["qw"], inp["kw"], inp["cos"],
+                                                   inp["sin"], w.half, w.eps, w.scale, False)
+    for b in range(B):
+        T = int(past[b]) + tq
+        for i in (0, tq - 1):
+            dec = oracle.decode(qn[b:b + 1, i], kc3[b:b + 1], vc3[b:b + 1], np.array([T]),
+                                np.array([past[b] + i]), inp["qw"], inp["cos"], inp["sin"], w.half, w.eps, w.scale)
+            np.testing.assert_allclose(out_nc[b, i], dec[0], rtol=0, atol=1e-14)
+
+
+def test_ragged_chunk_with_equal_lengths_is_the_batched_chunk():
+    """With every past[b] equal, the ragged step is prefill_chunk of the whole batch."""
+    w = synthetic.WORKLOADS["prefill_f32"]
+    inp = synthetic.make_prefill(w, seq=24, batch=3)
+    kc = np.full((3, 40, w.hkv, w.d), 0.5)
+    vc = np.full((3, 40, w.hkv, w.d), 1.5)
+    q, k, v = inp["q"][:, :10], inp["k"][:, :10], inp["v"][:, :10]
+    a = oracle.prefill_chunk(q, k, v, kc, vc, 11, inp["qw"], inp["kw"], inp["cos"], inp["sin"], w.half, w.eps,
+                             w.scale, True)
+    r = oracle.prefill_chunk_ragged(q, k, v, kc, vc, [11, 11, 11], inp["qw"], inp["kw"], inp["cos"], inp["sin"],
+                                    w.half, w.eps, w.scale, True)
+    for x, y in zip(a, r):
+        np.testing.assert_array_equal(x, y)
+
+
 def test_tiny_workload_end_to_end_against_library_routines():
     """The tiny f32 workload: oracle prefill vs torch rms_norm + complex turn + SDPA."""
     w = synthetic.WORKLOADS["tiny_f32"]

@@ -164,16 +164,23 @@ attn_status_t attn_prefill(const void *q, void *k, const void *v, void *out,
  *                hold the earlier tokens (keys prepped); rows n_past .. n_past + tq - 1
  *                are overwritten; later rows are not touched.
  *   out          [batch, tq, hq, d] contiguous; must not overlap any other buffer.
- *   n_past       the same for every sequence; 0 <= n_past, n_past + tq <= capacity
- *                (n_past = 0 is attn_prefill of the chunk with the cache as k and v).
+ *   n_past       with past NULL, every sequence's cached rows; 0 <= n_past, n_past + tq
+ *                <= capacity (n_past = 0 is attn_prefill of the chunk with the cache as
+ *                k and v).  With past given, the host bound on every past[b].
+ *   past         NULL, or device int32 [batch]: sequence b holds past[b] cached rows and
+ *                everything above reads past[b] for n_past for that sequence (one engine
+ *                step over sequences at different positions: compute guide "Tensors,
+ *                GPU kernels and AI models", Step 5).  A past[b] outside [0, n_past] gives
+ *                NaN output rows for sequence b and writes none of its cache rows.  Must
+ *                not overlap out or the caches.
  *   scale        finite and > 0.
  *   The caches must not overlap each other or k_new / v_new.  Errors as attn_prefill.
  */
 attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v_new, void *k_cache,
                                  void *v_cache, void *out, int64_t batch, int64_t tq, int64_t hq,
                                  int64_t hkv, int64_t d, int64_t capacity, int64_t n_past,
-                                 const attn_headprep_t *prep, int causal, double scale,
-                                 attn_dtype_t dtype, void *stream);
+                                 const int32_t *past, const attn_headprep_t *prep, int causal,
+                                 double scale, attn_dtype_t dtype, void *stream);
 
 /*
  * attn_prefill_chunk_paged -- attn_prefill_chunk with the cache in a paged KV pool
@@ -182,16 +189,17 @@ attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v
  * int32) as in attn_decode_paged, with page_rows a power of two in [64, 2^20].  The
  * chunk's keys (prepped when prep->kw is set) and values are written to rows n_past ..
  * n_past + tq - 1 of each sequence's pages; its queries then attend rows 0 .. n_past +
- * tq - 1 read through the table.  n_past + tq <= max_pages * page_rows.  A page id
- * outside [0, num_pages) is not written and gives NaN output rows for its sequence.
- * bf16 only (ATTN_ERR_UNSUPPORTED for f32).
+ * tq - 1 read through the table.  n_past + tq <= max_pages * page_rows.  past as in
+ * attn_prefill_chunk (sequence b's rows past[b] .. of its pages; n_past the bound).  A
+ * page id outside [0, num_pages) is not written and gives NaN output rows for its
+ * sequence.  bf16 only (ATTN_ERR_UNSUPPORTED for f32).
  */
 attn_status_t attn_prefill_chunk_paged(const void *q, const void *k_new, const void *v_new, void *k_pool,
                                        void *v_pool, void *out, int64_t batch, int64_t tq, int64_t hq,
                                        int64_t hkv, int64_t d, int64_t num_pages, int64_t page_rows,
                                        const int32_t *pages, int64_t max_pages, int64_t n_past,
-                                       const attn_headprep_t *prep, int causal, double scale,
-                                       attn_dtype_t dtype, void *stream);
+                                       const int32_t *past, const attn_headprep_t *prep, int causal,
+                                       double scale, attn_dtype_t dtype, void *stream);
 
 /*
  * attn_decode -- one new query row per sequence against a KV cache whose keys are

@@ -160,11 +160,11 @@ def test_prep_empty_is_a_no_op(lib):
 def _chunk(lib, **kw):
     a = dict(q=FAKE, kn=FAKE + (1 << 32), vn=FAKE + (2 << 32), kc=FAKE + (3 << 32), vc=FAKE + (4 << 32),
              out=FAKE + (5 << 32), batch=2, tq=16, hq=8, hkv=2, d=128, cap=1024, n_past=100,
-             prep=_prep(rows=4096), causal=1, scale=0.088, dtype=A.ATTN_BF16)
+             prep=_prep(rows=4096), causal=1, scale=0.088, dtype=A.ATTN_BF16, past=None)
     a.update(kw)
     prep = ctypes.byref(a["prep"]) if a["prep"] is not None else None
     return lib.attn_prefill_chunk(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["out"], a["batch"], a["tq"],
-                                  a["hq"], a["hkv"], a["d"], a["cap"], a["n_past"], prep, a["causal"],
+                                  a["hq"], a["hkv"], a["d"], a["cap"], a["n_past"], a["past"], prep, a["causal"],
                                   a["scale"], a["dtype"], None)
 
 
@@ -184,6 +184,9 @@ def _chunk(lib, **kw):
     (dict(out=FAKE + (3 << 32) + 4096), A.ATTN_ERR_ARG),  # out inside the k cache
     (dict(vc=FAKE + (3 << 32) + 8192), A.ATTN_ERR_ARG),   # the caches overlap
     (dict(kn=FAKE + (4 << 32) + 512), A.ATTN_ERR_ARG),    # new keys inside the v cache
+    (dict(past=FAKE + (5 << 32) + 64), A.ATTN_ERR_ARG),   # per-sequence lengths inside out
+    (dict(past=FAKE + (3 << 32) + 64), A.ATTN_ERR_ARG),   # per-sequence lengths inside a cache
+    (dict(past=FAKE + (6 << 32), n_past=1010), A.ATTN_ERR_ARG),   # the bound + tq > capacity
 ])
 def test_prefill_chunk_rejects(lib, kw, code):
     assert _chunk(lib, **kw) == code
@@ -295,7 +298,7 @@ def test_prefill_chunk_paged_rejects(lib):
         prep = _prep(rows=4097)
         return lib.attn_prefill_chunk_paged(FAKE, FAKE + (1 << 32), FAKE + (2 << 32), FAKE + (3 << 32),
                                             FAKE + (4 << 32), FAKE + (5 << 32), 4, a["tq"], 32, 8, 128, 256,
-                                            a["page_rows"], a["pages"], a["max_pages"], a["n_past"],
+                                            a["page_rows"], a["pages"], a["max_pages"], a["n_past"], None,
                                             ctypes.byref(prep), 1, a["scale"], a["dtype"], None)
     assert call(scale=0.0) == A.ATTN_ERR_ARG                  # every case fails on the host
     assert call(dtype=A.ATTN_F32) == A.ATTN_ERR_UNSUPPORTED
@@ -507,3 +510,26 @@ def test_rows8_rejects(lib, kw, code):
 
 def test_rows8_empty_is_a_no_op(lib):
     assert _rows8(lib, n=0) == A.ATTN_OK
+
+
+def test_guarded_kernels_do_not_spill():
+    """The kernels that count their own loads into LDS in vmcnt (bf16 prefill, whole-row
+    decode) are built without register spills: the build's resource report says so (the
+    build itself fails otherwise)."""
+    from transformer_attention_headprep_amd import build as B
+    if not os.path.exists(B.RESOURCE_REPORT):
+        pytest.skip("library not built in this tree")
+    rows = [line.split() for line in open(B.RESOURCE_REPORT) if line.strip()]
+    guarded = [r for r in rows if any(k in r[1] for k in B.NO_SPILL[r[0]])]
+    assert guarded, "no guarded kernel in the report"
+    for r in guarded:
+        assert r[3] == "vgpr_spill=0", r
+
+
+def test_resource_report_parser_reads_spills():
+    from transformer_attention_headprep_amd import build as B
+    text = ("x.hip:1:1: remark: Function Name: _Z3fooi [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:1:1: remark:     VGPRs: 256 [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:1:1: remark:     VGPRs Spill: 94 [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:1:1: remark:     SGPRs Spill: 3 [-Rpass-analysis=kernel-resource-usage]\n")
+    assert B.parse_resource_usage(text) == [("_Z3fooi", 256, 94, 3)]

@@ -271,6 +271,54 @@ def test_prefill_chunk_paged_matches_contiguous(page_rows, n_past, tq):
     assert_close(got, ref, "bf16", "paged chunk")
 
 
+@pytest.mark.parametrize("page_rows", [64, 128])
+def test_prefill_chunk_paged_per_sequence_lengths(page_rows):
+    """Sequences at different cache lengths (device int32 past, the bound 520): the pool
+    gives the contiguous caches' outputs and appended rows bit for bit, writes no page a
+    sequence does not own, and the output is within the bf16 tolerance of the oracle."""
+    require_gpu()
+    B, hq, hkv, d, tq, bound = 4, 8, 2, 128, 130, 520
+    past = [0, 300, 517, 64]
+    w = synthetic.Workload("pr", "prefill", "bf16", B, hq, hkv, bound + tq, d, d // 2, 1e4, 401 + page_rows)
+    inp = synthetic.make_prefill(w)
+    cap = bound + tq + 3
+    kc = np.full((B, cap, hkv, d), np.nan)
+    vc = np.full((B, cap, hkv, d), np.nan)
+    for b, pb in enumerate(past):
+        if pb:
+            kc[b, :pb] = synthetic.bf16_round(oracle.headprep(inp["k"][b:b + 1, :pb], inp["kw"], inp["cos"],
+                                                              inp["sin"], d // 2, np.arange(pb)[None], w.eps))[0]
+            vc[b, :pb] = inp["v"][b, :pb]
+    lens = [pb + tq for pb in past]
+    num_pages = sum((L + page_rows - 1) // page_rows for L in lens) + 4
+    pages = _page_table(lens, page_rows, num_pages, 0, seed=page_rows)
+    kpool = _fill_pool(kc, pages, past, page_rows, num_pages)
+    vpool = _fill_pool(vc, pages, past, page_rows, num_pages)
+    ch = {n: np.stack([inp[n][b, pb:pb + tq] for b, pb in enumerate(past)]) for n in ("q", "k", "v")}
+    hp = tah.HeadPrep(dev(inp["qw"], "f32"), dev(inp["kw"], "f32"), dev(inp["cos"], "f32"), dev(inp["sin"], "f32"),
+                      w.eps)
+    q, kn, vn = dev(ch["q"], "bf16"), dev(ch["k"], "bf16"), dev(ch["v"], "bf16")
+    pdev = _i32(past)
+    kcd, vcd = dev(kc, "bf16"), dev(vc, "bf16")
+    ref_out = host(tah.attn_prefill_chunk(q, kn, vn, kcd, vcd, bound, prep=hp, causal=True, scale=w.scale, past=pdev))
+    kpd, vpd = dev(kpool, "bf16"), dev(vpool, "bf16")
+    got = host(tah.attn_prefill_chunk_paged(q, kn, vn, kpd, vpd, _i32(pages), bound, prep=hp, causal=True,
+                                            scale=w.scale, past=pdev))
+    np.testing.assert_array_equal(got, ref_out)
+    kp_after, vp_after = host(kpd), host(vpd)
+    kc_after, vc_after = host(kcd), host(vcd)
+    for b, L in enumerate(lens):
+        np.testing.assert_array_equal(oracle.gather_paged(kp_after, pages[b:b + 1], [L])[0, :L], kc_after[b, :L])
+        np.testing.assert_array_equal(oracle.gather_paged(vp_after, pages[b:b + 1], [L])[0, :L], vc_after[b, :L])
+    used = set(int(x) for x in pages.reshape(-1) if x >= 0)
+    for pg in range(num_pages):
+        if pg not in used:
+            assert np.isnan(kp_after[pg]).all() and np.isnan(vp_after[pg]).all(), "page %d written" % pg
+    ref, _, _ = oracle.prefill_chunk_ragged(ch["q"], ch["k"], ch["v"], kc, vc, past, inp["qw"], inp["kw"], inp["cos"],
+                                            inp["sin"], d // 2, w.eps, w.scale, True)
+    assert_close(got, ref, "bf16", "paged ragged chunk")
+
+
 def test_prefill_chunk_paged_shared_prefix_and_bad_page():
     """Two sequences on one copy of a 128-row start, each appending into its own pages,
     give what private copies give; a page id outside the pool among the pages a chunk

@@ -328,6 +328,76 @@ def test_prefill_chunk_parity(dtype, d, half, hq, hkv, n_past, tq, causal):
     assert np.isnan(kc_gpu[:, end:]).all() and np.isnan(vc_gpu[:, end:]).all()   # later rows untouched
 
 
+def _ragged_inputs(dtype, d, half, hq, hkv, past, tq, bound, seed, spare=5):
+    """Sequences at different cache lengths: sequence b's cache holds the first past[b]
+    of its tokens (keys prepped by the oracle, stored in the dtype) and NaN from there on;
+    its chunk is its next tq tokens."""
+    B = len(past)
+    w = synthetic.Workload("r", "prefill", dtype, B, hq, hkv, bound + tq, d, half, 1e4, seed)
+    inp = synthetic.make_prefill(w)
+    cap = bound + tq + spare
+    kc = np.full((B, cap, hkv, d), np.nan)
+    vc = np.full((B, cap, hkv, d), np.nan)
+    for b, pb in enumerate(past):
+        if pb:
+            pos = np.arange(pb)[None]
+            kc[b, :pb] = synthetic.to_storage(
+                oracle.headprep(inp["k"][b:b + 1, :pb], inp["kw"], inp["cos"], inp["sin"], half, pos, w.eps), dtype)[0]
+            vc[b, :pb] = inp["v"][b, :pb]
+    chunk = {n: np.stack([inp[n][b, pb:pb + tq] for b, pb in enumerate(past)]) for n in ("q", "k", "v")}
+    return w, inp, kc, vc, chunk
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("dtype,d,half,hq,hkv,past,tq,bound", [
+    ("bf16", 128, 64, 8, 2, (0, 37, 300, 129), 150, 320),   # ragged tiles, one empty cache
+    ("bf16", 64, 32, 4, 4, (1000, 3, 511), 1, 1000),         # one token each
+    ("bf16", 128, 24, 8, 2, (90, 7), 77, 100),               # q prepped into out first
+    ("f32", 64, 32, 8, 2, (150, 0, 63), 70, 150),
+])
+def test_prefill_chunk_per_sequence_lengths(dtype, d, half, hq, hkv, past, tq, bound, causal):
+    """One step over sequences at different cache lengths (past, device int32) against
+    the oracle's per-sequence composition; each sequence's rows before past[b] and from
+    past[b] + tq on stay as they were."""
+    require_gpu()
+    w, inp, kc, vc, ch = _ragged_inputs(dtype, d, half, hq, hkv, list(past), tq, bound, seed=91 + tq + len(past))
+    dt = w.dtype
+    kcd, vcd = dev(kc, dt), dev(vc, dt)
+    pdev = torch.tensor(past, dtype=torch.int32, device="cuda:0")
+    out = tah.attn_prefill_chunk(dev(ch["q"], dt), dev(ch["k"], dt), dev(ch["v"], dt), kcd, vcd, bound,
+                                 prep=_prep_dev(inp), causal=causal, scale=w.scale, past=pdev)
+    got, kc_gpu, vc_gpu = host(out), host(kcd), host(vcd)
+    ref, kc_ref, vc_ref = oracle.prefill_chunk_ragged(ch["q"], ch["k"], ch["v"], kc, vc, past, inp["qw"], inp["kw"],
+                                                      inp["cos"], inp["sin"], half, w.eps, w.scale, causal)
+    assert_close(got, ref, dtype, "ragged chunk output")
+    for b, pb in enumerate(past):
+        end = pb + tq
+        assert_close(kc_gpu[b, pb:end], kc_ref[b, pb:end], dtype, "appended keys of sequence %d" % b)
+        np.testing.assert_array_equal(vc_gpu[b, pb:end], ch["v"][b])
+        np.testing.assert_array_equal(kc_gpu[b, :pb], kc[b, :pb])
+        assert np.isnan(kc_gpu[b, end:]).all() and np.isnan(vc_gpu[b, end:]).all()
+
+
+def test_prefill_chunk_per_sequence_lengths_out_of_range():
+    """A past[b] above the bound or below 0 gives NaN rows for that sequence only and
+    writes none of its cache rows; the others are as with their own lengths."""
+    require_gpu()
+    past = [40, 250, -3, 0]
+    w, inp, kc, vc, ch = _ragged_inputs("bf16", 128, 64, 8, 2, [40, 0, 0, 0], 64, 200, seed=5)
+    kcd, vcd = dev(kc, "bf16"), dev(vc, "bf16")
+    pdev = torch.tensor(past, dtype=torch.int32, device="cuda:0")
+    out = host(tah.attn_prefill_chunk(dev(ch["q"], "bf16"), dev(ch["k"], "bf16"), dev(ch["v"], "bf16"), kcd, vcd, 200,
+                                      prep=_prep_dev(inp), causal=True, scale=w.scale, past=pdev))
+    kc_gpu, vc_gpu = host(kcd), host(vcd)
+    assert np.isnan(out[1]).all() and np.isnan(out[2]).all()
+    assert np.isnan(kc_gpu[1]).all() and np.isnan(vc_gpu[1]).all()       # nothing written
+    assert np.isnan(kc_gpu[2]).all() and np.isnan(vc_gpu[2]).all()
+    ref, _, _ = oracle.prefill_chunk_ragged(ch["q"][[0, 3]], ch["k"][[0, 3]], ch["v"][[0, 3]], kc[[0, 3]], vc[[0, 3]],
+                                            [40, 0], inp["qw"], inp["kw"], inp["cos"], inp["sin"], 64, w.eps, w.scale,
+                                            True)
+    assert_close(out[[0, 3]], ref, "bf16", "in-range sequences")
+
+
 def test_prefill_chunk_with_prepped_keys():
     """prep->kw NULL: the chunk's keys are already prepped and are copied as they are."""
     require_gpu()

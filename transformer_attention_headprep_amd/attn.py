@@ -58,9 +58,9 @@ def load_library(path: str = LIB_PATH):
     lib.attn_prefill.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 10 + [hp, ctypes.c_int, _dbl,
                                                                          ctypes.c_int, _vp]
     lib.attn_prefill.restype = ctypes.c_int
-    lib.attn_prefill_chunk.argtypes = [_vp] * 6 + [_i64] * 7 + [hp, ctypes.c_int, _dbl, ctypes.c_int, _vp]
+    lib.attn_prefill_chunk.argtypes = [_vp] * 6 + [_i64] * 7 + [_vp, hp, ctypes.c_int, _dbl, ctypes.c_int, _vp]
     lib.attn_prefill_chunk.restype = ctypes.c_int
-    lib.attn_prefill_chunk_paged.argtypes = [_vp] * 6 + [_i64] * 7 + [_vp, _i64, _i64, hp, ctypes.c_int, _dbl,
+    lib.attn_prefill_chunk_paged.argtypes = [_vp] * 6 + [_i64] * 7 + [_vp, _i64, _i64, _vp, hp, ctypes.c_int, _dbl,
                                                                       ctypes.c_int, _vp]
     lib.attn_prefill_chunk_paged.restype = ctypes.c_int
     lib.attn_decode.argtypes = [_vp, _vp, _vp, _vp] + [_i64] * 5 + [_vp, _vp, _i64, _i64, hp, _dbl, _i64,
@@ -241,11 +241,21 @@ def attn_prefill(q, k, v, out=None, prep: HeadPrep | None = None, pos0: int = 0,
     return out
 
 
+def _past(past, B):
+    if past is None:
+        return None
+    if past.dtype != torch.int32 or past.dim() != 1 or past.shape[0] != B or not past.is_contiguous():
+        raise TypeError("past must be a contiguous int32 [B] device tensor")
+    return _ptr(past)
+
+
 def attn_prefill_chunk(q, k_new, v_new, k_cache, v_cache, n_past: int, out=None,
                        prep: HeadPrep | None = None, causal: bool = True, scale: float | None = None,
-                       stream=None) -> torch.Tensor:
+                       stream=None, past=None) -> torch.Tensor:
     """A chunk q [B, tq, Hq, D] against caches [B, capacity, Hkv, D] holding n_past rows:
-    appends prep(k_new) and v_new at rows n_past .., then attends rows 0 .. n_past + tq - 1."""
+    appends prep(k_new) and v_new at rows n_past .., then attends rows 0 .. n_past + tq - 1.
+    With ``past`` (int32 [B] on the device) sequence b holds past[b] rows instead, and
+    n_past is the bound on every past[b]."""
     lib = load_library()
     B, tq, hq, D = q.shape
     cap, hkv = k_cache.shape[1], k_cache.shape[2]
@@ -260,7 +270,7 @@ def attn_prefill_chunk(q, k_new, v_new, k_cache, v_cache, n_past: int, out=None,
         scale = 1.0 / math.sqrt(D)
     st = prep.struct() if prep is not None else None
     _check(lib.attn_prefill_chunk(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out),
-                                  B, tq, hq, hkv, D, cap, n_past,
+                                  B, tq, hq, hkv, D, cap, n_past, _past(past, B),
                                   ctypes.byref(st) if st is not None else None, int(bool(causal)),
                                   float(scale), _dtype_code(q), _stream(stream)))
     return out
@@ -268,7 +278,7 @@ def attn_prefill_chunk(q, k_new, v_new, k_cache, v_cache, n_past: int, out=None,
 
 def attn_prefill_chunk_paged(q, k_new, v_new, k_pool, v_pool, pages, n_past: int, out=None,
                              prep: HeadPrep | None = None, causal: bool = True, scale: float | None = None,
-                             stream=None) -> torch.Tensor:
+                             stream=None, past=None) -> torch.Tensor:
     """attn_prefill_chunk with the cache in a paged pool k_pool, v_pool [num_pages, page_rows,
     Hkv, D]; pages [B, max_pages] int32 maps each sequence's rows to pages."""
     lib = load_library()
@@ -288,7 +298,7 @@ def attn_prefill_chunk_paged(q, k_new, v_new, k_pool, v_pool, pages, n_past: int
     st = prep.struct() if prep is not None else None
     _check(lib.attn_prefill_chunk_paged(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(out),
                                         B, tq, hq, hkv, D, num_pages, page_rows, _ptr(pages), pages.shape[1], n_past,
-                                        ctypes.byref(st) if st is not None else None, int(bool(causal)),
+                                        _past(past, B), ctypes.byref(st) if st is not None else None, int(bool(causal)),
                                         float(scale), _dtype_code(q), _stream(stream)))
     return out
 

@@ -31,6 +31,10 @@ PEAK_SOURCES = ["peak.hip"]
 EXTRA = {"prefill_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"], "kvq.hip": ["-ffp-contract=off"],
          "rows8.hip": ["-ffp-contract=off"]}
 ARCH = "gfx950"
+# Kernels whose tile waits count their own loads into LDS (vmcnt) and so must not spill
+# registers: scratch traffic would count too.  The build fails if one of them spills.
+NO_SPILL = {"prefill_bf16.hip": ("prefill_bf16_kernel",), "decode.hip": ("decode_rows_kernel",)}
+RESOURCE_REPORT = os.path.join(BUILD_DIR, "resource_usage.txt")
 
 
 def hipcc() -> str:
@@ -48,11 +52,47 @@ def _flags():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + _flags() + EXTRA.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    report = ["-Rpass-analysis=kernel-resource-usage"] if src in NO_SPILL else []
+    cmd = [hipcc()] + _flags() + EXTRA.get(src, []) + report + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed on %s:\n%s" % (src, r.stderr))
+    if report:
+        _resources[src] = parse_resource_usage(r.stderr)
     return obj
+
+
+_resources: dict = {}
+
+
+def parse_resource_usage(text: str):
+    """[(kernel, vgprs, vgpr_spill, sgpr_spill)] from the compiler's resource remarks."""
+    rows, cur = [], None
+    for line in text.splitlines():
+        if "remark:" not in line:
+            continue
+        body = line.split("remark:", 1)[1].strip()
+        if body.startswith("Function Name:"):
+            cur = [body.split(":", 1)[1].split(" [")[0].strip(), None, None, None]
+            rows.append(cur)
+        elif cur is not None:
+            for key, i in (("VGPRs:", 1), ("VGPRs Spill:", 2), ("SGPRs Spill:", 3)):
+                if body.startswith(key):
+                    cur[i] = int(body.split(":", 1)[1].split()[0])
+    return [tuple(r) for r in rows]
+
+
+def _check_spills() -> None:
+    lines, bad = [], []
+    for src, rows in sorted(_resources.items()):
+        for name, vgprs, vspill, sspill in rows:
+            lines.append("%s %s vgprs=%s vgpr_spill=%s sgpr_spill=%s" % (src, name, vgprs, vspill, sspill))
+            if any(k in name for k in NO_SPILL[src]) and vspill:
+                bad.append("%s: %d VGPRs spilled" % (name, vspill))
+    with open(RESOURCE_REPORT, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if bad:
+        raise RuntimeError("kernels that must not spill registers do:\n" + "\n".join(bad))
 
 
 def _link(objs, out: str) -> None:
@@ -70,6 +110,7 @@ def build(jobs: int = 8) -> str:
     srcs = SOURCES + PEAK_SOURCES
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
         objs = list(ex.map(_compile, srcs))
+    _check_spills()
     _link(objs[:len(SOURCES)], OUT)
     _link(objs[len(SOURCES):], PEAK_OUT)
     return OUT

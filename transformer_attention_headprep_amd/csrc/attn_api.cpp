@@ -346,8 +346,9 @@ attn_status_t attn_prefill(const void *q, void *k, const void *v, void *out, int
 
 static attn_status_t chunk_impl(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                                 void *out, int64_t batch, int64_t tq, int64_t hq, int64_t hkv, int64_t d,
-                                int64_t capacity, const Paging *pg, int64_t n_past, const attn_headprep_t *prep,
-                                int causal, double scale, attn_dtype_t dtype, void *stream) {
+                                int64_t capacity, const Paging *pg, int64_t n_past, const int32_t *past,
+                                const attn_headprep_t *prep, int causal, double scale, attn_dtype_t dtype,
+                                void *stream) {
     g_last_error[0] = 0;
     attn_status_t st = check_dtype_d(dtype, d);
     if (st) return st;
@@ -395,6 +396,11 @@ static attn_status_t chunk_impl(const void *q, const void *k_new, const void *v_
         return fail(ATTN_ERR_ARG, "the page table overlaps a pool");
     if (overlap(skc, svc) || overlap(skn, skc) || overlap(skn, svc) || overlap(svn, skc) || overlap(svn, svc))
         return fail(ATTN_ERR_ARG, "the caches overlap each other or the new rows");
+    if (past) {
+        const Span sp{reinterpret_cast<uintptr_t>(past), reinterpret_cast<uintptr_t>(past + batch)};
+        if (overlap(sp, so) || overlap(sp, skc) || overlap(sp, svc))
+            return fail(ATTN_ERR_ARG, "past overlaps out or a cache");
+    }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf16 = dtype == ATTN_BF16;
     const int64_t crs = hkv * d, cbs = pg ? 0 : capacity * crs;    // cache row and sequence strides
@@ -405,19 +411,23 @@ static attn_status_t chunk_impl(const void *q, const void *k_new, const void *v_
     }
 
     // 1-2. Append: prepped keys and values into cache rows n_past .. n_past + tq - 1 (of
-    // each sequence's pages, with a pool).
+    // each sequence's pages, with a pool); with per-sequence lengths, rows past[b] .. of
+    // sequence b (the kernels offset each sequence themselves).
+    const int64_t host_row0 = past ? 0 : n_past;
     attn::CopyRowsLaunch cv{};
     cv.src = v_new;
-    cv.dst = pg ? v_cache : static_cast<uint8_t *>(v_cache) + (size_t)(n_past * crs) * es;
+    cv.dst = pg ? v_cache : static_cast<uint8_t *>(v_cache) + (size_t)(host_row0 * crs) * es;
     cv.src_bs = tq * crs; cv.src_rs = crs; cv.dst_bs = cbs; cv.dst_rs = crs;
     cv.batch = batch; cv.rows = tq; cv.row_elems = crs; cv.elem = (int64_t)es;
-    cv.dst_pages = pm; cv.dst_row0 = n_past;
-    void *k_dst = pg ? k_cache : static_cast<uint8_t *>(k_cache) + (size_t)(n_past * crs) * es;
+    cv.dst_pages = pm; cv.dst_row0 = host_row0;
+    cv.past = past; cv.past_max = n_past;
+    void *k_dst = pg ? k_cache : static_cast<uint8_t *>(k_cache) + (size_t)(host_row0 * crs) * es;
     if (prep_k) {
         attn::PrepLaunch pk{};
         pk.k_src = k_new; pk.k_dst = k_dst; pk.k_src_rs = crs; pk.k_dst_rs = crs; pk.hkv = hkv;
         pk.k_src_bs = tq * crs; pk.k_dst_bs = cbs;              // (unused with a pool)
-        pk.k_pages = pm; pk.k_row0 = n_past;
+        pk.k_pages = pm; pk.k_row0 = host_row0;
+        pk.past = past; pk.past_max = n_past;
         pk.batch = batch; pk.seq = tq; pk.d = d; pk.pos0 = n_past;
         pk.qw = prep->qw; pk.kw = prep->kw; pk.cos = prep->cos; pk.sin = prep->sin;
         pk.half = prep->half; pk.pairs = prep->pairs != 0; pk.eps = (float)prep->eps; pk.bf16 = bf16;
@@ -437,6 +447,7 @@ static attn_status_t chunk_impl(const void *q, const void *k_new, const void *v_
     a.kv_pages = pm;
     a.batch = batch; a.seq = tq; a.tk = n_past + tq; a.hq = hq; a.hkv = hkv; a.d = d; a.pos0 = n_past;
     a.causal = causal != 0; a.scale = (float)scale; a.bf16 = bf16;
+    a.past = past;
     if (prep) {
         if (!prep->pairs && attn::prefill_fuses_half(d, prep->half, bf16)) {
             a.prep_q = true;
@@ -447,6 +458,7 @@ static attn_status_t chunk_impl(const void *q, const void *k_new, const void *v_
             attn::PrepLaunch pq{};
             pq.q_src = q; pq.q_dst = out; pq.q_src_rs = hq * d; pq.q_dst_rs = hq * d; pq.hq = hq;
             pq.batch = batch; pq.seq = tq; pq.d = d; pq.pos0 = n_past;
+            pq.past = past; pq.past_max = n_past;
             pq.qw = prep->qw; pq.cos = prep->cos; pq.sin = prep->sin;
             pq.half = prep->half; pq.pairs = prep->pairs != 0; pq.eps = (float)prep->eps; pq.bf16 = bf16;
             if ((st = hip_status(attn::launch_prep(pq, s), "attn_prefill_chunk (q prep)"))) return st;
@@ -458,20 +470,22 @@ static attn_status_t chunk_impl(const void *q, const void *k_new, const void *v_
 
 attn_status_t attn_prefill_chunk(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                                  void *out, int64_t batch, int64_t tq, int64_t hq, int64_t hkv, int64_t d,
-                                 int64_t capacity, int64_t n_past, const attn_headprep_t *prep, int causal,
-                                 double scale, attn_dtype_t dtype, void *stream) {
-    return chunk_impl(q, k_new, v_new, k_cache, v_cache, out, batch, tq, hq, hkv, d, capacity, nullptr, n_past, prep,
-                      causal, scale, dtype, stream);
+                                 int64_t capacity, int64_t n_past, const int32_t *past,
+                                 const attn_headprep_t *prep, int causal, double scale, attn_dtype_t dtype,
+                                 void *stream) {
+    return chunk_impl(q, k_new, v_new, k_cache, v_cache, out, batch, tq, hq, hkv, d, capacity, nullptr, n_past, past,
+                      prep, causal, scale, dtype, stream);
 }
 
 attn_status_t attn_prefill_chunk_paged(const void *q, const void *k_new, const void *v_new, void *k_pool,
                                        void *v_pool, void *out, int64_t batch, int64_t tq, int64_t hq, int64_t hkv,
                                        int64_t d, int64_t num_pages, int64_t page_rows, const int32_t *pages,
-                                       int64_t max_pages, int64_t n_past, const attn_headprep_t *prep, int causal,
-                                       double scale, attn_dtype_t dtype, void *stream) {
+                                       int64_t max_pages, int64_t n_past, const int32_t *past,
+                                       const attn_headprep_t *prep, int causal, double scale, attn_dtype_t dtype,
+                                       void *stream) {
     const Paging pg{pages, page_rows, max_pages, num_pages};
-    return chunk_impl(q, k_new, v_new, k_pool, v_pool, out, batch, tq, hq, hkv, d, 0, &pg, n_past, prep, causal, scale,
-                      dtype, stream);
+    return chunk_impl(q, k_new, v_new, k_pool, v_pool, out, batch, tq, hq, hkv, d, 0, &pg, n_past, past, prep, causal,
+                      scale, dtype, stream);
 }
 
 attn_status_t attn_rows(void *qkv, int64_t n, int64_t heads, int64_t head, int64_t group, int64_t queries, void *out,

@@ -30,6 +30,11 @@ struct PrepLaunch {
     // outside the pool is not written.
     PageMap k_pages;
     int64_t k_row0;
+    // past != NULL (device int32 [batch]): sequence b's rows sit at positions past[b] + t
+    // (its table row, and its key's cache or pool row, k_dst not offset by the host);
+    // past[b] outside [0, past_max] leaves sequence b's key rows unwritten.
+    const int32_t *past;
+    int64_t past_max;
 };
 hipError_t launch_prep(const PrepLaunch &a, hipStream_t stream);
 
@@ -55,6 +60,10 @@ struct PrefillLaunch {
     bool causal;
     float scale;
     bool bf16;
+    // past != NULL (device int32 [batch], chunk mode): sequence b's query rows sit at
+    // positions past[b] + i over its keys 0 .. past[b] + seq - 1; pos0 (= tk - seq) is
+    // the host bound on every past[b], and one outside [0, pos0] gives NaN rows.
+    const int32_t *past;
 };
 hipError_t launch_prefill(const PrefillLaunch &a, hipStream_t stream);
 // true if the fused q prologue of the chosen kernel can turn pairs `half` apart.
@@ -84,6 +93,10 @@ struct CopyRowsLaunch {
     int64_t batch, rows, row_elems, elem;
     PageMap dst_pages;           // pages != NULL: row t of sequence b goes to pool row
     int64_t dst_row0;            // pool_row(dst_pages, b, dst_row0 + t); bad ids: not written
+    // past != NULL: row t of sequence b goes to its row past[b] + t (dst not offset by
+    // the host); past[b] outside [0, past_max]: not written.
+    const int32_t *past;
+    int64_t past_max;
 };
 hipError_t launch_copy_rows(const CopyRowsLaunch &a, hipStream_t stream);
 

@@ -100,6 +100,7 @@ struct PPArgs {
     int64_t q_bs, k_bs, v_bs, o_bs;
     int q_rs, k_rs, v_rs, o_rs;
     PageMap kv_pages;  // pages != NULL: k and v are paged pools (a 64-key tile lies in one page)
+    const int32_t *past;  // != NULL: per-sequence cache lengths (PrefillLaunch::past)
     int tq, tk, half, pos0;
     float eps, scale, kmax;
     // items (see launch_bf16_d)
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);   // 0..7
     const int grp = w >> 2, wg = w & 3;
     const int n = lane % 32, g = lane / 32;
-    const int tq = p.tq, tk = p.tk, qoff = tk - tq;
+    const int tq = p.tq;
     const float C = p.scale * kLog2e;
     const float sc = PREP ? 1.0f : C;
 
@@ -254,6 +255,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int pair = pl * p.xcds + list;
         const int b = pair / p.hkv;
         const int kvh = pair - b * p.hkv;
+        // the sequence's keys: query i sits at key position qoff + i = tk - tq + i; with
+        // per-sequence lengths tk = past[b] + tq (past[b] read as 0, and the rows NaN,
+        // when it lies outside [0, pos0]).  Only tk stays live: the rest is derived.
+        const int pv = p.past ? p.past[b] : 0;
+        const bool bad_seq = (unsigned)pv > (unsigned)p.pos0;
+        const int tk = __builtin_amdgcn_readfirstlane(p.past ? (bad_seq ? 0 : pv) + tq : p.tk);
+        const int qoff = tk - tq;
         // this group's slot (q head, query tile); the block's key extent covers both slots
         int h, qtile, qt_last;
         if (p.mode == 0) {
@@ -276,8 +284,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const bool paged = p.kv_pages.pages != nullptr;
         const uint16_t *src = (loads_k ? p.k : p.v) + (paged ? 0 : (int64_t)b * (loads_k ? p.k_bs : p.v_bs)) +
                               (int64_t)kvh * D;
-        bool bad_page = false;            // a page id outside the pool was met (every wave
-                                          // looks up the page of every tile it loads)
+        bool bad_page = bad_seq;          // a page id outside the pool was met (every wave
+                                          // looks up the page of every tile it loads), or
+                                          // the sequence's past[b] is out of range
         auto load_tile = [&](int kt, unsigned char *dst) __attribute__((always_inline)) {
             const int key0 = kt * kBN;
             __amdgpu_buffer_rsrc_t rsrc;
@@ -309,8 +318,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if constexpr (PREP) {
                 const int hc = p.half / 16;
                 const int64_t tbytes = (int64_t)wrows * p.half * 4;
-                const __amdgpu_buffer_rsrc_t crs = seq_rsrc(p.cos + (int64_t)(p.pos0 + row0w) * p.half, hc > 0 ? tbytes : 0);
-                const __amdgpu_buffer_rsrc_t srs = seq_rsrc(p.sin + (int64_t)(p.pos0 + row0w) * p.half, hc > 0 ? tbytes : 0);
+                // table row of query row i: pos0 + i, or past[b] + i
+                const int first = p.past ? qoff : p.pos0;
+                const __amdgpu_buffer_rsrc_t crs = seq_rsrc(p.cos + (int64_t)(first + row0w) * p.half, hc > 0 ? tbytes : 0);
+                const __amdgpu_buffer_rsrc_t srs = seq_rsrc(p.sin + (int64_t)(first + row0w) * p.half, hc > 0 ? tbytes : 0);
                 const int toff = (n * p.half + 8 * g) * 4;
                 float ss = 0.f;
 #pragma unroll
@@ -526,7 +537,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (t < ntiles && visible(t)) g1(kcur);
             __builtin_amdgcn_s_setprio(0);
             if (!loads_k) wait_older(t + 1 < ntiles);      // V_t in LDS (V_{t+1} may fly)
-            lds_barrier();
+            __syncthreads();
             // Both groups issue their loads as their softmax step starts, so each block
             // phase carries one group's load issue and no matrix step carries any.
             if (t + 2 < ntiles) load_tile(t + 2, loads_k ? knext2 : vnext2);
@@ -536,13 +547,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int t = 0;; t += 3) {
             period(t, kb0, kb2, vb2, vb2);
             if (t == ntiles) break;
-            lds_barrier();
+            __syncthreads();
             period(t + 1, kb1, kb0, vb0, vb0);
             if (t + 1 == ntiles) break;
-            lds_barrier();
+            __syncthreads();
             period(t + 2, kb2, kb1, vb1, vb1);
             if (t + 2 == ntiles) break;
-            lds_barrier();
+            __syncthreads();
         }
 
         // ---- epilogue (in the softmax step of period ntiles): divide by the row sum,
@@ -597,6 +608,7 @@ hipError_t launch_bf16_d(const PrefillLaunch &a, hipStream_t stream) {
     p.q_bs = a.q_bs; p.k_bs = a.k_bs; p.v_bs = a.v_bs; p.o_bs = a.o_bs;
     p.q_rs = (int)a.q_rs; p.k_rs = (int)a.k_rs; p.v_rs = (int)a.v_rs; p.o_rs = (int)a.o_rs;
     p.kv_pages = a.kv_pages;
+    p.past = a.past;
     p.tq = (int)a.seq; p.tk = (int)a.tk; p.half = (int)a.half; p.pos0 = (int)a.pos0;
     p.eps = a.eps; p.scale = a.scale; p.kmax = a.kmax;
     p.mode = group % 2 == 0 ? 0 : 1;

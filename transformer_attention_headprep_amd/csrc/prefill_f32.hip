@@ -27,7 +27,17 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(const PrefillLaunch 
     const int qtile = gridDim.x - 1 - blockIdx.x;         // longest causal rows first
     const int64_t r = (int64_t)qtile * kRows + threadIdx.x;
     const bool row_ok = r < p.seq;
-    const int64_t tk = p.tk, qoff = p.tk - p.seq;          // query r sits at key position r + qoff
+    // query r sits at key position r + qoff and table row first + r; with per-sequence
+    // lengths, at past[b] + r over keys 0 .. past[b] + seq - 1 (NaN rows when past[b]
+    // lies outside [0, pos0])
+    int64_t tk = p.tk, qoff = p.tk - p.seq, first = p.pos0;
+    bool bad_seq = false;
+    if (p.past) {
+        const int v = p.past[b];
+        bad_seq = v < 0 || v > p.pos0;
+        qoff = first = bad_seq ? 0 : v;
+        tk = qoff + p.seq;
+    }
     const int g = h / (p.hq / p.hkv);
     const float *qbase = static_cast<const float *>(p.q) + b * p.q_bs + (row_ok ? r : 0) * p.q_rs + h * D;
 
@@ -45,8 +55,8 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(const PrefillLaunch 
 #pragma unroll
         for (int e = 0; e < D; ++e) q[e] = q[e] * inv * p.qw[e];
         if (p.half > 0 && row_ok) {   // half = D/2 (other halves are prepped beforehand)
-            const float *cr = p.cos + (p.pos0 + r) * (D / 2);
-            const float *sr = p.sin + (p.pos0 + r) * (D / 2);
+            const float *cr = p.cos + (first + r) * (D / 2);
+            const float *sr = p.sin + (first + r) * (D / 2);
 #pragma unroll
             for (int e = 0; e < D / 2; ++e) {
                 const float a = q[e], bb = q[e + D / 2];
@@ -125,7 +135,7 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(const PrefillLaunch 
         }
     }
     if (row_ok) {
-        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        const float inv = bad_seq ? __builtin_nanf("") : (l > 0.f ? 1.0f / l : 0.f);
         float *ob = static_cast<float *>(p.out) + b * p.o_bs + r * p.o_rs + h * D;
 #pragma unroll
         for (int e = 0; e < D; e += 4)

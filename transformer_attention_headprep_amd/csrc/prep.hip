@@ -31,6 +31,8 @@ struct PrepParams {
     float eps;
     PageMap k_pages;            // pages != NULL: k rows go to pool rows (see PrepLaunch)
     int64_t k_row0;
+    const int32_t *past;        // per-sequence positions (see PrepLaunch)
+    int64_t past_max;
 };
 
 // Turn the adjacent pairs (e, e + 1), e even, of 4 values starting at e0 (a multiple of
@@ -86,28 +88,46 @@ struct PrepUnit {
 
     __device__ __forceinline__ void locate(const PrepParams &p, int64_t unit) {
         valid = unit < p.n_units;
-        int64_t row;
-        if (unit < p.n_q_units) {
+        int64_t row, bb;
+        const bool is_q = unit < p.n_q_units;
+        if (is_q) {
             const int64_t u = valid ? unit : 0;
             row = u / p.hq;
-            const int64_t h = u % p.hq, bb = row / p.seq, t = row % p.seq;
+            bb = row / p.seq;
+        } else {
+            const int64_t u = valid ? unit - p.n_q_units : 0;
+            row = u / p.hkv;
+            bb = row / p.seq;
+        }
+        // the sequence's first position: pos0, or its own past[b] (0 when out of range,
+        // and then its key rows are not written)
+        int64_t first = p.pos0, krow0 = p.k_row0;
+        bool seq_ok = true;
+        if (p.past) {
+            const int v = p.past[bb];
+            seq_ok = v >= 0 && v <= p.past_max;
+            first = seq_ok ? v : 0;
+            krow0 = first;
+        }
+        const int64_t t = row % p.seq;
+        if (is_q) {
+            const int64_t h = (valid ? unit : 0) % p.hq;
             src = p.q_src; dst = p.q_dst; w = p.qw;
             src_off = bb * p.q_src_bs + t * p.q_src_rs + h * D;
             dst_off = bb * p.q_dst_bs + t * p.q_dst_rs + h * D;
         } else {
-            const int64_t u = valid ? unit - p.n_q_units : 0;
-            row = u / p.hkv;
-            const int64_t h = u % p.hkv, bb = row / p.seq, t = row % p.seq;
+            const int64_t h = (valid ? unit - p.n_q_units : 0) % p.hkv;
             src = p.k_src; dst = p.k_dst; w = p.kw;
             src_off = bb * p.k_src_bs + t * p.k_src_rs + h * D;
-            dst_off = bb * p.k_dst_bs + t * p.k_dst_rs + h * D;
+            dst_off = bb * p.k_dst_bs + ((p.past ? krow0 : 0) + t) * p.k_dst_rs + h * D;
             if (p.k_pages.pages && valid) {
                 bool bad = false;
-                const int64_t prow = pool_row(p.k_pages, (int)bb, p.k_row0 + t, bad);
+                const int64_t prow = pool_row(p.k_pages, (int)bb, krow0 + t, bad);
                 dst_off = bad ? -1 : prow * p.k_dst_rs + h * D;
             }
+            if (!seq_ok) dst_off = -1;
         }
-        posrow = p.pos0 + row % p.seq;
+        posrow = first + t;
     }
 
     // The weights, (split halves, half = D/2) the lane's table entries and the values,
@@ -240,16 +260,24 @@ hipError_t launch_prep_d(const PrepParams &p, int mode, hipStream_t stream) {
 __global__ __launch_bounds__(256) void copy_rows_kernel(const uint8_t *src, uint8_t *dst, int64_t src_bs,
                                                         int64_t src_rs, int64_t dst_bs, int64_t dst_rs,
                                                         int64_t rows, int64_t row_bytes, int64_t total16,
-                                                        const PageMap pages, int64_t row0) {
+                                                        const PageMap pages, int64_t row0, const int32_t *past,
+                                                        int64_t past_max) {
     const int64_t per_row = row_bytes / 16;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total16; i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t rr = i / per_row, c = i % per_row;
         const int64_t bb = rr / rows, t = rr % rows;
+        int64_t r0 = row0, doff0 = 0;
+        if (past) {                         // the sequence's own first row
+            const int v = past[bb];
+            if (v < 0 || v > past_max) continue;
+            r0 = v;
+            doff0 = v;
+        }
         const uint4 v = *reinterpret_cast<const uint4 *>(src + bb * src_bs + t * src_rs + 16 * c);
-        int64_t doff = bb * dst_bs + t * dst_rs;
+        int64_t doff = bb * dst_bs + (doff0 + t) * dst_rs;
         if (pages.pages) {
             bool bad = false;
-            const int64_t prow = pool_row(pages, (int)bb, row0 + t, bad);
+            const int64_t prow = pool_row(pages, (int)bb, r0 + t, bad);
             if (bad) continue;
             doff = prow * dst_rs;
         }
@@ -357,7 +385,7 @@ hipError_t launch_copy_rows(const CopyRowsLaunch &a, hipStream_t stream) {
     hipLaunchKernelGGL(copy_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const uint8_t *>(a.src), static_cast<uint8_t *>(a.dst), a.src_bs * a.elem,
                        a.src_rs * a.elem, a.dst_bs * a.elem, a.dst_rs * a.elem, a.rows, row_bytes, total16,
-                       a.dst_pages, a.dst_row0);
+                       a.dst_pages, a.dst_row0, a.past, a.past_max);
     return hipGetLastError();
 }
 
@@ -380,6 +408,8 @@ hipError_t launch_prep(const PrepLaunch &a, hipStream_t stream) {
     p.eps = a.eps;
     p.k_pages = a.k_pages;
     p.k_row0 = a.k_row0;
+    p.past = a.past;
+    p.past_max = a.past_max;
     const int mode = a.half == 0 ? 0 : (a.pairs ? 3 : (2 * a.half == a.d ? 1 : 2));
     if (a.d == 64)
         return a.bf16 ? launch_prep_d<true, 64>(p, mode, stream) : launch_prep_d<false, 64>(p, mode, stream);

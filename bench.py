@@ -243,6 +243,10 @@ def main() -> int:
             fn()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
         torch.cuda.synchronize()
+        # The calls are queued behind a spin kernel (about 150 us a call), so each pair of
+        # events times one call's GPU work, not the host marshalling of its arguments
+        # (which can take longer than a short call runs).
+        torch.cuda._sleep(int(calls * 150e-6 * 2.1e9))
         for a, b in evs:
             a.record(stream)
             fn()

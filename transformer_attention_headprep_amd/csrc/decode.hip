@@ -873,11 +873,13 @@ int64_t decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t ma
 }
 
 int64_t decode_q_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len, int64_t kbits) {
-    // A chunk of coded rows carries 2 (8 bits) to 4 (4 and 2 bits) times fewer bytes than a
-    // bf16 one, so more blocks are needed to keep as many bytes in flight.
+    // About one round of blocks: two are resident per CU (the kernel's registers), and a
+    // second round pays the q prologue again (measured: 8/8, 4/4 and 4/2 all fastest or
+    // within a few percent of it at two blocks a CU).
+    (void)kbits;
     const int64_t gb = decode_heads_per_block(hq, hkv);
     const int64_t units = batch * hkv * ((hq / hkv + gb - 1) / gb);
-    const int64_t blocks = (kbits == 8 ? 2 : 4) * kCUs;
+    const int64_t blocks = 2 * kCUs;
     int64_t splits = (blocks + units - 1) / units;
     const int64_t most = (max_len + 255) / 256;
     if (splits > most) splits = most;

@@ -16,7 +16,9 @@
 //   params [batch, heads, capacity, 2] f32 (lo, step).
 //
 // The decode (decode_q_kernel) is decode_bf16_kernel's design with the cache rows
-// turned into bf16 matrix-core operands on their way to LDS:
+// turned into bf16 matrix-core operands as they arrive (keys straight from registers:
+// lane (n, kk) loads row n's codes of dims kk D/4 .., the A fragments of its products, and
+// q's fragments take the same dims; values through LDS for the transposing reads):
 //   - 8 bits: a code c becomes the bf16 c (exact: integers below 256 have 8 bits);
 //   - 4 and 2 bits: a pair of codes becomes the bf16 pair 128 + c (0x4300 | c, one
 //     mask-and-or per pair), i.e. an offset M = 128 that is taken out again below.
@@ -221,6 +223,16 @@ __device__ __forceinline__ void stage_codes(unsigned char *buf, const uint32_t (
     }
 }
 
+// Lane (lane & ~3) + i's value: the i-th of the lane's quad (DPP quad permute).
+__device__ __forceinline__ uint32_t quad_lane(uint32_t v, int i) {
+    switch (i) {
+        case 0: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xF, 0xF, false);
+        case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xF, 0xF, false);
+        case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xAA, 0xF, 0xF, false);
+        default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xFF, 0xF, 0xF, false);
+    }
+}
+
 template <int D, int GB, int KB, int VB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 4 ? 4 : 3))) void decode_q_kernel(const DecodeParams p) {
     typedef DecGeo<D> G;
@@ -262,10 +274,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
     const int nch = end > first ? (end - first + kChunk * kWaves - 1) / (kChunk * kWaves) : 0;
     const int n = lane % 16, kk = lane / 16;
 
+    // A chunk in registers: the lane's code words and the (lo, step) pairs of key
+    // 4 kk + n % 4 (the other keys of the lane's four come from its quad, by DPP).
+    // Key codes: lane (n, kk) holds row n's codes of dims kk D/4 .. (kk+1) D/4 - 1, the A
+    // fragments of its kKMfma products straight from registers (q's fragments take the
+    // same dims); values go through LDS for the transposing reads.
+    constexpr int kKW = D * KB / 128;          // words of key codes per lane (D/4 codes)
     struct Regs {
-        uint32_t k[GK::kNL][GK::kWords];
+        uint32_t k[kKW];
         uint32_t v[GV::kNL][GV::kWords];
-        u32x4 kp[2], vp[2];          // (lo, step) of keys 4 kk .. 4 kk + 3
+        uint32_t kp[2], vp[2];
     };
     // Chunk j: descriptors end at the last valid row (rows past it read as zeros).
     // A chunk's 16 rows lie in one unit (pages hold a multiple of 16 rows).
@@ -277,17 +295,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
         const __amdgpu_buffer_rsrc_t vr = seq_rsrc(static_cast<const uint8_t *>(p.v) + cr * GV::kRB, (int64_t)rows * GV::kRB);
         const __amdgpu_buffer_rsrc_t kpr = seq_rsrc(p.kpar + cr * 2, (int64_t)rows * 8);
         const __amdgpu_buffer_rsrc_t vpr = seq_rsrc(p.vpar + cr * 2, (int64_t)rows * 8);
-#pragma unroll
-        for (int i = 0; i < GK::kNL; ++i) load_words<GK::kLB>(r.k[i], kr, (64 * i + lane) * GK::kLB);
+        {
+            const int ko = n * GK::kRB + kk * (GK::kRB / 4);
+            if constexpr (kKW == 8) {
+                load_words<16>(r.k, kr, ko);
+                load_words<16>(r.k + 4, kr, ko + 16);
+            } else {
+                load_words<kKW * 4>(r.k, kr, ko);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < GV::kNL; ++i) load_words<GV::kLB>(r.v[i], vr, (64 * i + lane) * GV::kLB);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            r.kp[i] = __builtin_amdgcn_raw_buffer_load_b128(kpr, 32 * kk + 16 * i, 0, 0);
-            r.vp[i] = __builtin_amdgcn_raw_buffer_load_b128(vpr, 32 * kk + 16 * i, 0, 0);
-        }
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const int pofs = 8 * (4 * kk + n % 4);
+        const u32x2 kp2 = __builtin_amdgcn_raw_buffer_load_b64(kpr, pofs, 0, 0);
+        const u32x2 vp2 = __builtin_amdgcn_raw_buffer_load_b64(vpr, pofs, 0, 0);
+        r.kp[0] = kp2[0]; r.kp[1] = kp2[1];
+        r.vp[0] = vp2[0]; r.vp[1] = vp2[1];
     };
 
+    // Two chunks in registers: one in flight while the other is computed (a third costs
+    // more in register moves than it saves in waiting, measured).
     Regs ra, rb;
     issue(0, ra);
 
@@ -303,7 +331,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
         for (int c = 0; c < G::kKMfma; ++c) {
             u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
             if (n < nh) {
-                const float *src = &qh[n][32 * c + 8 * kk];
+                const float *src = &qh[n][kk * (D / 4) + 8 * c];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float a = src[2 * e], b2 = src[2 * e + 1];
@@ -338,22 +366,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
 
     auto compute = [&](int j, const Regs &r) {
         const int key0 = first + kChunk * kWaves * j;
-        stage_codes<D, KB, true>(kbuf, r.k, lane);
         stage_codes<D, VB, false>(vbuf, r.v, lane);
+        // the key operands: pairs of codes as bf16 M + c, 8 codes (4 pairs) a product
+        uint32_t kpairs[D / 8];
+#pragma unroll
+        for (int wd = 0; wd < kKW; ++wd) word_pairs<KB>(r.k[wd], kpairs + wd * (16 / KB));
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < G::kKMfma; ++c) {
-            const bf16x8 kc = *reinterpret_cast<const bf16x8 *>(kbuf + n * G::kRow + 16 * kslot<D>(n, 4 * c + kk));
+            const u32x4 k4 = {kpairs[4 * c], kpairs[4 * c + 1], kpairs[4 * c + 2], kpairs[4 * c + 3]};
+            const bf16x8 kc = __builtin_bit_cast(bf16x8, k4);
             s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, __builtin_bit_cast(bf16x8, qf[64 * (2 * c) + lane]), s, 0, 0, 0);
             s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, __builtin_bit_cast(bf16x8, qf[64 * (2 * c + 1) + lane]), s, 0, 0, 0);
         }
         // The keys' ranges: score = step q.u + (lo - M step) sq.
-        const float kpv[8] = {__uint_as_float(r.kp[0][0]), __uint_as_float(r.kp[0][1]), __uint_as_float(r.kp[0][2]),
-                              __uint_as_float(r.kp[0][3]), __uint_as_float(r.kp[1][0]), __uint_as_float(r.kp[1][1]),
-                              __uint_as_float(r.kp[1][2]), __uint_as_float(r.kp[1][3])};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float klo = kpv[2 * i], kst = kpv[2 * i + 1];
+            const float klo = __uint_as_float(quad_lane(r.kp[0], i)), kst = __uint_as_float(quad_lane(r.kp[1], i));
             s[i] = fmaf(kst, s[i], (klo - (float)GK::kM * kst) * sq);
         }
         if (key0 + kChunk > end) {
@@ -374,14 +403,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
             m_run = m_new;
             thr = (m_run + kRaiseAbove) / p.C;
         }
-        const float vpv[8] = {__uint_as_float(r.vp[0][0]), __uint_as_float(r.vp[0][1]), __uint_as_float(r.vp[0][2]),
-                              __uint_as_float(r.vp[0][3]), __uint_as_float(r.vp[1][0]), __uint_as_float(r.vp[1][1]),
-                              __uint_as_float(r.vp[1][2]), __uint_as_float(r.vp[1][3])};
         float pr[4], ps[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             pr[i] = fast_exp2(fmaf(s[i], p.C, -m_run));
-            const float vlo = vpv[2 * i], vst = vpv[2 * i + 1];
+            const float vlo = __uint_as_float(quad_lane(r.vp[0], i)), vst = __uint_as_float(quad_lane(r.vp[1], i));
             ps[i] = pr[i] * vst;
             b_lane = fmaf(pr[i], vlo - (float)GV::kM * vst, b_lane);
         }

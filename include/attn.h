@@ -90,6 +90,9 @@ typedef enum attn_status {
  *               tracking a running maximum: the same softmax, in fewer instructions
  *               per key tile.  Rows whose shift would exceed 48 (in log2 units) keep
  *               the running maximum.  An understated kmax can overflow the weights.
+ *               The bound derived from kw assumes cos and sin tables that turn: cos^2 +
+ *               sin^2 <= 1 at every entry (up to f32 rounding); with other tables give
+ *               kmax = 0 or a bound of your own.
  *               Other entry points ignore it.
  *               A zero-initialised record is the split-halves HeadPrep with no bound.
  */

@@ -27,14 +27,13 @@
 //   phase 2t   : A: S(t) = K_t Q^T ; O += P(t-1) V_{t-1}     B: P(t-1) = exp(S(t-1))
 //   phase 2t+1 : A: P(t) = exp(S(t))                        B: S(t), O += P(t-1) V_{t-1}
 //
-// K and V tiles move HBM -> LDS by buffer loads that write LDS directly, in rings of two
-// buffers each: at phase 2t the block issues K_{t+1} (into the buffer K_{t-1} left, last
-// read in phase 2t-1) and V_t (into the buffer of V_{t-2}, last read in phase 2t-1);
-// both are waited for at the end of phase 2t+1, one phase before their first reader.
-// Group A's waves load K, group B's load V.  Row pitches are padded (K by 16 bytes, V
-// by 64) so the 16-byte K fragment reads and the transposing V reads are free of bank
-// conflicts with immediate offsets.  A tile's buffer descriptor ends with the sequence:
-// keys past it read as zeros.
+// K and V tiles move HBM -> LDS by buffer loads that write LDS directly, in rings of
+// three buffers each (tile t in buffer t mod 3).  Group A's waves load K, group B's load
+// V, each as its softmax phase starts (tile t + 2 then), so the loads never hold up a
+// matrix phase; each tile has about a period and a half to arrive (see the tile steps
+// below).  Row pitches are padded (K by 16 bytes, V by 64) so the 16-byte K fragment
+// reads and the transposing V reads are free of bank conflicts with immediate offsets.
+// A tile's buffer descriptor ends with the sequence: keys past it read as zeros.
 //
 // Work order: blocks are persistent (one per CU) and walk a static list.  When the
 // (batch, kv head) pairs divide over the 8 XCDs, each pair's items go to the blocks of
@@ -43,17 +42,19 @@
 // blocks in a snake (block j takes items j, 2n-1-j, 2n+j, ... of n blocks), which evens
 // the causal work per block.
 //
-// Online softmax in base-2 units, as the single-group kernel: a prepped q is multiplied
-// by scale log2 e before its bf16 rounding, and every S^T accumulation starts from -m,
-// so the weights are a bare v_exp_f32 of the accumulator; with a bound on every key
-// row's norm (the caller's kmax, or sqrt(D) max|kw| when the call prepped k) the shift
-// m is fixed per row from the start (Cauchy-Schwarz: no score of row n exceeds |q_n| kb)
-// and no running maximum is kept; otherwise the running maximum moves only when a tile
-// exceeds it by more than 8 (weights below 256, exact in f32 sums and bf16).  The row
-// sum adds the bf16-rounded weights the P V product uses.
+// Online softmax in base-2 units: a prepped q is multiplied by scale log2 e before its
+// bf16 rounding, so a score accumulator is already in base 2.  With a bound on every key
+// row's norm (the caller's kmax, or sqrt(D) max|kw| when the call prepped k) and every
+// row's bound |q_n| kb at most 48 (Cauchy-Schwarz: no score of row n exceeds it), the
+// weights are bare exponentials of the accumulators and no maximum is kept; otherwise
+// the running maximum moves only when a tile exceeds it by more than 8 (weights below
+// 256, exact in f32 sums and bf16).  The row sum adds the f32 weights (the P V product
+// takes their bf16 roundings).
 //
 // q's HeadPrep (RMS, qw, split-half turn at the row's position, scale log2 e) runs in
 // each wave's prologue in registers; it needs half = 0 or a multiple of 16.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -233,6 +234,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const float kw_bound = __builtin_sqrtf((float)D) * max_lanes<64>(a) * (1.0f + 1.0f / 128);
             kbnd = kbnd > 0.f ? fminf(kbnd, kw_bound) : kw_bound;
         }
+        // (the same in every lane; read from one so the compiler knows it is uniform and
+        // keeps the branches that depend on it scalar)
+        kbnd = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, kbnd)));
     }
     __syncthreads();
 
@@ -492,14 +496,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // needed (any common factor cancels between the weighted sum and the row sum),
             // one exponential a weight.  Otherwise exp2(s sc - m sc), one fused multiply-add
             // more (the shift is 0 until the first visible key, when every weight is 0).
+            // (two copies of the loop, so the choice is one branch, not a select per weight)
             const float msc = m_run == -INFINITY ? 0.f : m_run * sc;
+            auto weights = [&](auto bare) __attribute__((always_inline)) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 float e8[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const float x = s[u / 2][8 * (u % 2) + i];
-                    e8[i] = fast_exp2(fixed ? x : __builtin_fmaf(x, sc, -msc));
+                    e8[i] = fast_exp2(decltype(bare)::value ? x : __builtin_fmaf(x, sc, -msc));
                 }
                 uint4 pk;
                 pk.x = pack_bf16x2(e8[0], e8[1]);
@@ -513,6 +519,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 l_run += ((e8[0] + e8[1]) + (e8[2] + e8[3])) + ((e8[4] + e8[5]) + (e8[6] + e8[7]));
                 pf[u] = __builtin_bit_cast(bf16x8, pk);
             }
+            };
+            if (fixed)
+                weights(std::true_type());
+            else
+                weights(std::false_type());
         };
 
         // ======== tile steps.  Every wave runs, per tile period t = 0 .. ntiles, a

@@ -118,13 +118,14 @@ struct PPArgs {
 };
 
 // q's HeadPrep for one lane: raw holds the lane's NC chunks of 8 bf16 values of its row
-// (chunk c = d 16c + 8g ..); chunk c < HC turns with chunk c + HC (half = 16 HC), from
-// 2 HC on the values pass through.  Each pair of chunks is finished (weight, turn, the
+// (chunk c = d 16c + 8g ..); chunk c < HC turns with chunk c + HC (half = 16 HC) by the
+// row's cos/sin (cv, sv: chunk c's 8 values, loaded by the caller), from 2 HC on the
+// values pass through.  Each pair of chunks is finished (weight, turn, the
 // row's factor f = scale log2 e / rms, bf16) before the next one's weights are read, so
 // no whole-row f32 copy is held.
 template <int NC, int HC>
-__device__ __forceinline__ void pp_prep_q(const u32x4 (&raw)[NC], const float *qw_lds, __amdgpu_buffer_rsrc_t crs,
-                                          __amdgpu_buffer_rsrc_t srs, int toff, int g, float f, bf16x8 (&qf)[NC]) {
+__device__ __forceinline__ void pp_prep_q(const u32x4 (&raw)[NC], const float *qw_lds, const f32x4 (&cv)[4][2],
+                                          const f32x4 (&sv)[4][2], int g, float f, bf16x8 (&qf)[NC]) {
     auto weight = [&](int c, float (&x)[8]) __attribute__((always_inline)) {
         const f32x4 w0 = *reinterpret_cast<const f32x4 *>(qw_lds + 16 * c + 8 * g);
         const f32x4 w1 = *reinterpret_cast<const f32x4 *>(qw_lds + 16 * c + 8 * g + 4);
@@ -145,14 +146,6 @@ __device__ __forceinline__ void pp_prep_q(const u32x4 (&raw)[NC], const float *q
         return __builtin_bit_cast(bf16x8, u);
     };
     if constexpr (HC >= 1 && 2 * HC <= NC) {
-        f32x4 cv[HC][2], sv[HC][2];
-#pragma unroll
-        for (int c = 0; c < HC; ++c)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                cv[c][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, toff + 64 * c + 16 * j, 0, 0));
-                sv[c][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, toff + 64 * c + 16 * j, 0, 0));
-            }
 #pragma unroll
         for (int c = 0; c < HC; ++c) {
             float a[8], b[8];
@@ -305,10 +298,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 if (t < nloads) buffer_to_lds16(rsrc, dst + (wg + 4 * t) * 1024, voff[t]);
         };
 
-        // ======== prologue step: this group's first two tiles (A: K_0, K_1; B: V_0, V_1)
-        // and q.
-        load_tile(0, loads_k ? kb0 : vb0);
-        if (ntiles > 1) load_tile(1, loads_k ? kb1 : vb1);
+        // ======== prologue step: q and the turn's table rows (neither waits for the other,
+        // nor behind the tile loads, whose issue is slow), then this group's first two
+        // tiles (A: K_0, K_1; B: V_0, V_1), then q's HeadPrep.  Constant load offsets go
+        // in the scalar offset, so the loads share one per-lane offset.
         bf16x8 qf[NC];
         float shift = 0.f;
         {
@@ -318,15 +311,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int qoff_lane = (n * p.q_rs + 8 * g) * 2;
             u32x4 raw[NC];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) raw[c] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, qoff_lane + 32 * c, 0, 0);
+            for (int c = 0; c < NC; ++c) raw[c] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, qoff_lane, 32 * c, 0);
+            f32x4 cv[4][2], sv[4][2];
+            const int hc = PREP ? p.half / 16 : 0;
             if constexpr (PREP) {
-                const int hc = p.half / 16;
                 const int64_t tbytes = (int64_t)wrows * p.half * 4;
                 // table row of query row i: pos0 + i, or past[b] + i
                 const int first = p.past ? qoff : p.pos0;
                 const __amdgpu_buffer_rsrc_t crs = seq_rsrc(p.cos + (int64_t)(first + row0w) * p.half, hc > 0 ? tbytes : 0);
                 const __amdgpu_buffer_rsrc_t srs = seq_rsrc(p.sin + (int64_t)(first + row0w) * p.half, hc > 0 ? tbytes : 0);
                 const int toff = (n * p.half + 8 * g) * 4;
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        if (2 * c < NC && c < hc) {
+                            cv[c][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, toff, 64 * c + 16 * j, 0));
+                            sv[c][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, toff, 64 * c + 16 * j, 0));
+                        } else {
+                            cv[c][j] = f32x4{1.f, 1.f, 1.f, 1.f};
+                            sv[c][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        }
+                    }
+            }
+            load_tile(0, loads_k ? kb0 : vb0);
+            if (ntiles > 1) load_tile(1, loads_k ? kb1 : vb1);
+            if constexpr (PREP) {
                 float ss = 0.f;
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
@@ -342,11 +352,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 // scale log2 e after the turn.
                 const float f = C * __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps);
                 switch (hc) {
-                    case 1: pp_prep_q<NC, 1>(raw, qw_s, crs, srs, toff, g, f, qf); break;
-                    case 2: pp_prep_q<NC, 2>(raw, qw_s, crs, srs, toff, g, f, qf); break;
-                    case 3: pp_prep_q<NC, 3>(raw, qw_s, crs, srs, toff, g, f, qf); break;
-                    case 4: pp_prep_q<NC, NC / 2 >= 4 ? 4 : 0>(raw, qw_s, crs, srs, toff, g, f, qf); break;
-                    default: pp_prep_q<NC, 0>(raw, qw_s, crs, srs, toff, g, f, qf); break;
+                    case 1: pp_prep_q<NC, 1>(raw, qw_s, cv, sv, g, f, qf); break;
+                    case 2: pp_prep_q<NC, 2>(raw, qw_s, cv, sv, g, f, qf); break;
+                    case 3: pp_prep_q<NC, 3>(raw, qw_s, cv, sv, g, f, qf); break;
+                    case 4: pp_prep_q<NC, NC / 2 >= 4 ? 4 : 0>(raw, qw_s, cv, sv, g, f, qf); break;
+                    default: pp_prep_q<NC, 0>(raw, qw_s, cv, sv, g, f, qf); break;
                 }
                 if (kbnd > 0.f) {
                     // |q| of the bf16 values the products take; Cauchy-Schwarz bounds

@@ -250,12 +250,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int sub = rem - pl * p.nsub;
         const int lcls = p.nlen - 1 - lr;                  // longest first
         const int pair = pl * p.xcds + list;
-        const int b = pair / p.hkv;
+        const int b = __builtin_amdgcn_readfirstlane(pair / p.hkv);
         const int kvh = pair - b * p.hkv;
         // the sequence's keys: query i sits at key position qoff + i = tk - tq + i; with
         // per-sequence lengths tk = past[b] + tq (past[b] read as 0, and the rows NaN,
         // when it lies outside [0, pos0]).  Only tk stays live: the rest is derived.
-        const int pv = p.past ? p.past[b] : 0;
+        // (read through the scalar cache: past is read-only here and b is uniform, so the
+        // read waits on no vector-memory operation -- a vector load's wait would also wait
+        // for the previous item's output stores)
+        const int pv = p.past ? ((const __attribute__((address_space(4))) int32_t *)p.past)[b] : 0;
         const bool bad_seq = (unsigned)pv > (unsigned)p.pos0;
         const int tk = __builtin_amdgcn_readfirstlane(p.past ? (bad_seq ? 0 : pv) + tq : p.tk);
         const int qoff = tk - tq;

@@ -76,6 +76,41 @@ __device__ __forceinline__ float pp_lane_pair(float x, int g) {
     return __uint_as_float(g == 0 ? r[1] : r[0]);
 }
 
+// x unchanged, computed here: the compiler can neither hoist it out of a loop nor sink it
+// (a value kept in a vector register, pp_pin_v, or a scalar one, pp_pin_s).
+__device__ __forceinline__ int pp_pin_v(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+__device__ __forceinline__ int pp_pin_s(int x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
+// 16 bytes per lane from a buffer straight into LDS (lane L writes lds + 16 L), at
+// per-lane offset voff plus the wave-uniform soff.
+__device__ __forceinline__ void pp_to_lds16(__amdgpu_buffer_rsrc_t rsrc, void *lds, int voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}
+
+// Wait until at most k (0 .. 10) vector-memory operations of this wave are in flight
+// (k is wave-uniform; the count is an immediate, hence the cases).
+__device__ __forceinline__ void wait_vmcnt_upto(int k) {
+    switch (k) {
+        case 10: ATTN_WAIT_VMCNT(10); break;
+        case 9: ATTN_WAIT_VMCNT(9); break;
+        case 8: ATTN_WAIT_VMCNT(8); break;
+        case 7: ATTN_WAIT_VMCNT(7); break;
+        case 6: ATTN_WAIT_VMCNT(6); break;
+        case 5: ATTN_WAIT_VMCNT(5); break;
+        case 4: ATTN_WAIT_VMCNT(4); break;
+        case 3: ATTN_WAIT_VMCNT(3); break;
+        case 2: ATTN_WAIT_VMCNT(2); break;
+        case 1: ATTN_WAIT_VMCNT(1); break;
+        default: ATTN_WAIT_VMCNT(0); break;
+    }
+}
+
 template <int D>
 struct PPGeo {
     static constexpr int kRow = 2 * D;
@@ -183,6 +218,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ __attribute__((aligned(16))) unsigned char vb1[G::kVBytes];
     __shared__ __attribute__((aligned(16))) unsigned char vb2[G::kVBytes];
     __shared__ __attribute__((aligned(16))) float qw_s[D];
+    // Rotary table staging of the prologue (see the prologue step): per wave, 32 rows of
+    // cos then 32 of sin, each row KC 16-byte slots.  Waves 0, 1 of a group use tst, waves
+    // 2, 3 the third K and V ring buffers.
+    constexpr int KC = D / 8;                     // 16-byte chunks per q row
+    constexpr int RPI = 64 / KC;                  // table rows per 64-lane load
+    constexpr int NT = 32 / RPI;                  // loads per table
+    constexpr int NV = KC / RPI > 1 ? KC / RPI : 1;   // swizzle patterns over the loads
+    constexpr int kTab = 32 * KC * 16;            // bytes per staged table
+    static_assert(2 * kTab <= G::kKBytes && 2 * kTab <= G::kVBytes, "table staging fits a ring buffer");
+    __shared__ __attribute__((aligned(16))) unsigned char tst[2][2 * kTab];
     constexpr int NC = D / 16;
     constexpr int NDB = D / 32;
 
@@ -208,6 +253,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int col = sidx - row * (loads_k ? G::kKSlots : G::kVSlots);
         voff[t] = (row * lrs + 8 * min(col, G::kChunks - 1)) * 2;
     }
+
+    // Table staging: load i of a table fills slots 64 i .. 64 i + 63 (row r = slot / KC,
+    // slot s = slot % KC), and slot s of row r holds the row's chunk s ^ (r mod KC), so the
+    // fragment reads below (16 lanes: 16 rows, one chunk) hit 16 distinct slots.  A slot
+    // whose chunk lies past a row of half < D / 2 floats holds bytes of the next row: it is
+    // never read.  (The per-lane offsets are made per item, in the prologue: kept for the
+    // whole kernel they would hold registers through the tile loop.)
+    unsigned char *const tslot = wg < 2 ? tst[wg] : (wg == 2 ? kb2 : vb2);
 
     // Per-lane LDS byte offsets of the fragment reads.
     const int k_lane = n * G::kKStride + 16 * g;
@@ -301,10 +354,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 if (t < nloads) buffer_to_lds16(rsrc, dst + (wg + 4 * t) * 1024, voff[t]);
         };
 
-        // ======== prologue step: q and the turn's table rows (neither waits for the other,
-        // nor behind the tile loads, whose issue is slow), then this group's first two
-        // tiles (A: K_0, K_1; B: V_0, V_1), then q's HeadPrep.  Constant load offsets go
-        // in the scalar offset, so the loads share one per-lane offset.
+        // ======== prologue step: q, then the turn's table rows, then this group's first
+        // two tiles (A: K_0, K_1; B: V_0, V_1), then q's HeadPrep.  q comes in the fragment
+        // layout (each load reads 32 rows).  The tables (32 consecutive rows of each) come
+        // as whole-row loads straight into LDS, staged as set out above, and are read back
+        // in the fragment layout: loads that each touch 32 rows were the prologue's slowest
+        // part.  The staging slots are free here: the third ring buffers are next filled
+        // in softmax step 0, and the two groups' prologues lie on either side of a
+        // barrier.  Constant load offsets go in the scalar offset.
         bf16x8 qf[NC];
         float shift = 0.f;
         {
@@ -315,27 +372,29 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             u32x4 raw[NC];
 #pragma unroll
             for (int c = 0; c < NC; ++c) raw[c] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, qoff_lane, 32 * c, 0);
-            f32x4 cv[4][2], sv[4][2];
             const int hc = PREP ? p.half / 16 : 0;
             if constexpr (PREP) {
+                // (issued even without a turn, hc = 0: the loads then read nothing and
+                // fill the slots with zeros, and the count of loads in flight stays fixed)
                 const int64_t tbytes = (int64_t)wrows * p.half * 4;
                 // table row of query row i: pos0 + i, or past[b] + i
                 const int first = p.past ? qoff : p.pos0;
-                const __amdgpu_buffer_rsrc_t crs = seq_rsrc(p.cos + (int64_t)(first + row0w) * p.half, hc > 0 ? tbytes : 0);
-                const __amdgpu_buffer_rsrc_t srs = seq_rsrc(p.sin + (int64_t)(first + row0w) * p.half, hc > 0 ? tbytes : 0);
-                const int toff = (n * p.half + 8 * g) * 4;
+                const __amdgpu_buffer_rsrc_t crs = seq_rsrc(p.cos + (int64_t)(first + row0w) * p.half, tbytes);
+                const __amdgpu_buffer_rsrc_t srs = seq_rsrc(p.sin + (int64_t)(first + row0w) * p.half, tbytes);
+                // per-lane offsets, one per pattern (load i uses pattern i mod NV), and the
+                // bytes per load (scalar), pinned here so they are not kept across the loop
+                const int rb = pp_pin_s(RPI * p.half * 4);
+                int tvoff[NV];
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
+                for (int k = 0; k < NV; ++k) {
+                    tvoff[k] = pp_pin_v((lane / KC) * (rb / RPI) + (((lane % KC) ^ ((k * RPI + lane / KC) % KC)) * 16));
+                }
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        if (2 * c < NC && c < hc) {
-                            cv[c][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, toff, 64 * c + 16 * j, 0));
-                            sv[c][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(srs, toff, 64 * c + 16 * j, 0));
-                        } else {
-                            cv[c][j] = f32x4{1.f, 1.f, 1.f, 1.f};
-                            sv[c][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        }
-                    }
+                for (int i = 0; i < NT; ++i)
+                    pp_to_lds16(crs, tslot + 1024 * i, tvoff[i % NV], i * rb);
+#pragma unroll
+                for (int i = 0; i < NT; ++i)
+                    pp_to_lds16(srs, tslot + kTab + 1024 * i, tvoff[i % NV], i * rb);
             }
             load_tile(0, loads_k ? kb0 : vb0);
             if (ntiles > 1) load_tile(1, loads_k ? kb1 : vb1);
@@ -354,6 +413,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 // RMS, weight and turn are linear: one multiply by the row's 1 / rms and
                 // scale log2 e after the turn.
                 const float f = C * __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps);
+                // The staged tables: wait for their loads (only the tile loads issued
+                // after them may still fly), then read the lane's chunks 4c + 2g + j.
+                f32x4 cv[4][2], sv[4][2];
+                wait_vmcnt_upto(nloads * (ntiles > 1 ? 2 : 1));
+                const int tsw = pp_pin_v(n % KC);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        if (2 * c < NC && c < hc) {
+                            const int at = (n * KC + ((4 * c + 2 * g + j) ^ tsw)) * 16;
+                            cv[c][j] = *reinterpret_cast<const f32x4 *>(tslot + at);
+                            sv[c][j] = *reinterpret_cast<const f32x4 *>(tslot + kTab + at);
+                        } else {
+                            cv[c][j] = f32x4{1.f, 1.f, 1.f, 1.f};
+                            sv[c][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        }
+                    }
                 switch (hc) {
                     case 1: pp_prep_q<NC, 1>(raw, qw_s, cv, sv, g, f, qf); break;
                     case 2: pp_prep_q<NC, 2>(raw, qw_s, cv, sv, g, f, qf); break;

@@ -286,9 +286,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __syncthreads();
 
-    // Group B runs one step behind group A for the whole kernel: one barrier here, and
-    // group A takes one more at the end.
-    if (grp == 1) __syncthreads();
+    // Group B runs one step behind group A inside each item's tile loop.  When the two
+    // groups' slots share their query rows (mode 0) the groups run their prologues side
+    // by side: B takes one barrier more after its prologue, A one more after its
+    // epilogue.  Otherwise B stays one step behind across items too: one barrier here,
+    // and A takes one more at the end.
+    const bool together = p.mode == 0;
+    if (grp == 1 && !together) __syncthreads();
 
     // ---- the block's items: a snake over its list.
     const int list = (int)blockIdx.x % p.xcds;
@@ -360,8 +364,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // as whole-row loads straight into LDS, staged as set out above, and are read back
         // in the fragment layout: loads that each touch 32 rows were the prologue's slowest
         // part.  The staging slots are free here: the third ring buffers are next filled
-        // in softmax step 0, and the two groups' prologues lie on either side of a
-        // barrier.  Constant load offsets go in the scalar offset.
+        // in softmax step 0, and the two groups' prologues either lie on either side of a
+        // barrier or (mode 0) stage the same rows, so that their writes to a slot agree.
+        // Constant load offsets go in the scalar offset.
         bf16x8 qf[NC];
         float shift = 0.f;
         {
@@ -468,6 +473,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+        if (grp == 1 && together) __syncthreads();       // B: past A's matrix step 0
         if (loads_k) __builtin_amdgcn_s_waitcnt(0);         // K_0, K_1 in LDS before A's first read
         __syncthreads();
         // Wait until at most this wave's latest batch of tile loads (nloads, or none when
@@ -620,9 +626,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // matrix step (P(t-1) V_{t-1}, then S(t): the weights free their registers
         // before the K fragments take theirs), a barrier, a softmax step (P(t); the
         // epilogue at t = ntiles), a barrier.  Group B runs one step behind A, so B's
-        // matrix step runs beside A's softmax step and the other way round:
-        //   A: prologue  M0  S0  M1  S1 ...  MT  epilogue | next prologue ...
-        //   B:    ...    prologue M0  S0  M1 ...  ST-1  MT  epilogue | ...
+        // matrix step runs beside A's softmax step and the other way round (phases
+        // between barriers; mode 0, prologues side by side):
+        //   A: prologue | M0 | S0 | ... | MT   | epilogue | prologue           | M0 | S0 ...
+        //   B: prologue |    | M0 | ... | ST-1 | MT       | epilogue, prologue |    | M0 ...
+        // (other modes, prologues one after the other:
+        //   A: prologue | M0       | S0 | ... | MT   | epilogue | prologue | M0       ...
+        //   B:          | prologue | M0 | ... | ST-1 | MT       | epilogue | prologue ...)
         // Tiles live in rings of three LDS buffers (tile t in buffer t mod 3).  A issues
         // K_{t+2} as its softmax step t starts (the buffer held K_{t-1}, whose last
         // reader, B's matrix step t-1, ended two barriers before) and, at the end of that
@@ -678,9 +688,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     *reinterpret_cast<uint2 *>(orow + 32 * db + 8 * i + 4 * g) = u;
                 }
         }
-        __syncthreads();
+        if (grp == 0 || !together) __syncthreads();
     }
-    if (grp == 0) __syncthreads();
+    if (grp == 0 && !together) __syncthreads();
 }
 
 int cu_count() {

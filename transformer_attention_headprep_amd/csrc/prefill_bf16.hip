@@ -288,9 +288,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     // Group B runs one step behind group A inside each item's tile loop.  When the two
     // groups' slots share their query rows (mode 0) the groups run their prologues side
-    // by side: B takes one barrier more after its prologue, A one more after its
-    // epilogue.  Otherwise B stays one step behind across items too: one barrier here,
-    // and A takes one more at the end.
+    // by side: B takes one barrier more after its prologue and skips the one between its
+    // last matrix step and its epilogue.  Otherwise B stays one step behind across items
+    // too: one barrier here, and A takes one more at the end.
     const bool together = p.mode == 0;
     if (grp == 1 && !together) __syncthreads();
 
@@ -394,12 +394,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 for (int k = 0; k < NV; ++k) {
                     tvoff[k] = pp_pin_v((lane / KC) * (rb / RPI) + (((lane % KC) ^ ((k * RPI + lane / KC) % KC)) * 16));
                 }
+                // (whole offsets per lane: the range check covers the per-lane offset)
 #pragma unroll
                 for (int i = 0; i < NT; ++i)
-                    pp_to_lds16(crs, tslot + 1024 * i, tvoff[i % NV], i * rb);
+                    pp_to_lds16(crs, tslot + 1024 * i, tvoff[i % NV] + i * rb, 0);
 #pragma unroll
                 for (int i = 0; i < NT; ++i)
-                    pp_to_lds16(srs, tslot + kTab + 1024 * i, tvoff[i % NV], i * rb);
+                    pp_to_lds16(srs, tslot + kTab + 1024 * i, tvoff[i % NV] + i * rb, 0);
             }
             load_tile(0, loads_k ? kb0 : vb0);
             if (ntiles > 1) load_tile(1, loads_k ? kb1 : vb1);
@@ -628,8 +629,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // epilogue at t = ntiles), a barrier.  Group B runs one step behind A, so B's
         // matrix step runs beside A's softmax step and the other way round (phases
         // between barriers; mode 0, prologues side by side):
-        //   A: prologue | M0 | S0 | ... | MT   | epilogue | prologue           | M0 | S0 ...
-        //   B: prologue |    | M0 | ... | ST-1 | MT       | epilogue, prologue |    | M0 ...
+        //   A: prologue | M0 | S0 | ... | MT   | epilogue     | prologue | M0 | S0 ...
+        //   B: prologue |    | M0 | ... | ST-1 | MT, epilogue | prologue |    | M0 ...
         // (other modes, prologues one after the other:
         //   A: prologue | M0       | S0 | ... | MT   | epilogue | prologue | M0       ...
         //   B:          | prologue | M0 | ... | ST-1 | MT       | epilogue | prologue ...)
@@ -648,7 +649,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (t < ntiles && visible(t)) g1(kcur);
             __builtin_amdgcn_s_setprio(0);
             if (!loads_k) wait_older(t + 1 < ntiles);      // V_t in LDS (V_{t+1} may fly)
-            __syncthreads();
+            if (!(t == ntiles && grp == 1 && together)) __syncthreads();
             // Both groups issue their loads as their softmax step starts, so each block
             // phase carries one group's load issue and no matrix step carries any.
             if (t + 2 < ntiles) load_tile(t + 2, loads_k ? knext2 : vnext2);
@@ -667,15 +668,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             __syncthreads();
         }
 
-        // ---- epilogue (in the softmax step of period ntiles): divide by the row sum,
-        // round once to bf16, store.
-        const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-        if (rrow < tq) {
+        // ---- epilogue (in the softmax step of period ntiles, or for B in mode 0 right
+        // after its last matrix step): divide by the row sum, round once to bf16, store.
+        // The wave's 32 x D output tile goes through LDS (chunk c of row r at slot
+        // c ^ (r mod KC), as the tables), so that each store writes whole rows (a store of
+        // the fragment layout touches 32 rows).  Staging: A in tst (no table is staged
+        // until the next prologue), B in the K ring (mode 0: no matrix step reads K from
+        // the last one on) or the V ring (other modes: the epilogue lies between B's last
+        // matrix step and its next prologue); two waves a buffer.  Rows past the query
+        // tail fall outside the store's range and are dropped.
+        {
+            const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
             const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
             // A bad page: quiet-NaN bf16 bits (set as integers: this file is built without
             // NaN semantics).
             const uint32_t nan_mask = bad_page ? 0xFFFFFFFFu : 0u;
-            uint16_t *orow = p.out + (int64_t)b * p.o_bs + (int64_t)rrow * p.o_rs + (int64_t)h * D;
+            unsigned char *const est = (grp == 0 ? tst[wg >> 1] : together ? ((wg >> 1) ? kb1 : kb0) : ((wg >> 1) ? vb1 : vb0)) +
+                                       (wg & 1) * kTab;
+            const int esw = pp_pin_v(n % KC);          // (made here, not kept across the loop)
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -685,10 +695,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     u.y = pack_bf16x2(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
                     u.x = (u.x & ~nan_mask) | (0x7FC07FC0u & nan_mask);
                     u.y = (u.y & ~nan_mask) | (0x7FC07FC0u & nan_mask);
-                    *reinterpret_cast<uint2 *>(orow + 32 * db + 8 * i + 4 * g) = u;
+                    // columns 32 db + 8 i + 4 g .. + 3 of row n: chunk 4 db + i, half g
+                    *reinterpret_cast<uint2 *>(est + n * (2 * D) + (((4 * db + i) ^ esw) * 16) + 8 * g) = u;
                 }
+            const __amdgpu_buffer_rsrc_t ors =
+                seq_rsrc(p.out + (int64_t)b * p.o_bs + (int64_t)row0w * p.o_rs + (int64_t)h * D,
+                         wrows > 0 ? ((int64_t)(wrows - 1) * p.o_rs + D) * 2 : 0);
+            // (the whole offset per lane, scalar offset 0: the range check then sees it, and
+            // the compiler keeps the wait a store of more than 8 bytes needs before its data
+            // registers are written again -- it drops that wait for a register scalar offset)
+            const int rl = pp_pin_v(lane / KC), cl = pp_pin_v(lane % KC);
+#pragma unroll
+            for (int k = 0; k < NT; ++k) {
+                const int r = k * RPI + rl;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(est + r * (2 * D) + ((cl ^ (r % KC)) * 16));
+                __builtin_amdgcn_raw_buffer_store_b128(v, ors, (r * p.o_rs + 8 * cl) * 2, 0, 0);
+            }
         }
-        if (grp == 0 || !together) __syncthreads();
+        __syncthreads();
     }
     if (grp == 0 && !together) __syncthreads();
 }

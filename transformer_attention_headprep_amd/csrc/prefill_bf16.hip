@@ -642,31 +642,42 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // held V_{t-1}, last read by B's matrix step t, a barrier before) and, at the end
         // of its matrix step t+1, waits for V_{t+1}, which A's matrix step t+2 reads
         // next.  So each tile has about a period and a half to arrive.
-        auto period = [&](int t, const unsigned char *kcur, unsigned char *knext2, const unsigned char *vprev,
-                          unsigned char *vnext2) __attribute__((always_inline)) {
+        auto mstep = [&](int t, const unsigned char *kcur, const unsigned char *vprev) __attribute__((always_inline)) {
             __builtin_amdgcn_s_setprio(1);
             if (t >= 1 && visible(t - 1)) g2(vprev);
             if (t < ntiles && visible(t)) g1(kcur);
             __builtin_amdgcn_s_setprio(0);
             if (!loads_k) wait_older(t + 1 < ntiles);      // V_t in LDS (V_{t+1} may fly)
-            if (!(t == ntiles && grp == 1 && together)) __syncthreads();
+        };
+        auto sstep = [&](int t, unsigned char *knext2, unsigned char *vnext2) __attribute__((always_inline)) {
             // Both groups issue their loads as their softmax step starts, so each block
             // phase carries one group's load issue and no matrix step carries any.
             if (t + 2 < ntiles) load_tile(t + 2, loads_k ? knext2 : vnext2);
             if (t < ntiles && visible(t)) sm(t);
             if (loads_k) wait_older(t + 2 < ntiles);       // K_{t+1} in LDS (K_{t+2} may fly)
         };
+        // (periods 0 .. ntiles - 1 here; the matrix step of period ntiles ends the loop)
         for (int t = 0;; t += 3) {
-            period(t, kb0, kb2, vb2, vb2);
+            mstep(t, kb0, vb2);
             if (t == ntiles) break;
             __syncthreads();
-            period(t + 1, kb1, kb0, vb0, vb0);
+            sstep(t, kb2, vb2);
+            __syncthreads();
+            mstep(t + 1, kb1, vb0);
             if (t + 1 == ntiles) break;
             __syncthreads();
-            period(t + 2, kb2, kb1, vb1, vb1);
+            sstep(t + 1, kb0, vb0);
+            __syncthreads();
+            mstep(t + 2, kb2, vb1);
             if (t + 2 == ntiles) break;
             __syncthreads();
+            sstep(t + 2, kb1, vb1);
+            __syncthreads();
         }
+        // The softmax step of period ntiles holds no tile work: A waits for its last
+        // loads, and the epilogue follows (for B in mode 0 without a barrier).
+        if (!(grp == 1 && together)) __syncthreads();
+        if (loads_k) __builtin_amdgcn_s_waitcnt(0);
 
         // ---- epilogue (in the softmax step of period ntiles, or for B in mode 0 right
         // after its last matrix step): divide by the row sum, round once to bf16, store.

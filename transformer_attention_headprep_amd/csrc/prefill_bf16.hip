@@ -394,13 +394,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 for (int k = 0; k < NV; ++k) {
                     tvoff[k] = pp_pin_v((lane / KC) * (rb / RPI) + (((lane % KC) ^ ((k * RPI + lane / KC) % KC)) * 16));
                 }
-                // (whole offsets per lane: the range check covers the per-lane offset)
+                // (whole offsets per lane: the range check covers the per-lane offset).  With
+                // prologues side by side the two groups' waves wg stage the same rows: A
+                // loads cos, B sin, and a barrier below publishes both.
+                if (!together || grp == 0) {
 #pragma unroll
-                for (int i = 0; i < NT; ++i)
-                    pp_to_lds16(crs, tslot + 1024 * i, tvoff[i % NV] + i * rb, 0);
+                    for (int i = 0; i < NT; ++i)
+                        pp_to_lds16(crs, tslot + 1024 * i, tvoff[i % NV] + i * rb, 0);
+                }
+                if (!together || grp == 1) {
 #pragma unroll
-                for (int i = 0; i < NT; ++i)
-                    pp_to_lds16(srs, tslot + kTab + 1024 * i, tvoff[i % NV] + i * rb, 0);
+                    for (int i = 0; i < NT; ++i)
+                        pp_to_lds16(srs, tslot + kTab + 1024 * i, tvoff[i % NV] + i * rb, 0);
+                }
             }
             load_tile(0, loads_k ? kb0 : vb0);
             if (ntiles > 1) load_tile(1, loads_k ? kb1 : vb1);
@@ -420,9 +426,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 // scale log2 e after the turn.
                 const float f = C * __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps);
                 // The staged tables: wait for their loads (only the tile loads issued
-                // after them may still fly), then read the lane's chunks 4c + 2g + j.
+                // after them may still fly; with prologues side by side, a barrier then
+                // publishes the other group's half), then read the lane's chunks 4c + 2g + j.
                 f32x4 cv[4][2], sv[4][2];
                 wait_vmcnt_upto(nloads * (ntiles > 1 ? 2 : 1));
+                if (together) lds_barrier();
                 const int tsw = pp_pin_v(n % KC);
 #pragma unroll
                 for (int c = 0; c < 4; ++c)

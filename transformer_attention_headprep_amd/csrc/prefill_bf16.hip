@@ -294,21 +294,61 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool together = p.mode == 0;
     if (grp == 1 && !together) __syncthreads();
 
-    // ---- the block's items: a snake over its list.
+    // ---- the block's items: a snake over its list.  Item r's place in the list, its
+    // length class (longest first), its slot index within the pair and its pair.
     const int list = (int)blockIdx.x % p.xcds;
     const int jb = (int)blockIdx.x / p.xcds;
-    for (int r = 0;; ++r) {
-        const int idx = r * p.nbx + ((r & 1) ? p.nbx - 1 - jb : jb);
-        if (idx >= p.items_x) break;
+    struct Item {
+        int idx, lcls, sub, b, kvh;
+    };
+    auto item_at = [&](int r) __attribute__((always_inline)) {
+        Item it;
+        it.idx = r * p.nbx + ((r & 1) ? p.nbx - 1 - jb : jb);
         const int per_len = p.ppx * p.nsub;
-        const int lr = idx / per_len;
-        const int rem = idx - lr * per_len;
+        const int lr = it.idx / per_len;
+        const int rem = it.idx - lr * per_len;
         const int pl = rem / p.nsub;
-        const int sub = rem - pl * p.nsub;
-        const int lcls = p.nlen - 1 - lr;                  // longest first
+        it.sub = rem - pl * p.nsub;
+        it.lcls = p.nlen - 1 - lr;
         const int pair = pl * p.xcds + list;
-        const int b = __builtin_amdgcn_readfirstlane(pair / p.hkv);
-        const int kvh = pair - b * p.hkv;
+        it.b = __builtin_amdgcn_readfirstlane(pair / p.hkv);
+        it.kvh = pair - it.b * p.hkv;
+        return it;
+    };
+    // This group's slot of an item: its q head, its query tile and the block's last one.
+    auto slot_of = [&](const Item &it, int &h, int &qtile, int &qt_last) __attribute__((always_inline)) {
+        if (p.mode == 0) {
+            h = it.kvh * p.group + 2 * it.sub + grp;
+            qtile = it.lcls;
+            qt_last = it.lcls;
+        } else {
+            h = it.kvh * p.group + it.sub;
+            qtile = 2 * it.lcls + grp;
+            qt_last = 2 * it.lcls + 1;
+        }
+    };
+    // The wave's 32 q rows of an item in the fragment layout (each load reads 32 rows);
+    // rows past the query tail read as zeros.  Issued for the next item before this
+    // item's output stores, so the prologue does not wait behind them.
+    u32x4 raw[NC];
+    auto load_q = [&](const Item &it) __attribute__((always_inline)) {
+        int h, qtile, qt_last;
+        slot_of(it, h, qtile, qt_last);
+        const int row0w = qtile * kBM + 32 * wg;
+        const int wrows = max(0, min(32, tq - row0w));
+        const __amdgpu_buffer_rsrc_t qsrc =
+            seq_rsrc(p.q + (int64_t)it.b * p.q_bs + (int64_t)row0w * p.q_rs + (int64_t)h * D,
+                     wrows > 0 ? ((int64_t)(wrows - 1) * p.q_rs + D) * 2 : 0);
+        const int qoff_lane = (n * p.q_rs + 8 * g) * 2;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) raw[c] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, qoff_lane, 32 * c, 0);
+    };
+    Item cur = item_at(0);
+    if (cur.idx < p.items_x) load_q(cur);
+    for (int r = 0;; ++r) {
+        if (cur.idx >= p.items_x) break;
+        const int b = cur.b;
+        const int kvh = cur.kvh;
         // the sequence's keys: query i sits at key position qoff + i = tk - tq + i; with
         // per-sequence lengths tk = past[b] + tq (past[b] read as 0, and the rows NaN,
         // when it lies outside [0, pos0]).  Only tk stays live: the rest is derived.
@@ -321,15 +361,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int qoff = tk - tq;
         // this group's slot (q head, query tile); the block's key extent covers both slots
         int h, qtile, qt_last;
-        if (p.mode == 0) {
-            h = kvh * p.group + 2 * sub + grp;
-            qtile = lcls;
-            qt_last = lcls;
-        } else {
-            h = kvh * p.group + sub;
-            qtile = 2 * lcls + grp;
-            qt_last = 2 * lcls + 1;
-        }
+        slot_of(cur, h, qtile, qt_last);
         const int blk_last = CAUSAL ? min(tk - 1, qt_last * kBM + kBM - 1 + qoff) : tk - 1;
         const int ntiles = blk_last / kBN + 1;              // block-uniform
 
@@ -370,13 +402,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         bf16x8 qf[NC];
         float shift = 0.f;
         {
-            const __amdgpu_buffer_rsrc_t qsrc =
-                seq_rsrc(p.q + (int64_t)b * p.q_bs + (int64_t)row0w * p.q_rs + (int64_t)h * D,
-                         wrows > 0 ? ((int64_t)(wrows - 1) * p.q_rs + D) * 2 : 0);
-            const int qoff_lane = (n * p.q_rs + 8 * g) * 2;
-            u32x4 raw[NC];
-#pragma unroll
-            for (int c = 0; c < NC; ++c) raw[c] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, qoff_lane, 32 * c, 0);
             const int hc = PREP ? p.half / 16 : 0;
             if constexpr (PREP) {
                 // (issued even without a turn, hc = 0: the loads then read nothing and
@@ -686,6 +711,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // loads, and the epilogue follows (for B in mode 0 without a barrier).
         if (!(grp == 1 && together)) __syncthreads();
         if (loads_k) __builtin_amdgcn_s_waitcnt(0);
+        const Item nxt = item_at(r + 1);
+        if (nxt.idx < p.items_x) load_q(nxt);
 
         // ---- epilogue (in the softmax step of period ntiles, or for B in mode 0 right
         // after its last matrix step): divide by the row sum, round once to bf16, store.
@@ -732,6 +759,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             }
         }
         __syncthreads();
+        cur = nxt;
     }
     if (grp == 0 && !together) __syncthreads();
 }

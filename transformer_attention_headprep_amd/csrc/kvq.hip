@@ -184,7 +184,7 @@ __device__ __forceinline__ void load_words(uint32_t *w, __amdgpu_buffer_rsrc_t r
 // The bf16 operand pairs of word w (32 / BITS consecutive codes): pair i holds codes
 // 2i and 2i + 1 as bf16 values M + c.
 template <int BITS>
-__device__ __forceinline__ void word_pairs(uint32_t w, uint32_t *out) {
+__device__ __forceinline__ void word_pairs(uint32_t w, uint32_t *out, uint32_t bias = 0x43004300u) {
     if constexpr (BITS == 8) {
         // j = 0, 1 at bytes 0, 2; j = 2, 3 at bytes 1, 3.  Integers below 256 are exact
         // in bf16: the high half of their f32.
@@ -195,14 +195,15 @@ __device__ __forceinline__ void word_pairs(uint32_t w, uint32_t *out) {
     } else {
         constexpr uint32_t mask = ((1u << BITS) - 1) * 0x00010001u;
 #pragma unroll
-        for (int i = 0; i < 16 / BITS; ++i) out[i] = ((w >> (BITS * i)) & mask) | 0x43004300u;
+        for (int i = 0; i < 16 / BITS; ++i) out[i] = ((w >> (BITS * i)) & mask) | bias;
     }
 }
 
 // Store a lane's loaded codes of one chunk as bf16 operands into the rows of the chunk's
 // K (IS_K) or V buffer, in the bf16 decode's swizzled layout.
 template <int D, int BITS, bool IS_K>
-__device__ __forceinline__ void stage_codes(unsigned char *buf, const uint32_t (*words)[QGeo<D, BITS>::kWords], int lane) {
+__device__ __forceinline__ void stage_codes(unsigned char *buf, const uint32_t (*words)[QGeo<D, BITS>::kWords], int lane,
+                                            uint32_t bias = 0x43004300u) {
     typedef QGeo<D, BITS> Q;
     typedef DecGeo<D> G;
 #pragma unroll
@@ -212,7 +213,7 @@ __device__ __forceinline__ void stage_codes(unsigned char *buf, const uint32_t (
         const int d0 = (o % Q::kRB) * 8 / BITS;
         uint32_t pr[Q::kCodes / 2];
 #pragma unroll
-        for (int wd = 0; wd < Q::kWords; ++wd) word_pairs<BITS>(words[i][wd], pr + wd * (16 / BITS));
+        for (int wd = 0; wd < Q::kWords; ++wd) word_pairs<BITS>(words[i][wd], pr + wd * (16 / BITS), bias);
 #pragma unroll
         for (int sl = 0; sl < Q::kCodes / 8; ++sl) {
             const int slot = d0 / 8 + sl;
@@ -221,6 +222,12 @@ __device__ __forceinline__ void stage_codes(unsigned char *buf, const uint32_t (
             *reinterpret_cast<u32x4 *>(buf + row * G::kRow + 16 * phys) = v4;
         }
     }
+}
+
+// x, held in a vector register (the compiler cannot fold it back into a literal).
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
 }
 
 // Lane (lane & ~3) + i's value: the i-th of the lane's quad (DPP quad permute).
@@ -314,10 +321,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
         r.vp[0] = vp2[0]; r.vp[1] = vp2[1];
     };
 
-    // Two chunks in registers: one in flight while the other is computed (a third costs
-    // more in register moves than it saves in waiting, measured).
-    Regs ra, rb;
+    // Four chunks in registers: two in flight while two are computed.
+    Regs ra, rb, ra2, rb2;
     issue(0, ra);
+    issue(1, rb);
 
     float (*qs)[D] = reinterpret_cast<float (*)[D]>(smem);
     float (*qh)[D] = reinterpret_cast<float (*)[D]>(smem + GB * D * 4);
@@ -364,33 +371,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
     for (int t = 0; t < G::kNT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, thr = -INFINITY, l_lane = 0.f, b_lane = 0.f;
 
-    auto compute = [&](int j, const Regs &r) {
-        const int key0 = first + kChunk * kWaves * j;
-        stage_codes<D, VB, false>(vbuf, r.v, lane);
-        // the key operands: pairs of codes as bf16 M + c, 8 codes (4 pairs) a product
-        uint32_t kpairs[D / 8];
+    // Two of this wave's chunks (j, j + 1) per step: two independent score chains, one
+    // maximum over both, and their P V products interleaved per output block.  Chunk j's
+    // values are staged in vbuf, chunk j + 1's in kbuf (keys never go through LDS here).
+    auto compute2 = [&](int j, const Regs &ra_, const Regs &rb_) {
+        const int key0a = first + kChunk * kWaves * j;
+        const int key0b = key0a + kChunk * kWaves;
+        // (the bf16 bias 128 of each code pair held in a vector register: an and-or then
+        // takes one instruction, where two literal operands would need two)
+        const uint32_t bias = in_vgpr(0x43004300u);
+        stage_codes<D, VB, false>(vbuf, ra_.v, lane, bias);
+        stage_codes<D, VB, false>(kbuf, rb_.v, lane, bias);
+        uint32_t kpa[D / 8], kpb[D / 8];
 #pragma unroll
-        for (int wd = 0; wd < kKW; ++wd) word_pairs<KB>(r.k[wd], kpairs + wd * (16 / KB));
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        for (int wd = 0; wd < kKW; ++wd) {
+            word_pairs<KB>(ra_.k[wd], kpa + wd * (16 / KB), bias);
+            word_pairs<KB>(rb_.k[wd], kpb + wd * (16 / KB), bias);
+        }
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < G::kKMfma; ++c) {
-            const u32x4 k4 = {kpairs[4 * c], kpairs[4 * c + 1], kpairs[4 * c + 2], kpairs[4 * c + 3]};
-            const bf16x8 kc = __builtin_bit_cast(bf16x8, k4);
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, __builtin_bit_cast(bf16x8, qf[64 * (2 * c) + lane]), s, 0, 0, 0);
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc, __builtin_bit_cast(bf16x8, qf[64 * (2 * c + 1) + lane]), s, 0, 0, 0);
+            const u32x4 ka4 = {kpa[4 * c], kpa[4 * c + 1], kpa[4 * c + 2], kpa[4 * c + 3]};
+            const u32x4 kb4 = {kpb[4 * c], kpb[4 * c + 1], kpb[4 * c + 2], kpb[4 * c + 3]};
+            const bf16x8 qh8 = __builtin_bit_cast(bf16x8, qf[64 * (2 * c) + lane]);
+            const bf16x8 ql8 = __builtin_bit_cast(bf16x8, qf[64 * (2 * c + 1) + lane]);
+            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka4), qh8, sa, 0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb4), qh8, sb, 0, 0, 0);
+            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka4), ql8, sa, 0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb4), ql8, sb, 0, 0, 0);
         }
         // The keys' ranges: score = step q.u + (lo - M step) sq.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float klo = __uint_as_float(quad_lane(r.kp[0], i)), kst = __uint_as_float(quad_lane(r.kp[1], i));
-            s[i] = fmaf(kst, s[i], (klo - (float)GK::kM * kst) * sq);
+            const float kla = __uint_as_float(quad_lane(ra_.kp[0], i)), ksa = __uint_as_float(quad_lane(ra_.kp[1], i));
+            const float klb = __uint_as_float(quad_lane(rb_.kp[0], i)), ksb = __uint_as_float(quad_lane(rb_.kp[1], i));
+            sa[i] = fmaf(ksa, sa[i], (kla - (float)GK::kM * ksa) * sq);
+            sb[i] = fmaf(ksb, sb[i], (klb - (float)GK::kM * ksb) * sq);
         }
-        if (key0 + kChunk > end) {
+        if (key0b + kChunk > end) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (key0 + 4 * kk + i >= end) s[i] = -INFINITY;
+            for (int i = 0; i < 4; ++i) {
+                if (key0a + 4 * kk + i >= end) sa[i] = -INFINITY;
+                if (key0b + 4 * kk + i >= end) sb[i] = -INFINITY;
+            }
         }
-        const float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        const float mx = fmaxf(fmaxf(fmaxf(sa[0], sa[1]), fmaxf(sa[2], sa[3])), fmaxf(fmaxf(sb[0], sb[1]), fmaxf(sb[2], sb[3])));
         if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {
             float mh = fmaxf(mx, __shfl_xor(mx, 16, 64));
             mh = fmaxf(mh, __shfl_xor(mh, 32, 64));
@@ -403,37 +428,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
             m_run = m_new;
             thr = (m_run + kRaiseAbove) / p.C;
         }
-        float pr[4], ps[4];
+        // weights, as bf16 high parts and remainders of p step (chunk a, then b)
+        auto weights = [&](const f32x4 &sc4, const Regs &r, i16x4 &pfh, i16x4 &pfl) __attribute__((always_inline)) {
+            float pr[4], ps[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pr[i] = fast_exp2(fmaf(s[i], p.C, -m_run));
-            const float vlo = __uint_as_float(quad_lane(r.vp[0], i)), vst = __uint_as_float(quad_lane(r.vp[1], i));
-            ps[i] = pr[i] * vst;
-            b_lane = fmaf(pr[i], vlo - (float)GV::kM * vst, b_lane);
-        }
-        l_lane += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        const uint32_t h01 = pack_bf16x2(ps[0], ps[1]), h23 = pack_bf16x2(ps[2], ps[3]);
-        float a0, a1, a2, a3;
-        unpack_bf16x2(h01, a0, a1);
-        unpack_bf16x2(h23, a2, a3);
-        const uint32_t l01 = pack_bf16x2(ps[0] - a0, ps[1] - a1), l23 = pack_bf16x2(ps[2] - a2, ps[3] - a3);
-        const i16x4 pfh = __builtin_bit_cast(i16x4, make_uint2(h01, h23));
-        const i16x4 pfl = __builtin_bit_cast(i16x4, make_uint2(l01, l23));
+            for (int i = 0; i < 4; ++i) {
+                pr[i] = fast_exp2(fmaf(sc4[i], p.C, -m_run));
+                const float vlo = __uint_as_float(quad_lane(r.vp[0], i)), vst = __uint_as_float(quad_lane(r.vp[1], i));
+                ps[i] = pr[i] * vst;
+                b_lane = fmaf(pr[i], vlo - (float)GV::kM * vst, b_lane);
+            }
+            l_lane += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+            const uint32_t h01 = pack_bf16x2(ps[0], ps[1]), h23 = pack_bf16x2(ps[2], ps[3]);
+            float a0, a1, a2, a3;
+            unpack_bf16x2(h01, a0, a1);
+            unpack_bf16x2(h23, a2, a3);
+            const uint32_t l01 = pack_bf16x2(ps[0] - a0, ps[1] - a1), l23 = pack_bf16x2(ps[2] - a2, ps[3] - a3);
+            pfh = __builtin_bit_cast(i16x4, make_uint2(h01, h23));
+            pfl = __builtin_bit_cast(i16x4, make_uint2(l01, l23));
+        };
+        i16x4 pha, pla, phb, plb;
+        weights(sa, ra_, pha, pla);
+        weights(sb, rb_, phb, plb);
         const int vkey = 4 * kk + (lane % 16) / 4, q = lane % 4;
 #pragma unroll
         for (int t = 0; t < G::kNT; ++t) {
-            const i16x4 a = lds_read_tr16(vbuf + vkey * G::kRow + 16 * vslot<D>(vkey, 2 * t + q / 2) + 8 * (q % 2));
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pfh, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pfl, acc[t], 0, 0, 0);
+            const int vo = vkey * G::kRow + 16 * vslot<D>(vkey, 2 * t + q / 2) + 8 * (q % 2);
+            const i16x4 aa = lds_read_tr16(vbuf + vo);
+            const i16x4 ab = lds_read_tr16(kbuf + vo);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aa, pha, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aa, pla, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ab, phb, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ab, plb, acc[t], 0, 0, 0);
         }
     };
 
-    for (int j = 0; j < nch; j += 2) {
-        issue(j + 1, rb);
-        compute(j, ra);
-        if (j + 1 >= nch) break;
-        issue(j + 2, ra);
-        compute(j + 1, rb);
+    for (int j = 0; j < nch; j += 4) {
+        issue(j + 2, ra2);
+        issue(j + 3, rb2);
+        compute2(j, ra, rb);
+        if (j + 2 >= nch) break;
+        issue(j + 4, ra);
+        issue(j + 5, rb);
+        compute2(j + 2, ra2, rb2);
     }
 
     // The ranges' offsets of the values: every output value of head n gains sum p (lo - M step).

@@ -232,7 +232,7 @@ def main() -> int:
     vcs = [v_raw] + [v_raw.clone() for _ in range(args.cache_copies - 1)]
     lens = torch.tensor(idc["lens"], device=dev)
     pos = torch.tensor(idc["pos"], device=dev)
-    splits = tah.decode_default_splits(wd.batch, wd.hq, wd.hkv, wd.seq)
+    splits = tah.decode_default_splits(wd.batch, wd.hq, wd.hkv, wd.d, wd.seq)
     need = tah.decode_workspace_size(wd.batch, wd.hq, wd.hkv, wd.d, wd.seq, splits)
     ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
     out4 = torch.empty_like(q4)

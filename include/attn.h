@@ -235,7 +235,7 @@ attn_status_t attn_prefill_chunk_paged(const void *q, const void *k_new, const v
  */
 size_t attn_decode_workspace_size(int64_t batch, int64_t hq, int64_t hkv, int64_t d,
                                   int64_t max_len, int64_t splits);
-int64_t attn_decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len);
+int64_t attn_decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t d, int64_t max_len);
 attn_status_t attn_decode(const void *q, const void *k_cache, const void *v_cache, void *out,
                           int64_t batch, int64_t hq, int64_t hkv, int64_t d, int64_t capacity,
                           const int32_t *lens, const int32_t *pos, int64_t max_len, int64_t max_pos,

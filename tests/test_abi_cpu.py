@@ -311,19 +311,21 @@ def test_prefill_chunk_paged_rejects(lib):
 
 
 def test_decode_sizes(lib):
-    # up to 8 kv heads with up to 8 q heads each: a block per (sequence, key split) reads
-    # whole cache rows; about one block per CU, at least 256 keys per split
-    assert lib.attn_decode_default_splits(32, 32, 8, 4096) == 8
-    assert lib.attn_decode_workspace_size(32, 32, 8, 128, 4096, 0) == 8 * 32 * 32 * 130 * 4
+    # up to 8 kv heads with up to 8 q heads each: a block per (sequence, group of 512 / d
+    # kv heads, key split) reads whole cache-row pieces; about one block per CU, at least
+    # 256 keys per split
+    assert lib.attn_decode_default_splits(32, 32, 8, 128, 4096) == 4      # 2 groups of 4 kv heads
+    assert lib.attn_decode_default_splits(32, 32, 8, 64, 4096) == 8       # 1 group of 8
+    assert lib.attn_decode_workspace_size(32, 32, 8, 128, 4096, 0) == 4 * 32 * 32 * 130 * 4
     assert lib.attn_decode_workspace_size(32, 32, 8, 128, 4096, 1) == 0
     assert lib.attn_decode_workspace_size(32, 32, 8, 128, 4096, 3) == 3 * 32 * 32 * 130 * 4
-    assert lib.attn_decode_default_splits(1, 32, 8, 4096) == 16
+    assert lib.attn_decode_default_splits(1, 32, 8, 128, 4096) == 16
     assert lib.attn_decode_workspace_size(1, 32, 8, 128, 4096, 0) == 16 * 32 * 130 * 4
-    assert lib.attn_decode_default_splits(1, 32, 8, 100000) == 256
-    assert lib.attn_decode_default_splits(256, 32, 8, 4096) == 1
+    assert lib.attn_decode_default_splits(1, 32, 8, 128, 100000) == 128
+    assert lib.attn_decode_default_splits(256, 32, 8, 128, 4096) == 1
     # 16 q heads per kv head: blocks per (sequence, kv head, group of 8 q heads); 256 such
     # units already give every CU a block: one split, no workspace
-    assert lib.attn_decode_default_splits(32, 64, 4, 4096) == 1
+    assert lib.attn_decode_default_splits(32, 64, 4, 128, 4096) == 1
     assert lib.attn_decode_workspace_size(32, 64, 4, 128, 4096, 0) == 0
     assert lib.attn_decode_workspace_size(0, 32, 8, 128, 4096, 0) == 0
     assert _decode(lib, batch=0) == A.ATTN_OK

@@ -86,12 +86,13 @@ def test_static_decode_f32():
 
 def test_static_decode_lowers_default_splits_to_fit():
     require_gpu()
-    # 64 sequences x 64 q heads (d 128): the default 4 splits need 64 * 64 * 130 * 4 * 4
-    # bytes, more than the 8 MiB scratch, so the static call runs 3 (random operands
-    # drawn on the device; this only compares the two entry points)
-    b, hq, hkv, d, cap = 64, 64, 8, 128, 1024
+    # 127 sequences x 64 q heads (d 128, two groups of 4 kv heads): the default 2 splits
+    # need 2 * 127 * 64 * 130 * 4 bytes, more than the 8 MiB scratch, so the static call
+    # runs one (random operands drawn on the device; this only compares the two entry
+    # points)
+    b, hq, hkv, d, cap = 127, 64, 8, 128, 1024
     cap_bytes = tah.decode_static_scratch_bytes()
-    default = tah.decode_default_splits(b, hq, hkv, cap)
+    default = tah.decode_default_splits(b, hq, hkv, d, cap)
     per_split = b * hq * (d + 2) * 4
     assert default * per_split > cap_bytes
     lowered = max(1, min(default, cap_bytes // per_split))

@@ -69,7 +69,7 @@ def load_library(path: str = LIB_PATH):
     lib.attn_decode.restype = ctypes.c_int
     lib.attn_decode_workspace_size.argtypes = [_i64] * 6
     lib.attn_decode_workspace_size.restype = ctypes.c_size_t
-    lib.attn_decode_default_splits.argtypes = [_i64] * 4
+    lib.attn_decode_default_splits.argtypes = [_i64] * 5
     lib.attn_decode_default_splits.restype = _i64
     lib.attn_kv_quantize.argtypes = [_vp] + [_i64] * 6 + [_vp, _vp, _i64, _i64, ctypes.c_int, _vp]
     lib.attn_kv_quantize.restype = ctypes.c_int
@@ -506,8 +506,8 @@ def _max_pos(prep: "HeadPrep | None", max_pos: "int | None") -> int:
     return prep.table_rows - 1 if prep is not None and prep.half else 0
 
 
-def decode_default_splits(batch: int, hq: int, hkv: int, max_len: int) -> int:
-    return int(load_library().attn_decode_default_splits(batch, hq, hkv, max_len))
+def decode_default_splits(batch: int, hq: int, hkv: int, d: int, max_len: int) -> int:
+    return int(load_library().attn_decode_default_splits(batch, hq, hkv, d, max_len))
 
 
 def attn_decode(q, k_cache, v_cache, lens, pos, max_len: int, prep: HeadPrep | None = None,

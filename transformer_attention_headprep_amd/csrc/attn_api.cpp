@@ -584,9 +584,9 @@ attn_status_t attn_row_norm_rope(void *x, int64_t rows, int64_t width, int64_t h
     return hip_status(attn::launch_row_norm_rope(a, static_cast<hipStream_t>(stream)), "attn_row_norm_rope");
 }
 
-int64_t attn_decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len) {
-    if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || max_len <= 0) return 0;
-    return attn::decode_default_splits(batch, hq, hkv, max_len);
+int64_t attn_decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t d, int64_t max_len) {
+    if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || d <= 0 || max_len <= 0) return 0;
+    return attn::decode_default_splits(batch, hq, hkv, d, max_len);
 }
 
 int64_t attn_decode_q_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len, int64_t k_bits) {
@@ -598,7 +598,7 @@ int64_t attn_decode_q_default_splits(int64_t batch, int64_t hq, int64_t hkv, int
 size_t attn_decode_workspace_size(int64_t batch, int64_t hq, int64_t hkv, int64_t d, int64_t max_len,
                                   int64_t splits) {
     if (batch <= 0 || hq <= 0 || hkv <= 0 || hq % hkv != 0 || d <= 0 || max_len <= 0 || splits < 0) return 0;
-    if (splits == 0) splits = attn::decode_default_splits(batch, hq, hkv, max_len);
+    if (splits == 0) splits = attn::decode_default_splits(batch, hq, hkv, d, max_len);
     return attn::decode_workspace_bytes(batch, hq, d, splits);
 }
 
@@ -639,7 +639,7 @@ static attn_status_t decode_impl(const void *q, const void *k_cache, const void 
                         (long long)prep->table_rows);
     }
     if (batch == 0) return ATTN_OK;
-    if (splits == 0) splits = attn::decode_default_splits(batch, hq, hkv, max_len);
+    if (splits == 0) splits = attn::decode_default_splits(batch, hq, hkv, d, max_len);
     if (splits * batch >= ((int64_t)1 << 31) || splits >= 65536 || batch >= 65536 || hkv * hq >= 65536)
         return fail(ATTN_ERR_ARG, "problem too large for one launch");
     const size_t need = attn::decode_workspace_bytes(batch, hq, d, splits);
@@ -713,7 +713,7 @@ attn_status_t attn_decode_static(const void *q, const void *k_cache, const void 
         const size_t per_split = attn::decode_workspace_bytes(batch, hq, d, 2) / 2;
         if (s == 0) {
             // the library's choice, lowered until the partials fit (one split needs none)
-            s = attn::decode_default_splits(batch, hq, hkv, max_len);
+            s = attn::decode_default_splits(batch, hq, hkv, d, max_len);
             if (s > 1 && (size_t)s * per_split > cap) s = std::max<int64_t>(1, (int64_t)(cap / per_split));
         }
         need = attn::decode_workspace_bytes(batch, hq, d, s);

@@ -65,10 +65,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const void *base, int
     return __builtin_amdgcn_make_buffer_rsrc(sbase, (short)0, __builtin_amdgcn_readfirstlane(n), 0x00020000);
 }
 
-// 16 bytes per lane from a buffer straight into LDS: lane L writes lds + 16 L.
+// Cache-policy bits of a buffer access: kStream (nt, non-temporal) marks data read once,
+// so that streaming it does not push out lines the caches hold for reuse -- or that are
+// still waiting to be written back.
+constexpr int kStream = 2;
+
+// 16 bytes per lane from a buffer straight into LDS: lane L writes lds + 16 L (policy:
+// 0 or kStream).
+template <int POLICY = 0>
 __device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t rsrc, void *lds, int voffset) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)lds, 16, voffset,
-                                             0, 0, 0);
+                                             0, 0, POLICY);
 }
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element i % 4 of

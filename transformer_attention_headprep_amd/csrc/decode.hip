@@ -106,8 +106,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
 #pragma unroll
         for (int i = 0; i < G::kLoads; ++i) {
             const int64_t skip = (int64_t)(G::kRpi * i) * rowb;
-            r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(seq_rsrc(kbase + crow * rowb + skip, bytes - skip), loff, 0, 0);
-            r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(seq_rsrc(vbase + crow * rowb + skip, bytes - skip), loff, 0, 0);
+            r.k[i] = __builtin_amdgcn_raw_buffer_load_b128(seq_rsrc(kbase + crow * rowb + skip, bytes - skip), loff, 0, kStream);
+            r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(seq_rsrc(vbase + crow * rowb + skip, bytes - skip), loff, 0, kStream);
         }
     };
 
@@ -317,8 +317,10 @@ __global__ __launch_bounds__(512) void decode_rows_kernel(const DecodeParams p, 
         const __amdgpu_buffer_rsrc_t vr = seq_rsrc(static_cast<const uint8_t *>(p.v) + crow * RP + hoff, bytes);
 #pragma unroll
         for (int x = 0; x < per_w; ++x) {
-            buffer_to_lds16(kr, buf + 1024 * (w + nw * x), (int)koff[x]);
-            buffer_to_lds16(vr, buf + kChunk * RPb + 1024 * (w + nw * x), (int)voff[x]);
+            // (the cache is read once: streamed, so it neither evicts nor waits behind
+            // lines that other work left to be written back)
+            buffer_to_lds16<kStream>(kr, buf + 1024 * (w + nw * x), (int)koff[x]);
+            buffer_to_lds16<kStream>(vr, buf + kChunk * RPb + 1024 * (w + nw * x), (int)voff[x]);
         }
     };
 
@@ -853,10 +855,12 @@ bool decode_rows_fits(int64_t hq, int64_t hkv) {
     return hkv <= 8 && hq / hkv <= 8;      // a wave per kv head, up to 8 q heads each
 }
 
-int64_t decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len) {
+int64_t decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t d, int64_t max_len) {
     if (decode_rows_fits(hq, hkv)) {
-        // a block per (sequence, split): about one block per CU, at least 256 keys each
-        int64_t splits = (kCUs + batch - 1) / batch;
+        // a block per (sequence, group of kv heads, split): about one block per CU (one
+        // round of blocks), at least 256 keys each
+        const int64_t groups = hkv / decode_rows_group(hkv, d);
+        int64_t splits = (kCUs + batch * groups - 1) / (batch * groups);
         const int64_t most = (max_len + 255) / 256;
         if (splits > most) splits = most;
         return splits < 1 ? 1 : splits;

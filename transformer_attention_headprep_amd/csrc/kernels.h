@@ -164,7 +164,7 @@ hipError_t launch_kv_quantize(const KvQuantLaunch &a, hipStream_t stream);
 int64_t decode_heads_per_block(int64_t hq, int64_t hkv);
 // true when the bf16 decode runs as whole-row blocks (a wave per kv head)
 bool decode_rows_fits(int64_t hq, int64_t hkv);
-int64_t decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len);
+int64_t decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t d, int64_t max_len);
 int64_t decode_q_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len, int64_t kbits);
 size_t decode_workspace_bytes(int64_t batch, int64_t hq, int64_t d, int64_t splits);
 // The decode scratch that lives in the library (for callers that cannot allocate): its

@@ -167,17 +167,18 @@ struct QGeo {
     static_assert(kCodes % 8 == 0, "whole 16-byte bf16 slots");
 };
 
+// LB bytes a lane of a coded tensor, streamed (read once).
 template <int LB>
 __device__ __forceinline__ void load_words(uint32_t *w, __amdgpu_buffer_rsrc_t rs, int off) {
     if constexpr (LB == 16) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kStream);
         w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
     } else if constexpr (LB == 8) {
         typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kStream);
         w[0] = v[0]; w[1] = v[1];
     } else {
-        w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kStream);
     }
 }
 
@@ -315,8 +316,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 
         for (int i = 0; i < GV::kNL; ++i) load_words<GV::kLB>(r.v[i], vr, (64 * i + lane) * GV::kLB);
         typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
         const int pofs = 8 * (4 * kk + n % 4);
-        const u32x2 kp2 = __builtin_amdgcn_raw_buffer_load_b64(kpr, pofs, 0, 0);
-        const u32x2 vp2 = __builtin_amdgcn_raw_buffer_load_b64(vpr, pofs, 0, 0);
+        const u32x2 kp2 = __builtin_amdgcn_raw_buffer_load_b64(kpr, pofs, 0, kStream);
+        const u32x2 vp2 = __builtin_amdgcn_raw_buffer_load_b64(vpr, pofs, 0, kStream);
         r.kp[0] = kp2[0]; r.kp[1] = kp2[1];
         r.vp[0] = vp2[0]; r.vp[1] = vp2[1];
     };

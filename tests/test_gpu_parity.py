@@ -117,9 +117,11 @@ def test_prefill_f32_workloads_full(name):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("seq,hq,hkv", [(300, 8, 2), (1, 4, 4), (129, 6, 3), (64, 2, 1)])
+@pytest.mark.parametrize("seq,hq,hkv", [(300, 8, 2), (1, 4, 4), (129, 6, 3), (64, 2, 1), (300, 4, 4), (200, 3, 1)])
 def test_prefill_small_full(dtype, d, causal, seq, hq, hkv):
-    """Several 128-row query tiles and 64-key tiles, with ragged tails, every element."""
+    """Several 128-row query tiles and 64-key tiles, with ragged tails, every element
+    (q heads per kv head even, so a block's two slots share their query rows, and odd:
+    each block holds two query tiles of one q head)."""
     require_gpu()
     w = synthetic.Workload("s", "prefill", dtype, 2, hq, hkv, seq, d, d // 2, 1e4, 7, causal=causal)
     inp = synthetic.make_prefill(w)

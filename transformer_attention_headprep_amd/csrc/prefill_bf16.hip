@@ -51,6 +51,12 @@
 // 256, exact in f32 sums and bf16).  The row sum adds the f32 weights (the P V product
 // takes their bf16 roundings).
 //
+// Between items: with two q heads a block (the slots share their query rows) the two
+// groups run their prologues side by side and split the rotary table rows between them;
+// those rows come by whole-row loads into LDS and are read back in the fragment layout,
+// and each item's q loads are issued in the previous item's epilogue.  The output tile
+// goes through LDS too, so that every store writes whole rows.
+//
 // q's HeadPrep (RMS, qw, split-half turn at the row's position, scale log2 e) runs in
 // each wave's prologue in registers; it needs half = 0 or a multiple of 16.
 #include <type_traits>

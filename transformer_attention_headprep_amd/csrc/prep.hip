@@ -86,19 +86,19 @@ struct PrepUnit {
     float lo[4], hi[4];
     float4 wl, wh, cq, sq;
 
+    // IX: the integer type of the unit index arithmetic (32-bit when every unit index
+    // fits: two divisions then cost a few instructions each instead of a long 64-bit
+    // sequence, for every lane of every head).
+    template <typename IX>
     __device__ __forceinline__ void locate(const PrepParams &p, int64_t unit) {
         valid = unit < p.n_units;
-        int64_t row, bb;
         const bool is_q = unit < p.n_q_units;
-        if (is_q) {
-            const int64_t u = valid ? unit : 0;
-            row = u / p.hq;
-            bb = row / p.seq;
-        } else {
-            const int64_t u = valid ? unit - p.n_q_units : 0;
-            row = u / p.hkv;
-            bb = row / p.seq;
-        }
+        const IX uu = (IX)(valid ? (is_q ? unit : unit - p.n_q_units) : 0);
+        const IX heads = (IX)(is_q ? p.hq : p.hkv);
+        const IX rowi = uu / heads;
+        const IX hi_ = uu - rowi * heads;
+        const IX bbi = rowi / (IX)p.seq;
+        const int64_t bb = (int64_t)bbi, hh = (int64_t)hi_;
         // the sequence's first position: pos0, or its own past[b] (0 when out of range,
         // and then its key rows are not written)
         int64_t first = p.pos0, krow0 = p.k_row0;
@@ -109,14 +109,14 @@ struct PrepUnit {
             first = seq_ok ? v : 0;
             krow0 = first;
         }
-        const int64_t t = row % p.seq;
+        const int64_t t = (int64_t)(rowi - bbi * (IX)p.seq);
         if (is_q) {
-            const int64_t h = (valid ? unit : 0) % p.hq;
+            const int64_t h = hh;
             src = p.q_src; dst = p.q_dst; w = p.qw;
             src_off = bb * p.q_src_bs + t * p.q_src_rs + h * D;
             dst_off = bb * p.q_dst_bs + t * p.q_dst_rs + h * D;
         } else {
-            const int64_t h = (valid ? unit - p.n_q_units : 0) % p.hkv;
+            const int64_t h = hh;
             src = p.k_src; dst = p.k_dst; w = p.kw;
             src_off = bb * p.k_src_bs + t * p.k_src_rs + h * D;
             dst_off = bb * p.k_dst_bs + ((p.past ? krow0 : 0) + t) * p.k_dst_rs + h * D;
@@ -215,7 +215,7 @@ struct PrepUnit {
 // MODE 3: adjacent pairs, any half, in-lane.  A group of D/8 lanes takes U consecutive
 // heads, whose loads are all in flight together (U = 1 for MODE 2, whose LDS stage holds
 // one head per lane group).
-template <bool BF16, int D, int MODE, int U>
+template <bool BF16, int D, int MODE, int U, bool NARROW>
 __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepParams p) {
     constexpr int LPH = D / 8;                  // lanes per head
     constexpr int HPB = kPrepThreads / LPH;     // lane groups per block
@@ -227,7 +227,13 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const PrepParams p) 
     const int e_lo = 4 * li, e_hi = D / 2 + 4 * li;
     PrepUnit<BF16, D, MODE> units[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) units[u].locate(p, ((int64_t)blockIdx.x * HPB + hb) * U + u);
+    for (int u = 0; u < U; ++u) {
+        const int64_t unit = ((int64_t)blockIdx.x * HPB + hb) * U + u;
+        if constexpr (NARROW)
+            units[u].template locate<uint32_t>(p, unit);
+        else
+            units[u].template locate<int64_t>(p, unit);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) units[u].load(p, e_lo, e_hi);
 #pragma unroll
@@ -243,14 +249,27 @@ hipError_t launch_prep_d(const PrepParams &p, int mode, hipStream_t stream) {
     const int64_t blocks1 = (p.n_units + HPB - 1) / HPB;
     const int64_t blocksU = (p.n_units + HPB * U - 1) / (HPB * U);
     if (blocks1 == 0) return hipSuccess;
-    if (mode == 0)
-        hipLaunchKernelGGL((prep_kernel<BF16, D, 0, U>), dim3(blocksU), dim3(kPrepThreads), 0, stream, p);
-    else if (mode == 1)
-        hipLaunchKernelGGL((prep_kernel<BF16, D, 1, U>), dim3(blocksU), dim3(kPrepThreads), 0, stream, p);
-    else if (mode == 2)
-        hipLaunchKernelGGL((prep_kernel<BF16, D, 2, 1>), dim3(blocks1), dim3(kPrepThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((prep_kernel<BF16, D, 3, U>), dim3(blocksU), dim3(kPrepThreads), 0, stream, p);
+    // 32-bit unit arithmetic when every unit index (and so every row and head index) fits
+    const bool narrow = p.n_units + HPB * U < ((int64_t)1 << 32);
+    if (narrow) {
+        if (mode == 0)
+            hipLaunchKernelGGL((prep_kernel<BF16, D, 0, U, true>), dim3(blocksU), dim3(kPrepThreads), 0, stream, p);
+        else if (mode == 1)
+            hipLaunchKernelGGL((prep_kernel<BF16, D, 1, U, true>), dim3(blocksU), dim3(kPrepThreads), 0, stream, p);
+        else if (mode == 2)
+            hipLaunchKernelGGL((prep_kernel<BF16, D, 2, 1, true>), dim3(blocks1), dim3(kPrepThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((prep_kernel<BF16, D, 3, U, true>), dim3(blocksU), dim3(kPrepThreads), 0, stream, p);
+    } else {
+        if (mode == 0)
+            hipLaunchKernelGGL((prep_kernel<BF16, D, 0, U, false>), dim3(blocksU), dim3(kPrepThreads), 0, stream, p);
+        else if (mode == 1)
+            hipLaunchKernelGGL((prep_kernel<BF16, D, 1, U, false>), dim3(blocksU), dim3(kPrepThreads), 0, stream, p);
+        else if (mode == 2)
+            hipLaunchKernelGGL((prep_kernel<BF16, D, 2, 1, false>), dim3(blocks1), dim3(kPrepThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((prep_kernel<BF16, D, 3, U, false>), dim3(blocksU), dim3(kPrepThreads), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -458,9 +458,9 @@ def test_decode_q_rejects(lib, kw, code):
 def test_decode_q_default_splits(lib):
     # the decode workload's 256 (sequence, kv head) units: one round of 2 blocks per CU
     assert lib.attn_decode_q_default_splits(32, 32, 8, 4096, 8) == 2
-    assert lib.attn_decode_q_default_splits(32, 32, 8, 4096, 4) == 2
-    assert lib.attn_decode_q_default_splits(32, 32, 8, 4096, 2) == 2
-    assert lib.attn_decode_q_default_splits(4, 32, 8, 4096, 4) == 16
+    assert lib.attn_decode_q_default_splits(32, 32, 8, 4096, 4) == 3
+    assert lib.attn_decode_q_default_splits(32, 32, 8, 4096, 2) == 3
+    assert lib.attn_decode_q_default_splits(4, 32, 8, 4096, 4) == 16      # at most max_len / 256
     assert lib.attn_decode_q_default_splits(4, 32, 8, 300, 4) == 2      # at least 256 keys a split
     assert lib.attn_decode_q_default_splits(32, 32, 8, 4096, 3) == 0     # not a width
     assert lib.attn_decode_q_default_splits(0, 32, 8, 4096, 8) == 0

@@ -877,13 +877,12 @@ int64_t decode_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t d,
 }
 
 int64_t decode_q_default_splits(int64_t batch, int64_t hq, int64_t hkv, int64_t max_len, int64_t kbits) {
-    // About one round of blocks: two are resident per CU (the kernel's registers), and a
-    // second round pays the q prologue again (measured: 8/8, 4/4 and 4/2 all fastest or
-    // within a few percent of it at two blocks a CU).
-    (void)kbits;
+    // About one round of blocks: a second round pays the q prologue again.  The kernel's
+    // registers leave two blocks resident per CU with 8-bit keys and three with 4- or 2-bit
+    // keys (measured at d = 128: 8/8 fastest at two blocks a CU, 4/4 and 4/2 at three).
     const int64_t gb = decode_heads_per_block(hq, hkv);
     const int64_t units = batch * hkv * ((hq / hkv + gb - 1) / gb);
-    const int64_t blocks = 2 * kCUs;
+    const int64_t blocks = (kbits == 8 ? 2 : 3) * kCUs;
     int64_t splits = (blocks + units - 1) / units;
     const int64_t most = (max_len + 255) / 256;
     if (splits > most) splits = most;

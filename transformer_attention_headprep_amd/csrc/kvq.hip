@@ -241,8 +241,13 @@ __device__ __forceinline__ uint32_t quad_lane(uint32_t v, int i) {
     }
 }
 
+// At d = 128 the occupancy hint asks for no more than two waves per SIMD: a higher one
+// caps the vector registers at 128, and the compiler then parks the excess in
+// accumulation registers (or scratch) and copies it back and forth inside the chunk loop
+// (about a fifth of the loop's vector instructions at 4/4).  Without the cap the 4- and
+// 2-bit kernels need ~150 registers, so three waves per SIMD still fit; 8-bit ~180 (two).
 template <int D, int GB, int KB, int VB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 4 ? 4 : 3))) void decode_q_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : (GB <= 4 ? 4 : 3)))) void decode_q_kernel(const DecodeParams p) {
     typedef DecGeo<D> G;
     typedef QGeo<D, KB> GK;
     typedef QGeo<D, VB> GV;

@@ -37,8 +37,10 @@
 namespace attn {
 namespace {
 
+// At d = 128 at most two waves per SIMD are asked for: a higher hint caps the vector
+// registers at 128 and the excess goes through accumulation registers inside the loop.
 template <int D, int GB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(GB <= 4 ? 4 : 3))) void decode_bf16_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : (GB <= 4 ? 4 : 3)))) void decode_bf16_kernel(const DecodeParams p) {
     typedef DecGeo<D> G;
     constexpr int kTiles = kWaves * 2 * G::kBuf;               // K and V chunk of every wave
     constexpr int kQBytes = 2 * GB * D * 4 + 4 * (kThreads / 64);

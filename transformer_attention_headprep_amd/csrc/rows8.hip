@@ -288,8 +288,12 @@ struct Geo8 {
     static_assert(kTile * kKSlots % 64 == 0 && D * kVSlots % 64 == 0, "whole 64-lane loads");
 };
 
+// The occupancy hint caps the register budget per wave at 256 (d = 128) or 128: with a
+// larger budget the compiler keeps the products' results in accumulation registers and
+// copies every score and every rescaled output value through them (about four in ten of
+// the tile loop's vector instructions, on a loop bound by its vector instructions).
 template <int D>
-__global__ __launch_bounds__(256) void attn8_kernel(const Rows8Launch a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 4))) void attn8_kernel(const Rows8Launch a) {
     typedef Geo8<D> G;
     constexpr int NC = D / 32;       // k steps of S^T (32 bytes each)
     constexpr int NDB = D / 32;      // 32-wide d blocks of the output

@@ -233,6 +233,11 @@ __global__ __launch_bounds__(256) void rows8_vt_kernel(const Rows8Launch a) {
     const int64_t row0 = gstart + (int64_t)t * kTile;
     const uint16_t *qkv = static_cast<const uint16_t *>(a.qkv);
     const int64_t rs = 3 * a.heads * D;
+    // The group's amax of v is the largest of its tiles' (written by the quantizing
+    // kernel): the threads read them side by side, reduced over the block below.
+    __shared__ float red[4];
+    float amax = 0.f;
+    for (int tt = tid; tt < a.tiles; tt += 256) amax = fmaxf(amax, a.vmax[((int64_t)g * a.tiles + tt) * a.heads + h]);
     for (int idx = tid; idx < kTile * (D / 8); idx += 256) {     // 16-byte loads: 8 values each
         const int i = idx / (D / 8), e0 = 8 * (idx % (D / 8));
         const int64_t r = row0 + i;
@@ -247,10 +252,10 @@ __global__ __launch_bounds__(256) void rows8_vt_kernel(const Rows8Launch a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) vs[i][e0 + j] = x[j];
     }
+    amax = max_lanes<64>(amax);
+    if (tid % 64 == 0) red[tid / 64] = amax;
     __syncthreads();
-    // The group's amax of v: the largest of its tiles' (written by the quantizing kernel).
-    float amax = 0.f;
-    for (int tt = 0; tt < a.tiles; ++tt) amax = fmaxf(amax, a.vmax[((int64_t)g * a.tiles + tt) * a.heads + h]);
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
     const float inv = __fdiv_rn(1.0f, s);
     uint8_t *tile = a.v8t + (((int64_t)g * a.tiles + t) * a.heads + h) * D * kTile;

@@ -70,6 +70,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t seq_rsrc(const void *base, int
 // still waiting to be written back.
 constexpr int kStream = 2;
 
+// XCDs (accelerator complex dies, each with its own L2) of the chip; a launch deals its
+// blocks to them round robin.
+constexpr int kXcds = 8;
+
 // 16 bytes per lane from a buffer straight into LDS: lane L writes lds + 16 L (policy:
 // 0 or kStream).
 template <int POLICY = 0>

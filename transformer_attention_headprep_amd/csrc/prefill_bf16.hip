@@ -72,7 +72,6 @@ namespace {
 
 constexpr int kBN = 64;              // keys per tile
 constexpr int kBM = 128;             // query rows per slot (4 waves x 32)
-constexpr int kXcds = 8;
 constexpr float kRaiseAbove = 8.0f;  // base-2 headroom before the running maximum moves
 constexpr float kFixedShiftMax = 48.0f;
 

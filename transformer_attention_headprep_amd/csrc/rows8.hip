@@ -307,11 +307,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
     const int n = lane % 32, g = lane / 32;
-    // Blocks are dealt to the 8 XCDs round robin: give each XCD a run of consecutive
+    // Blocks are dealt to the XCDs round robin: give each XCD a run of consecutive
     // (query tile, head) indices, so the query tiles of a head share one L2.
     const unsigned nbx = gridDim.x, nb = nbx * gridDim.y, lin = blockIdx.x + blockIdx.y * nbx;
-    const unsigned full = nb / 8 * 8;
-    const unsigned vid = lin < full ? (lin % 8) * (nb / 8) + lin / 8 : lin;
+    const unsigned full = nb / kXcds * kXcds;
+    const unsigned vid = lin < full ? (lin % kXcds) * (nb / kXcds) + lin / kXcds : lin;
     const int bx = (int)(vid % nbx), h = (int)(vid / nbx);
     const int qt = bx % a.qtiles, grp = bx / a.qtiles;
     const int64_t gstart = (int64_t)grp * a.group;

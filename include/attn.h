@@ -334,8 +334,8 @@ attn_status_t attn_kv_quantize(const void *x, int64_t batch, int64_t seq, int64_
  *                (2, 2).
  *   lens, pos, max_len, max_pos, prep, scale: as attn_decode.
  *   splits       number of key splits per sequence; 0 = attn_decode_q_default_splits
- *                (more splits than the bf16 decode takes: a coded chunk carries fewer
- *                bytes, so more blocks keep the memory busy).
+ *                (about one round of blocks: two per CU with 8-bit keys, three with 4- or
+ *                2-bit keys, whose kernels hold fewer registers; at least 256 keys a split).
  *   workspace    at least attn_decode_workspace_size(batch, hq, hkv, d, max_len, s) bytes
  *                where s is the split count the call uses (the default resolved above
  *                when splits = 0); NULL is allowed when that size is 0.
